@@ -1,0 +1,276 @@
+/*
+ * oracle.c -- plain, slow CPU definition of the BitLinear forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark, never by the library.  It is written
+ * from the method's definition, one step per function, in the order the
+ * pages give (RMSNorm -> quantise -> ternary add/subtract -> rescale), with
+ * no blocking, fusion or reordering.  Source tags ([ld246], [jiqizhixin],
+ * [datacamp]) are expanded in oracle.h.
+ *
+ * Build: gcc -std=c11 -O2 (ISO mode: no FMA contraction, no fast-math), so
+ * every fp32 expression below rounds once per operation, round-half-even.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> float                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* A bf16 value is the top 16 bits of the fp32 value with the same sign,
+ * exponent and leading 7 fraction bits, so widening is exact. */
+float orc_bf16_to_float(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Nearest bf16 to v, ties to even, from the definition: bf16 carries 8
+ * significant bits, so the spacing of representable values at |v| in
+ * [2^(e-1), 2^e) is 2^(e-8), and never below the subnormal spacing 2^-133.
+ * Round |v| to a whole number of spacings, then read the bit pattern off the
+ * (exactly representable) fp32 value.  Inf/NaN are outside the contract. */
+uint16_t orc_double_to_bf16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);              /* a = f * 2^e, 0.5 <= f < 1 */
+    int qe = e - 8;
+    if (qe < -133) qe = -133;
+    double n = rint(ldexp(a, -qe));  /* default rounding mode: ties to even */
+    float f = (float)ldexp(n, qe);   /* exact: at most 9 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weights: absmean ternarisation and 2-bit storage                          */
+/* ------------------------------------------------------------------------ */
+
+/* [datacamp, "Thay MatMul bằng các phép toán tam phân"]: the weight scale is
+ * the mean absolute value of the matrix ("its" mean, one scalar per
+ * matrix).  Reading: the sum is taken in fp64 in row-major order, divided in
+ * fp64 and rounded once to fp32. */
+float orc_absmean_gamma(const float* W, int64_t N, int64_t K) {
+    double sum = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            sum += fabs((double)W[n * K + k]);
+    return (float)(sum / (double)(N * K));
+}
+
+/* [datacamp, same section]: each weight is scaled by the matrix's mean
+ * absolute value and rounded to the nearest of -1, 0, +1; [ld246,
+ * "三值权重的应用"] restricts weights to {-1, 0, +1}.  Readings: the scaling
+ * divides by gamma + 1e-5 (the page's "multiply" would send almost every
+ * weight to 0), the division and the rounding are fp32, ties go to even. */
+void orc_ternarize(const float* W, int64_t N, int64_t K, float gamma, int8_t* w) {
+    float d = gamma + 1e-5f;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            float t = rintf(W[n * K + k] / d);
+            if (t > 1.0f) t = 1.0f;
+            if (t < -1.0f) t = -1.0f;
+            w[n * K + k] = (int8_t)t;
+        }
+    }
+}
+
+/* Storage format (the pages give none; this is the library's own):
+ *   - row n of w occupies K/4 bytes, rows back to back; K % 16 == 0;
+ *   - along a row, weights go in groups of 16 (k = 16*grp + j, j = 0..15);
+ *     group grp lives in bytes 4*grp .. 4*grp+3 of the row;
+ *   - weight j = 4*i + t of a group sits in byte 4*grp + t, bits 2i+1..2i;
+ *   - the 2-bit code is w + 1: 0 -> -1, 1 -> 0, 2 -> +1; code 3 is unused.
+ * The function reads the format straight off this description. */
+static int64_t orc_code_byte(int64_t K, int64_t n, int64_t k) {
+    int64_t grp = k / 16, j = k % 16, t = j % 4;
+    return n * (K / 4) + 4 * grp + t;
+}
+static int orc_code_shift(int64_t k) {
+    int64_t j = k % 16, i = j / 4;
+    return (int)(2 * i);
+}
+
+int orc_pack(const int8_t* w, int64_t N, int64_t K, uint8_t* packed) {
+    if (K % 16 != 0) return -1;
+    memset(packed, 0, (size_t)(N * (K / 4)));
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int v = w[n * K + k];
+            if (v < -1 || v > 1) return -1;
+            uint8_t code = (uint8_t)(v + 1);
+            packed[orc_code_byte(K, n, k)] |= (uint8_t)(code << orc_code_shift(k));
+        }
+    }
+    return 0;
+}
+
+int orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* w) {
+    if (K % 16 != 0) return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int code = (packed[orc_code_byte(K, n, k)] >> orc_code_shift(k)) & 3;
+            if (code == 3) return -1;
+            w[n * K + k] = (int8_t)(code - 1);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activations: RMSNorm then per-token absmax int8                            */
+/* ------------------------------------------------------------------------ */
+
+/* [datacamp, "Các thành phần lõi: MLGRU và GLU", figure panel "RMS norm"]:
+ * activations are RMS-normalised before quantisation; [ld246, "融合
+ * BitLinear 层的创新"] and [jiqizhixin, Algorithm 1 title]: the quantisation
+ * follows RMSNorm inside BitLinear.  Readings (pages silent):
+ *   RMSNorm:  r = 1 / sqrt(mean(x^2) + eps), xn = (x * r) * g;
+ *             sum of squares in fp64 (k ascending), mean rounded to fp32,
+ *             then fp32 add, sqrt and divide (each correctly rounded);
+ *   quantise: per token (row), symmetric absmax to 127:
+ *             s = 127 / max(max|xn|, 1e-5), q = clip(round(xn * s), -128, 127),
+ *             fp32, round half to even. */
+void orc_rmsnorm_quant(const uint16_t* x, const float* g, int64_t M, int64_t K,
+                       float eps, int8_t* q, float* s) {
+    float* xn = (float*)malloc((size_t)K * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)orc_bf16_to_float(row[k]);
+            ss += v * v;
+        }
+        float ms = (float)(ss / (double)K);
+        float r = 1.0f / sqrtf(ms + eps);
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            xn[k] = (orc_bf16_to_float(row[k]) * r) * g[k];
+            float a = fabsf(xn[k]);
+            if (a > amax) amax = a;
+        }
+        float scale = 127.0f / (amax > 1e-5f ? amax : 1e-5f);
+        for (int64_t k = 0; k < K; ++k) {
+            float v = rintf(xn[k] * scale);
+            if (v > 127.0f) v = 127.0f;
+            if (v < -128.0f) v = -128.0f;
+            q[m * K + k] = (int8_t)v;
+        }
+        s[m] = scale;
+    }
+    free(xn);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ternary accumulation and rescale                                          */
+/* ------------------------------------------------------------------------ */
+
+/* [ld246, "三值权重的应用"]: weight +1 adds the input, -1 subtracts it, 0
+ * does nothing; [jiqizhixin, "具有三值权重的 MatMul-free 密集层"]: the
+ * ternary product is written with additions and subtractions only. */
+void orc_ternary_accumulate(const int8_t* q, const int8_t* w, int64_t M, int64_t N,
+                            int64_t K, int32_t* acc) {
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t a = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                if (w[n * K + k] == 1)
+                    a += q[m * K + k];
+                else if (w[n * K + k] == -1)
+                    a -= q[m * K + k];
+            }
+            acc[m * N + n] = a;
+        }
+    }
+}
+
+/* [datacamp, figure panel "MatMul vs scaled ternary accumulation"]: the
+ * integer accumulation is scaled back.  Reading: q ~= s * xn and W ~= gamma
+ * * w, so y = acc * gamma / s; no bias. */
+void orc_rescale(const int32_t* acc, float gamma, const float* s, int64_t M,
+                 int64_t N, double* y) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (double)acc[m * N + n] * (double)gamma / (double)s[m];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Compositions                                                              */
+/* ------------------------------------------------------------------------ */
+
+void orc_bitlinear_ternary(const uint16_t* x, const float* g, const int8_t* w,
+                           float gamma, int64_t M, int64_t N, int64_t K, float eps,
+                           double* y, int8_t* q_out, float* s_out, int32_t* acc_out) {
+    int8_t* q = q_out ? q_out : (int8_t*)malloc((size_t)(M * K));
+    float* s = s_out ? s_out : (float*)malloc((size_t)M * sizeof(float));
+    int32_t* acc = acc_out ? acc_out : (int32_t*)malloc((size_t)(M * N) * sizeof(int32_t));
+    orc_rmsnorm_quant(x, g, M, K, eps, q, s);
+    orc_ternary_accumulate(q, w, M, N, K, acc);
+    orc_rescale(acc, gamma, s, M, N, y);
+    if (!q_out) free(q);
+    if (!s_out) free(s);
+    if (!acc_out) free(acc);
+}
+
+void orc_bitlinear(const uint16_t* x, const float* g, const float* W, int64_t M,
+                   int64_t N, int64_t K, float eps, double* y, float* gamma_out,
+                   int8_t* w_out, int8_t* q_out, float* s_out, int32_t* acc_out) {
+    int8_t* w = w_out ? w_out : (int8_t*)malloc((size_t)(N * K));
+    float gamma = orc_absmean_gamma(W, N, K);
+    orc_ternarize(W, N, K, gamma, w);
+    orc_bitlinear_ternary(x, g, w, gamma, M, N, K, eps, y, q_out, s_out, acc_out);
+    if (gamma_out) *gamma_out = gamma;
+    if (!w_out) free(w);
+}
+
+/* [datacamp, "Các thành phần lõi: MLGRU và GLU"]: the input goes through two
+ * BitLinear layers, one output passes SiLU and is multiplied element-wise by
+ * the other, and a third BitLinear maps the result to the output;
+ * [jiqizhixin, "MatMul-free 语言模型架构"]: the GLU channel mixer is built from
+ * BitLinear only.  Readings: gate and up are one fused [2F][D] matrix with
+ * one gamma (gate = rows 0..F-1), SiLU(v) = v / (1 + exp(-v)) in fp64, and
+ * the product is stored as bf16 (activations between layers are BF16,
+ * [jiqizhixin, "MatMul-free 语言模型的扩展规律"]) before the down layer, which
+ * applies its own RMSNorm and quantisation. */
+void orc_glu_ternary(const uint16_t* x, const float* g_gu, const int8_t* w_gu,
+                     float gamma_gu, const float* g_down, const int8_t* w_down,
+                     float gamma_down, int64_t M, int64_t D, int64_t F, float eps,
+                     double* y, uint16_t* h_out) {
+    double* z = (double*)malloc((size_t)(M * 2 * F) * sizeof(double));
+    uint16_t* h = h_out ? h_out : (uint16_t*)malloc((size_t)(M * F) * sizeof(uint16_t));
+    orc_bitlinear_ternary(x, g_gu, w_gu, gamma_gu, M, 2 * F, D, eps, z, NULL, NULL, NULL);
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t f = 0; f < F; ++f) {
+            double gate = z[m * 2 * F + f];
+            double up = z[m * 2 * F + F + f];
+            double silu = gate / (1.0 + exp(-gate));
+            h[m * F + f] = orc_double_to_bf16(silu * up);
+        }
+    }
+    orc_bitlinear_ternary(h, g_down, w_down, gamma_down, M, D, F, eps, y, NULL, NULL, NULL);
+    free(z);
+    if (!h_out) free(h);
+}
+
+void orc_glu(const uint16_t* x, const float* g_gu, const float* W_gu,
+             const float* g_down, const float* W_down, int64_t M, int64_t D,
+             int64_t F, float eps, double* y, uint16_t* h_out) {
+    int8_t* w_gu = (int8_t*)malloc((size_t)(2 * F * D));
+    int8_t* w_down = (int8_t*)malloc((size_t)(D * F));
+    float gamma_gu = orc_absmean_gamma(W_gu, 2 * F, D);
+    float gamma_down = orc_absmean_gamma(W_down, D, F);
+    orc_ternarize(W_gu, 2 * F, D, gamma_gu, w_gu);
+    orc_ternarize(W_down, D, F, gamma_down, w_down);
+    orc_glu_ternary(x, g_gu, w_gu, gamma_gu, g_down, w_down, gamma_down, M, D, F, eps,
+                    y, h_out);
+    free(w_gu);
+    free(w_down);
+}

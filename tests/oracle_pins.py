@@ -1,0 +1,376 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Each pin_* function takes an oracle.Oracle and raises AssertionError when
+the oracle disagrees with something the pages or the mathematics fix: a
+closed form, an invariant, brute force in exact rational arithmetic, a
+library routine that computes the same plain definition, or the
+quantisation error bound.  test_oracle_pins.py runs them on the oracle;
+test_oracle_mutants.py runs them on deliberately altered builds of the
+oracle and checks that every alteration is caught by at least one pin.
+"""
+import math
+import os
+import sys
+from fractions import Fraction
+
+import numpy as np
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+import workloads as wl  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------------------
+# bf16 conversions
+# --------------------------------------------------------------------------
+
+def pin_bf16_widening(orc):
+    """bf16 is the top half of an fp32 pattern: 0x3F80 = 1, 0xC040 = -3,
+    0x0001 = 2^-133 (smallest subnormal), 0x7F7F = largest finite."""
+    assert orc.bf16_to_float(0x3F80) == 1.0
+    assert orc.bf16_to_float(0xC040) == -3.0
+    assert orc.bf16_to_float(0x0001) == np.float32(2.0 ** -133)
+    assert orc.bf16_to_float(0x7F7F) == np.float32((2 - 2 ** -7) * 2.0 ** 127)
+
+
+def pin_bf16_rounding(orc):
+    """Nearest bf16, ties to even: worked ties around 1.0 (spacing 2^-7),
+    then brute force on random doubles: the result is no farther than either
+    neighbouring bf16 value."""
+    one = 0x3F80
+    assert orc.double_to_bf16(1.0) == one
+    assert orc.double_to_bf16(1.0 + 2.0 ** -8) == one          # tie -> even (…80)
+    assert orc.double_to_bf16(1.0 + 3 * 2.0 ** -8) == one + 2  # tie -> even (…82)
+    assert orc.double_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == one + 1
+    assert orc.double_to_bf16(-1.0) == 0x8000 | one
+    assert orc.double_to_bf16(0.0) == 0
+    r = wl.rng(11, 0)
+    vals = r.standard_normal(400) * np.exp(r.uniform(-30, 30, 400))
+    for v in vals:
+        b = orc.double_to_bf16(v)
+        got = float(orc.bf16_to_float(b))
+        assert math.copysign(1.0, got) == math.copysign(1.0, v)
+        for nb in ((b + 1) & 0xFFFF, (b - 1) & 0xFFFF):
+            other = float(orc.bf16_to_float(nb))
+            if math.isfinite(other) and (nb & 0x7FFF) != 0x7F80:
+                assert abs(got - v) <= abs(other - v), (v, b, nb)
+
+
+# --------------------------------------------------------------------------
+# absmean weight scale and ternarisation
+# --------------------------------------------------------------------------
+
+def pin_gamma_closed_forms(orc):
+    """gamma of +-a everywhere is a; of zeros is 0; of N(0, sigma^2) is
+    sigma*sqrt(2/pi) within sampling error; equals NumPy's fp64 mean of |W|."""
+    a = np.float32(0.0371)
+    W = np.full((7, 48), a, np.float32)
+    W[::2, 1::3] *= -1
+    assert orc.gamma(W) == a
+    assert orc.gamma(np.zeros((3, 16), np.float32)) == 0.0
+    W = wl.w_normal(256, 512, 0.02, seed=5)
+    g = float(orc.gamma(W))
+    expect = 0.02 * math.sqrt(2 / math.pi)
+    sd = 0.02 * math.sqrt(1 - 2 / math.pi) / math.sqrt(W.size)
+    assert abs(g - expect) < 6 * sd, (g, expect)
+    assert orc.gamma(W) == np.float32(np.abs(W.astype(np.float64)).mean())
+
+
+def pin_ternarize_closed_forms(orc):
+    """Codes are in {-1,0,1}; +-a with a >> 1e-5 maps to +-1; 0 maps to 0;
+    thresholds at half the divisor; ties round to even (0.5 -> 0, 1.5 -> 2 ->
+    clipped 1); odd symmetry."""
+    gamma = np.float32(0.02)
+    d = np.float32(gamma + np.float32(1e-5))
+    cases = {
+        0.0: 0, 0.49: 0, 0.51: 1, -0.51: -1, 0.99: 1, 1.49: 1, 1.51: 1, 2.6: 1,
+        -7.0: -1, 0.5: 0, -0.5: 0, 1.5: 1,
+    }
+    vals = np.array([list(cases)], np.float64)
+    W = (vals * np.float64(d)).astype(np.float32)
+    # nudge the exact ties so that W / d is exactly the tie in fp32
+    for j, c in enumerate(cases):
+        if abs(c) in (0.5, 1.5):
+            W[0, j] = np.float32(np.float32(c) * d)
+            assert np.float32(W[0, j] / d) == np.float32(c)
+    w = orc.ternarize(W, gamma)
+    assert list(w[0]) == list(cases.values()), (list(w[0]), list(cases.values()))
+    a = np.float32(0.3)
+    W = np.array([[a, -a, a, 0]], np.float32)
+    assert list(orc.ternarize(W, orc.gamma(W))[0]) == [1, -1, 1, 0]
+    W = wl.w_normal(64, 128, seed=3)
+    g = orc.gamma(W)
+    assert np.array_equal(orc.ternarize(-W, g), -orc.ternarize(W, g))
+
+
+def pin_ternarize_statistics(orc):
+    """For N(0, sigma^2) weights the zero fraction is P(|Z| < sqrt(2/pi)/2)
+    = 0.3101 and the +1/-1 fractions are equal, within sampling error."""
+    W = wl.w_normal(512, 512, seed=7)
+    w = orc.ternarize(W, orc.gamma(W))
+    assert set(np.unique(w)) <= {-1, 0, 1}
+    z = float(np.mean(w == 0))
+    p0 = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    sd = math.sqrt(p0 * (1 - p0) / w.size)
+    assert abs(z - p0) < 6 * sd, (z, p0)
+    pos, neg = float(np.mean(w == 1)), float(np.mean(w == -1))
+    assert abs(pos - neg) < 6 * math.sqrt(0.35 / w.size)
+
+
+# --------------------------------------------------------------------------
+# packed storage
+# --------------------------------------------------------------------------
+
+def _golden_pack():
+    with open(os.path.join(GOLDEN, "pack_example.txt")) as f:
+        lines = [ln for ln in f if not ln.startswith("#") and ln.strip()]
+    kv = dict(ln.split(":", 1) for ln in lines)
+    w = np.array([int(t) for t in kv["weights"].split()], np.int8)[None, :]
+    b = np.array([int(t, 16) for t in kv["bytes"].split()], np.uint8)[None, :]
+    return w, b
+
+
+def pin_pack_golden(orc):
+    """The hand-worked row in tests/golden/pack_example.txt packs to its
+    bytes and unpacks back."""
+    w, b = _golden_pack()
+    assert np.array_equal(orc.pack(w), b), orc.pack(w)
+    assert np.array_equal(orc.unpack(b, 16), w)
+
+
+def pin_pack_roundtrip(orc):
+    """unpack(pack(w)) == w for random codes over several groups and rows;
+    the code 3 and K % 16 != 0 are rejected; a zero row packs to 0x55."""
+    r = wl.rng(21, 0)
+    w = r.integers(-1, 2, size=(9, 80)).astype(np.int8)
+    p = orc.pack(w)
+    assert p.shape == (9, 20)
+    assert np.array_equal(orc.unpack(p, 80), w)
+    assert np.all(orc.pack(np.zeros((2, 32), np.int8)) == 0x55)
+    bad = p.copy()
+    bad[4, 7] |= 0xC0
+    try:
+        orc.unpack(bad, 80)
+        raise AssertionError("code 3 accepted")
+    except ValueError:
+        pass
+    try:
+        orc.pack(np.zeros((1, 12), np.int8))
+        raise AssertionError("K=12 accepted")
+    except ValueError:
+        pass
+
+
+# --------------------------------------------------------------------------
+# RMSNorm + absmax quantisation
+# --------------------------------------------------------------------------
+
+def _round_half_even(fr):
+    fl = math.floor(fr)
+    d = fr - fl
+    if d > Fraction(1, 2):
+        return fl + 1
+    if d < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def pin_quant_exact_rational(orc):
+    """r cancels: q_k = round(127 * x_k g_k / max_j |x_j g_j|) exactly.
+    Brute force in rationals on small rows with a non-trivial gain; elements
+    within 1e-3 of a rounding tie are skipped (fp32 may fall either side)."""
+    M, K = 6, 48
+    x = wl.x_normal(M, K, seed=31, outlier_frac=0.05, outlier_scale=20.0)
+    g = wl.rms_weight(K, "random", seed=31)
+    q, s = orc.rmsnorm_quant(x, g)
+    xf = wl.bf16_bits_to_f32(x)
+    checked = 0
+    for m in range(M):
+        prod = [Fraction(float(xf[m, k])) * Fraction(float(g[k])) for k in range(K)]
+        amax = max(abs(p) for p in prod)
+        for k in range(K):
+            exact = 127 * prod[k] / amax
+            if abs(abs(exact - math.floor(exact)) - Fraction(1, 2)) < Fraction(1, 1000):
+                continue
+            assert q[m, k] == _round_half_even(exact), (m, k, float(exact), q[m, k])
+            checked += 1
+    assert checked > M * K * 0.95
+
+
+def pin_quant_scale_formula(orc):
+    """s = 127 / (max_k |x_k| * g_k * r), r = 1/sqrt(mean(x^2) + eps), eps
+    inside the root: checked in fp64 to 1e-6 on ordinary rows and on tiny
+    rows where mean(x^2) is comparable to eps."""
+    K = 64
+    x = wl.x_normal(4, K, seed=41)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    xf[2] *= 1e-3
+    xf[3] *= 3e-4
+    x = wl.f32_to_bf16_bits(xf.astype(np.float32))
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    g = wl.rms_weight(K, "random", seed=41).astype(np.float64)
+    for eps in (1e-6, 1e-3):
+        _, s = orc.rmsnorm_quant(x, g.astype(np.float32), eps)
+        for m in range(4):
+            r = 1.0 / math.sqrt(np.mean(xf[m] ** 2) + eps)
+            expect = 127.0 / np.max(np.abs(xf[m] * g) * r)
+            assert abs(s[m] / expect - 1) < 1e-6, (m, eps, s[m], expect)
+
+
+def pin_quant_invariants(orc):
+    """q in [-127, 127]; the row maximum maps to +-127; q(-x) = -q(x); a
+    zero row gives q = 0 and s = 127/1e-5; a constant row gives +-127."""
+    M, K = 8, 96
+    x = wl.x_student_t(M, K, seed=51)
+    g = wl.rms_weight(K, "random", seed=51)
+    q, s = orc.rmsnorm_quant(x, g)
+    assert q.min() >= -127 and q.max() <= 127
+    xg = np.abs(wl.bf16_bits_to_f32(x) * g)
+    for m in range(M):
+        assert abs(int(q[m, int(np.argmax(xg[m]))])) == 127
+    qn, sn = orc.rmsnorm_quant(x ^ np.uint16(0x8000), g)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    z = np.zeros((2, K), np.uint16)
+    z[1, :] = 0xBF80  # -1.0
+    qz, sz = orc.rmsnorm_quant(z, np.ones(K, np.float32))
+    assert np.all(qz[0] == 0) and sz[0] == np.float32(127.0) / np.float32(1e-5)
+    assert np.all(qz[1] == -127)
+
+
+# --------------------------------------------------------------------------
+# ternary accumulation and rescale
+# --------------------------------------------------------------------------
+
+def pin_accumulate_vs_integer_matmul(orc):
+    """The add/subtract loop equals the integer product sum_k q w in int64
+    (NumPy), bit for bit, on a non-square case."""
+    r = wl.rng(61, 0)
+    q = r.integers(-128, 128, size=(5, 96)).astype(np.int8)
+    w = r.integers(-1, 2, size=(7, 96)).astype(np.int8)
+    ref = q.astype(np.int64) @ w.astype(np.int64).T
+    assert np.array_equal(orc.accumulate(q, w), ref)
+
+
+def pin_accumulate_structure(orc):
+    """Identity weights return q; a single +1 at (n, k) copies column k; a
+    zero row gives a zero column; acc(-w) = -acc(w); permuting k in both
+    operands leaves acc unchanged."""
+    r = wl.rng(62, 0)
+    K = 32
+    q = r.integers(-127, 128, size=(4, K)).astype(np.int8)
+    assert np.array_equal(orc.accumulate(q, np.eye(K, dtype=np.int8)), q.astype(np.int32))
+    w = np.zeros((3, K), np.int8)
+    w[1, 5] = 1
+    w[2, 9] = -1
+    acc = orc.accumulate(q, w)
+    assert np.all(acc[:, 0] == 0)
+    assert np.array_equal(acc[:, 1], q[:, 5].astype(np.int32))
+    assert np.array_equal(acc[:, 2], -q[:, 9].astype(np.int32))
+    w = r.integers(-1, 2, size=(6, K)).astype(np.int8)
+    assert np.array_equal(orc.accumulate(q, -w), -orc.accumulate(q, w))
+    perm = r.permutation(K)
+    assert np.array_equal(orc.accumulate(q[:, perm], w[:, perm]), orc.accumulate(q, w))
+
+
+def pin_rescale_vs_dequantised_matmul(orc):
+    """y equals the fp64 product of the dequantised operands,
+    (q / s) @ (gamma * w)^T, to 1e-12 relative."""
+    M, N, K = 5, 11, 64
+    x = wl.x_normal(M, K, seed=71, outlier_frac=0.02, outlier_scale=20.0)
+    g = wl.rms_weight(K, "random", seed=71)
+    W = wl.w_normal(N, K, seed=71)
+    out = orc.bitlinear(x, g, W)
+    deq_x = out["q"].astype(np.float64) / out["s"].astype(np.float64)[:, None]
+    deq_w = out["w"].astype(np.float64) * float(out["gamma"])
+    ref = deq_x @ deq_w.T
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # zero weight row -> zero output column
+    W2 = W.copy()
+    W2[3] = 0
+    y2 = orc.bitlinear(x, g, W2)["y"]
+    assert np.all(y2[:, 3] == 0.0)
+
+
+def pin_bitlinear_error_bound(orc):
+    """The quantised layer stays within the int8 rounding bound of the
+    unquantised one: with xn the fp64 RMSNorm output and W~ = gamma * w,
+    |y - xn W~^T| <= gamma * sum_k |w_nk| * (0.5 / s + 1e-6 |xn_k|) per element.
+    Checked on a non-square layer with a non-trivial gain."""
+    M, N, K = 6, 40, 128
+    x = wl.x_normal(M, K, seed=81, outlier_frac=0.01, outlier_scale=20.0)
+    g = wl.rms_weight(K, "random", seed=81)
+    W = wl.w_normal(N, K, seed=81)
+    out = orc.bitlinear(x, g, W)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(xf ** 2, axis=1, keepdims=True) + 1e-6)
+    xn = xf * r * g.astype(np.float64)
+    wt = out["w"].astype(np.float64) * float(out["gamma"])
+    y_cont = xn @ wt.T
+    s = out["s"].astype(np.float64)
+    bound = (np.abs(wt) @ (0.5 / s[:, None] + 1e-6 * np.abs(xn)).T).T
+    err = np.abs(out["y"] - y_cont)
+    assert np.all(err <= bound * 1.0001 + 1e-30), float((err / (bound + 1e-30)).max())
+    # the bound is not vacuous: it sits well below the outputs, and the
+    # typical error (rounding errors average out) is a small fraction of them
+    assert np.median(np.abs(y_cont)) > 2 * np.median(bound)
+    assert np.median(err) < 0.05 * np.median(np.abs(y_cont))
+
+
+# --------------------------------------------------------------------------
+# GLU channel mixer
+# --------------------------------------------------------------------------
+
+def pin_glu_step(orc):
+    """h = bf16(SiLU(gate) * up) with gate the first F rows of the fused
+    projection, SiLU(v) = v * sigmoid(v) evaluated independently in NumPy,
+    and y = the down BitLinear of h.  Zero gate rows give h = 0 (SiLU(0) = 0)."""
+    M, D, F = 3, 64, 48
+    x = wl.x_normal(M, D, seed=91)
+    g_gu = wl.rms_weight(D, "random", seed=91)
+    g_dn = wl.rms_weight(F, "random", seed=92)
+    W_gu = wl.w_normal(2 * F, D, seed=91)
+    W_dn = wl.w_normal(D, F, seed=92)
+    out = orc.glu(x, g_gu, W_gu, g_dn, W_dn)
+    z = orc.bitlinear(x, g_gu, W_gu)["y"]
+    gate, up = z[:, :F], z[:, F:]
+    h_val = gate / (1.0 + np.exp(-gate)) * up
+    h_bits = np.array([[orc.double_to_bf16(v) for v in row] for row in h_val], np.uint16)
+    hf = wl.bf16_bits_to_f32(h_bits).astype(np.float64)
+    # NumPy's and libm's exp agree to an ulp or so: bf16 ties aside, equal
+    close = np.abs(wl.bf16_bits_to_f32(out["h"]) - hf) <= 2.0 ** -7 * np.abs(hf)
+    assert close.all()
+    assert np.mean(out["h"] == h_bits) > 0.999
+    y_ref = orc.bitlinear(out["h"], g_dn, W_dn)["y"]
+    assert np.array_equal(out["y"], y_ref)
+    W0 = W_gu.copy()
+    W0[:F] = 0
+    out0 = orc.glu(x, g_gu, W0, g_dn, W_dn)
+    assert np.all(wl.bf16_bits_to_f32(out0["h"]) == 0.0)
+    assert np.all(out0["y"] == 0.0)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+def run_all(lib_path=None):
+    """Run every pin against the library at lib_path; exit status 1 on the
+    first failure (used on altered oracle builds)."""
+    import oracle
+    orc = oracle.Oracle(oracle.lib(lib_path) if lib_path else None)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # noqa: BLE001  (a raise is a failed pin too)
+            failed.append((pin.__name__, str(e)[:200]))
+    for name, msg in failed:
+        print(f"FAILED {name}: {msg}")
+    return 1 if failed else 0
+
+
+if __name__ == "__main__":
+    sys.exit(run_all(sys.argv[1] if len(sys.argv) > 1 else None))

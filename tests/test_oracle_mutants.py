@@ -1,0 +1,55 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case rebuilds oracle.c on the CPU with one deliberate mistake (a wrong
+sign, index, constant, rounding, dropped term or swapped operand) into a
+temporary library and runs every pin against it in a child process.  The
+case passes when at least one pin fails (or the child dies).  The oracle
+source itself is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = [
+    ("gamma_drops_abs", "sum += fabs((double)W[n * K + k]);", "sum += (double)W[n * K + k];"),
+    ("gamma_wrong_count", "return (float)(sum / (double)(N * K));", "return (float)(sum / (double)(N * K + K));"),
+    ("ternarize_multiplies", "float t = rintf(W[n * K + k] / d);", "float t = rintf(W[n * K + k] * d);"),
+    ("ternarize_truncates", "float t = rintf(W[n * K + k] / d);", "float t = truncf(W[n * K + k] / d);"),
+    ("ternarize_rounds_half_away", "float t = rintf(W[n * K + k] / d);", "float t = roundf(W[n * K + k] / d);"),
+    ("pack_twos_complement", "uint8_t code = (uint8_t)(v + 1);", "uint8_t code = (uint8_t)(v & 3);"),
+    ("pack_group_transposed", "int64_t grp = k / 16, j = k % 16, t = j % 4;", "int64_t grp = k / 16, j = k % 16, t = j / 4;"),
+    ("rms_mean_off_by_one", "float ms = (float)(ss / (double)K);", "float ms = (float)(ss / (double)(K - 1));"),
+    ("rms_eps_outside_root", "float r = 1.0f / sqrtf(ms + eps);", "float r = 1.0f / (sqrtf(ms) + eps);"),
+    ("rms_drops_gain", "xn[k] = (orc_bf16_to_float(row[k]) * r) * g[k];", "xn[k] = (orc_bf16_to_float(row[k]) * r);"),
+    ("quant_128", "float scale = 127.0f / (amax > 1e-5f ? amax : 1e-5f);", "float scale = 128.0f / (amax > 1e-5f ? amax : 1e-5f);"),
+    ("quant_floor", "float v = rintf(xn[k] * scale);", "float v = floorf(xn[k] * scale);"),
+    ("quant_absmax_signed", "float a = fabsf(xn[k]);", "float a = xn[k];"),
+    ("accumulate_sign_swapped", "a -= q[m * K + k];", "a += q[m * K + k];"),
+    ("accumulate_wrong_row", "if (w[n * K + k] == 1)", "if (w[((n + 1) % N) * K + k] == 1)"),
+    ("rescale_inverted", "(double)acc[m * N + n] * (double)gamma / (double)s[m];", "(double)acc[m * N + n] * (double)s[m] / (double)gamma;"),
+    ("rescale_wrong_token", "(double)gamma / (double)s[m];", "(double)gamma / (double)s[(m + 1) % M];"),
+    ("glu_swaps_gate_up", "double gate = z[m * 2 * F + f];\n            double up = z[m * 2 * F + F + f];",
+     "double up = z[m * 2 * F + f];\n            double gate = z[m * 2 * F + F + f];"),
+    ("glu_sigmoid_not_silu", "double silu = gate / (1.0 + exp(-gate));", "double silu = 1.0 / (1.0 + exp(-gate));"),
+    ("bf16_truncates", "double n = rint(ldexp(a, -qe));", "double n = trunc(ldexp(a, -qe));"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutated = tmp_path / "oracle.c"
+    mutated.write_text(src.replace(old, new))
+    (tmp_path / "oracle.h").write_text(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-o", str(lib), str(mutated), "-lm"], check=True)
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), str(lib)],
+                         capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode != 0, f"mutant {name} survived every pin:\n{res.stdout}\n{res.stderr}"
