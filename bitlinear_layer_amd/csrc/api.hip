@@ -1,0 +1,338 @@
+// api.hip -- the C ABI declared in include/bitlinear.h: argument checks,
+// workspace carving and kernel dispatch.  No allocation, no host sync.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "bitlinear.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return BITLINEAR_OK;
+    return fail(BITLINEAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // any one matrix, in elements
+constexpr int64_t kMaxBatch = 65535;             // grid y limit
+
+#define CHECK(cond, status, ...)                   \
+    do {                                           \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+#define CHECK_SCALAR(p)                                                                    \
+    do {                                                                                   \
+        CHECK((p) != nullptr && aligned((p), 4), BITLINEAR_ERR_INVALID_ARG,                \
+              "%s must be a non-NULL 4-byte aligned device pointer", #p);                  \
+    } while (0)
+
+#define CHECK_PTR(p)                                                                      \
+    do {                                                                                  \
+        CHECK((p) != nullptr, BITLINEAR_ERR_INVALID_ARG, "%s must not be NULL", #p);      \
+        CHECK(aligned((p), 16), BITLINEAR_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p); \
+    } while (0)
+
+int check_k(int64_t K, const char* name) {
+    CHECK(K > 0, BITLINEAR_ERR_INVALID_ARG, "%s must be > 0 (got %lld)", name, (long long)K);
+    CHECK(K % 16 == 0, BITLINEAR_ERR_INVALID_ARG, "%s must be a multiple of 16 (got %lld)", name,
+          (long long)K);
+    CHECK(K <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "%s exceeds BITLINEAR_MAX_DIM", name);
+    return BITLINEAR_OK;
+}
+
+int check_rows(int64_t R, const char* name) {
+    CHECK(R >= 0, BITLINEAR_ERR_INVALID_ARG, "%s must be >= 0 (got %lld)", name, (long long)R);
+    CHECK(R <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "%s exceeds BITLINEAR_MAX_DIM", name);
+    return BITLINEAR_OK;
+}
+
+int check_eps(float eps) {
+    CHECK(isfinite(eps) && eps > 0.0f, BITLINEAR_ERR_INVALID_ARG, "eps must be finite and > 0");
+    return BITLINEAR_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return BITLINEAR_OK;
+    CHECK(ws != nullptr, BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    CHECK(aligned(ws, 256), BITLINEAR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    CHECK(ws_bytes >= need, BITLINEAR_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes,
+          need);
+    return BITLINEAR_OK;
+}
+
+#define TRY(expr)                        \
+    do {                                 \
+        int _st = (expr);                \
+        if (_st != BITLINEAR_OK) return _st; \
+    } while (0)
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool use_gemv(int64_t M, int kernel) {
+    if (kernel == BITLINEAR_KERNEL_GEMV) return true;
+    if (kernel == BITLINEAR_KERNEL_MFMA) return false;
+    return M <= 4;
+}
+
+int check_kernel(int kernel, int64_t M) {
+    CHECK(kernel == BITLINEAR_KERNEL_AUTO || kernel == BITLINEAR_KERNEL_GEMV ||
+              kernel == BITLINEAR_KERNEL_MFMA,
+          BITLINEAR_ERR_INVALID_ARG, "unknown kernel choice %d", kernel);
+    CHECK(kernel != BITLINEAR_KERNEL_GEMV || M <= bl::kGemvMaxM, BITLINEAR_ERR_INVALID_ARG,
+          "the GEMV kernel takes M <= %d (got %lld)", bl::kGemvMaxM, (long long)M);
+    return BITLINEAR_OK;
+}
+
+// Ternary product + epilogue for `batch` problems whose activation stage is
+// already in `act`.
+int run_product(const bl::ActStage& act, const uint8_t* packed, const float* gamma, int64_t M,
+                int64_t N, int64_t K, int64_t batch, void* out, bl::Epilogue ep, int kernel,
+                hipStream_t stream) {
+    bl::ProductArgs a;
+    a.q = act.q;
+    a.s = act.s;
+    a.sumq = act.sumq;
+    a.packed = packed;
+    a.gamma = gamma;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.batch = (int)batch;
+    a.out = out;
+    hipError_t e = use_gemv(M, kernel) ? bl::launch_gemv(a, ep, stream)
+                                       : bl::launch_gemm_mfma(a, ep, stream);
+    return hip_status(e, "ternary product launch");
+}
+
+int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                 const float* gamma, int64_t B, int64_t M, int64_t N, int64_t K, float eps,
+                 float* y, void* ws, size_t ws_bytes, void* stream, int kernel) {
+    TRY(check_rows(M, "M"));
+    TRY(check_rows(N, "N"));
+    TRY(check_k(K, "K"));
+    TRY(check_eps(eps));
+    CHECK(B >= 1 && B <= kMaxBatch, BITLINEAR_ERR_INVALID_ARG, "batch must be in [1, %lld]",
+          (long long)kMaxBatch);
+    CHECK(B * M <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "B*M exceeds BITLINEAR_MAX_DIM");
+    CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems,
+          BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    TRY(check_kernel(kernel, M));
+    if (M == 0 || N == 0) return BITLINEAR_OK;
+    CHECK_PTR(x);
+    CHECK_PTR(rms_weight);
+    CHECK_PTR(packed);
+    CHECK_SCALAR(gamma);
+    CHECK_PTR(y);
+    const size_t need = bl::act_stage_bytes(B * M, K);
+    TRY(check_ws(ws, ws_bytes, need));
+    hipStream_t st = as_stream(stream);
+    bl::ActStage act = bl::act_stage_carve(ws, B * M, K);
+    TRY(hip_status(bl::launch_quant(x, rms_weight, B * M, M, (int)K, eps, act, st), "quantise launch"));
+    return run_product(act, packed, gamma, M, N, K, B, y, bl::Epilogue::kF32, kernel, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return 1; }
+
+const char* bitlinear_last_error(void) { return g_last_error.c_str(); }
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+    if (N < 0 || K < 0 || K % 16 != 0) return 0;
+    return (size_t)(N * (K / 4));
+}
+
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return 0;
+    return (size_t)bl::round_up((int64_t)bl::gamma_partials(N * K) * 8, 256);
+}
+
+int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                           void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_k(K, "K"));
+    CHECK(N >= 1 && N <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "N must be in [1, MAX_DIM]");
+    CHECK(N * K <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    CHECK_PTR(W);
+    CHECK_PTR(packed);
+    CHECK_SCALAR(gamma);
+    TRY(check_ws(ws, ws_bytes, bitlinear_pack_workspace_bytes(N, K)));
+    hipStream_t st = as_stream(stream);
+    const int64_t total = N * K;
+    TRY(hip_status(bl::launch_gamma(W, total, static_cast<double*>(ws), gamma, st), "gamma launch"));
+    return hip_status(bl::launch_ternarize_pack(W, total, gamma, reinterpret_cast<uint32_t*>(packed), st),
+                      "pack launch");
+}
+
+int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, void* stream) {
+    TRY(check_k(K, "K"));
+    TRY(check_rows(N, "N"));
+    CHECK(N * K <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    if (N == 0) return BITLINEAR_OK;
+    CHECK_PTR(packed);
+    CHECK_PTR(w);
+    return hip_status(bl::launch_unpack(reinterpret_cast<const uint32_t*>(packed), N * K / 16, w,
+                                        as_stream(stream)),
+                      "unpack launch");
+}
+
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    (void)N;
+    if (M <= 0 || K <= 0) return 0;
+    return bl::act_stage_bytes(M, K);
+}
+
+size_t bitlinear_forward_batched_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K) {
+    (void)N;
+    if (B <= 0 || M <= 0 || K <= 0) return 0;
+    return bl::act_stage_bytes(B * M, K);
+}
+
+int bitlinear_forward(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                      const float* gamma, int64_t M, int64_t N, int64_t K, float eps, float* y,
+                      void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(x, rms_weight, packed, gamma, 1, M, N, K, eps, y, ws, ws_bytes, stream,
+                        BITLINEAR_KERNEL_AUTO);
+}
+
+int bitlinear_forward_ex(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                         const float* gamma, int64_t M, int64_t N, int64_t K, float eps, float* y,
+                         void* ws, size_t ws_bytes, void* stream, int kernel) {
+    return forward_impl(x, rms_weight, packed, gamma, 1, M, N, K, eps, y, ws, ws_bytes, stream,
+                        kernel);
+}
+
+int bitlinear_forward_batched(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                              const float* gamma, int64_t B, int64_t M, int64_t N, int64_t K,
+                              float eps, float* y, void* ws, size_t ws_bytes, void* stream) {
+    CHECK(B >= 1, BITLINEAR_ERR_INVALID_ARG, "B must be >= 1");
+    return forward_impl(x, rms_weight, packed, gamma, B, M, N, K, eps, y, ws, ws_bytes, stream,
+                        BITLINEAR_KERNEL_AUTO);
+}
+
+size_t bitlinear_glu_workspace_bytes(int64_t M, int64_t D, int64_t F) {
+    if (M <= 0 || D <= 0 || F <= 0) return 0;
+    return bl::act_stage_bytes(M, D) + (size_t)bl::round_up(M * F * 2, 256) +
+           bl::act_stage_bytes(M, F);
+}
+
+int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
+                         const float* gamma_gu, int64_t M, int64_t D, int64_t F, float eps,
+                         uint16_t* h, void* ws, size_t ws_bytes, void* stream, int kernel) {
+    TRY(check_rows(M, "M"));
+    TRY(check_k(D, "D"));
+    TRY(check_k(F, "F"));
+    TRY(check_eps(eps));
+    CHECK(M * D <= kMaxElems && 2 * F * D <= kMaxElems && M * F <= kMaxElems,
+          BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    TRY(check_kernel(kernel, M));
+    if (M == 0) return BITLINEAR_OK;
+    CHECK_PTR(x);
+    CHECK_PTR(rms_w_gu);
+    CHECK_PTR(packed_gu);
+    CHECK_SCALAR(gamma_gu);
+    CHECK_PTR(h);
+    TRY(check_ws(ws, ws_bytes, bl::act_stage_bytes(M, D)));
+    hipStream_t st = as_stream(stream);
+    bl::ActStage act = bl::act_stage_carve(ws, M, D);
+    TRY(hip_status(bl::launch_quant(x, rms_w_gu, M, M, (int)D, eps, act, st), "quantise launch"));
+    return run_product(act, packed_gu, gamma_gu, M, F, D, 1, h, bl::Epilogue::kGluBf16, kernel, st);
+}
+
+int bitlinear_glu_forward(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
+                          const float* gamma_gu, const float* rms_w_down,
+                          const uint8_t* packed_down, const float* gamma_down, int64_t M, int64_t D,
+                          int64_t F, float eps, float* y, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_rows(M, "M"));
+    TRY(check_k(D, "D"));
+    TRY(check_k(F, "F"));
+    TRY(check_eps(eps));
+    CHECK(M * D <= kMaxElems && 2 * F * D <= kMaxElems && M * F <= kMaxElems,
+          BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    if (M == 0) return BITLINEAR_OK;
+    CHECK_PTR(x);
+    CHECK_PTR(rms_w_gu);
+    CHECK_PTR(packed_gu);
+    CHECK_SCALAR(gamma_gu);
+    CHECK_PTR(rms_w_down);
+    CHECK_PTR(packed_down);
+    CHECK_SCALAR(gamma_down);
+    CHECK_PTR(y);
+    TRY(check_ws(ws, ws_bytes, bitlinear_glu_workspace_bytes(M, D, F)));
+    hipStream_t st = as_stream(stream);
+    char* base = static_cast<char*>(ws);
+    bl::ActStage act_x = bl::act_stage_carve(base, M, D);
+    base += bl::act_stage_bytes(M, D);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base);
+    base += bl::round_up(M * F * 2, 256);
+    bl::ActStage act_h = bl::act_stage_carve(base, M, F);
+    TRY(hip_status(bl::launch_quant(x, rms_w_gu, M, M, (int)D, eps, act_x, st), "quantise launch"));
+    TRY(run_product(act_x, packed_gu, gamma_gu, M, F, D, 1, h, bl::Epilogue::kGluBf16,
+                    BITLINEAR_KERNEL_AUTO, st));
+    TRY(hip_status(bl::launch_quant(h, rms_w_down, M, M, (int)F, eps, act_h, st), "quantise launch"));
+    return run_product(act_h, packed_down, gamma_down, M, D, F, 1, y, bl::Epilogue::kF32,
+                       BITLINEAR_KERNEL_AUTO, st);
+}
+
+int bitlinear_quantize(const uint16_t* x, const float* rms_weight, int64_t M, int64_t K, float eps,
+                       int8_t* q, float* s, void* stream) {
+    TRY(check_rows(M, "M"));
+    TRY(check_k(K, "K"));
+    TRY(check_eps(eps));
+    CHECK(M * K <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    if (M == 0) return BITLINEAR_OK;
+    CHECK_PTR(x);
+    CHECK_PTR(rms_weight);
+    CHECK_PTR(q);
+    CHECK_PTR(s);
+    // The stage call returns q and s only; a NULL code-sum pointer tells the
+    // kernel to skip that output.
+    bl::ActStage act;
+    act.q = q;
+    act.s = s;
+    act.sumq = nullptr;
+    return hip_status(bl::launch_quant(x, rms_weight, M, M, (int)K, eps, act, as_stream(stream)),
+                      "quantise launch");
+}
+
+int bitlinear_ternary_matmul_i32(const int8_t* q, const uint8_t* packed, int64_t M, int64_t N,
+                                 int64_t K, int32_t* acc, void* ws, size_t ws_bytes, void* stream,
+                                 int kernel) {
+    TRY(check_rows(M, "M"));
+    TRY(check_rows(N, "N"));
+    TRY(check_k(K, "K"));
+    CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems,
+          BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    TRY(check_kernel(kernel, M));
+    if (M == 0 || N == 0) return BITLINEAR_OK;
+    CHECK_PTR(q);
+    CHECK_PTR(packed);
+    CHECK_PTR(acc);
+    TRY(check_ws(ws, ws_bytes, bitlinear_forward_workspace_bytes(M, N, K)));
+    hipStream_t st = as_stream(stream);
+    bl::ActStage act = bl::act_stage_carve(ws, M, K);
+    act.q = const_cast<int8_t*>(q);
+    TRY(hip_status(bl::launch_row_sums(q, M, (int)K, act.sumq, st), "row sums launch"));
+    return run_product(act, packed, nullptr, M, N, K, 1, acc, bl::Epilogue::kI32, kernel, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// launch.h -- host-side launchers of the BitLinear kernels (library internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bl {
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Per-token activation stage produced by the quantisation kernel:
+// q int8 [rows][K] (row stride K), s fp32 [rows], sumq int32 [rows] = sum_k q.
+struct ActStage {
+    int8_t* q;
+    float* s;
+    int32_t* sumq;
+};
+
+// Workspace layout of one activation stage (each part 256-byte aligned).
+size_t act_stage_bytes(int64_t rows, int64_t K);
+ActStage act_stage_carve(void* base, int64_t rows, int64_t K);
+
+// --- weights ---------------------------------------------------------------
+// Number of fp64 partial sums the gamma reduction uses for `total` weights.
+int gamma_partials(int64_t total);
+hipError_t launch_gamma(const float* W, int64_t total, double* partial, float* gamma,
+                        hipStream_t stream);
+hipError_t launch_ternarize_pack(const float* W, int64_t total, const float* gamma,
+                                 uint32_t* packed, hipStream_t stream);
+hipError_t launch_unpack(const uint32_t* packed, int64_t nwords, int8_t* w, hipStream_t stream);
+
+// --- activations -------------------------------------------------------------
+// RMSNorm + absmax int8 over `rows` rows of length K.  Row r uses the RMSNorm
+// weight vector g + (r / rows_per_g) * K (rows_per_g = rows for one shared
+// vector).
+hipError_t launch_quant(const uint16_t* x, const float* g, int64_t rows, int64_t rows_per_g,
+                        int K, float eps, ActStage out, hipStream_t stream);
+// sumq[r] = sum_k q[r][k] for caller-provided codes.
+hipError_t launch_row_sums(const int8_t* q, int64_t rows, int K, int32_t* sumq,
+                           hipStream_t stream);
+
+// --- ternary product -----------------------------------------------------------
+enum class Epilogue {
+    kF32,      // y[m][n] = float(acc) * (gamma / s[m])
+    kI32,      // acc[m][n]
+    kGluBf16,  // h[m][f] = bf16(silu(z[m][f]) * z[m][F + f]), z = float(acc) * gamma / s
+};
+
+// One problem, or `batch` problems of the same shape laid out back to back:
+// problem b uses q rows [b*M, (b+1)*M), packed + b*Nrows*K/4, gamma + b and
+// out + b*M*Ncols, where Nrows = N (or 2F for the GLU) and Ncols = N (or F).
+struct ProductArgs {
+    const int8_t* q;
+    const float* s;
+    const int32_t* sumq;
+    const uint8_t* packed;
+    const float* gamma;
+    int M;      // tokens per problem
+    int N;      // output columns per problem (F for the GLU epilogue)
+    int K;
+    int batch;
+    void* out;  // float*, int32_t* or uint16_t* by epilogue
+};
+
+hipError_t launch_gemv(const ProductArgs& a, Epilogue ep, hipStream_t stream);
+hipError_t launch_gemm_mfma(const ProductArgs& a, Epilogue ep, hipStream_t stream);
+
+// Largest M the GEMV kernel takes.
+constexpr int kGemvMaxM = 8;
+
+}  // namespace bl

@@ -1,0 +1,224 @@
+/*
+ * bitlinear.h -- C ABI of the fused BitLinear layer for AMD Instinct MI355X
+ * (gfx950 / CDNA4).
+ *
+ * BitLinear is the dense layer of "Scalable MatMul-free Language Modeling".
+ * Sources, as the pages that describe it:
+ *   [ld246]      ld246.com article 1724132886152: section "三值权重的应用"
+ *                (weights are -1, 0 or +1, so +1 adds the input, -1
+ *                subtracts it and 0 skips it) and section "融合 BitLinear 层的
+ *                创新" (RMSNorm and quantisation fused in front of the product,
+ *                activations read from HBM once).
+ *   [jiqizhixin] jiqizhixin.com article 2024-06-11-4: section "具有三值权重的
+ *                MatMul-free 密集层" (ternary dense layer; Algorithm 1: RMSNorm
+ *                fused with quantisation and BitLinear), section "MatMul-free
+ *                语言模型架构" (GLU channel mixer built from BitLinear) and
+ *                section "MatMul-free 语言模型的扩展规律" (BitLinear activations
+ *                are BF16).
+ *   [datacamp]   datacamp.com/vi/blog/matmul-free-language-models: section
+ *                "Thay MatMul bằng các phép toán tam phân" (absmean
+ *                ternarisation of the weight matrix) and section "Các thành
+ *                phần lõi: MLGRU và GLU" (RMSNorm before quantisation, scaled
+ *                ternary accumulation, GLU = two BitLinear, SiLU on one,
+ *                element-wise product, third BitLinear).
+ *
+ * What the layer computes (per token row m of x, output feature n):
+ *   gamma   = mean_{n,k} |W[n][k]|                        (sum in fp64)
+ *   w[n][k] = clip(round(W[n][k] / (gamma + 1e-5)), -1, 1)   (fp32, ties even)
+ *   r_m     = 1 / sqrt(fp32(sum_k x^2 / K) + eps)         (sum in fp64)
+ *   xn      = (x * r_m) * rms_weight                      (fp32)
+ *   s_m     = 127 / max(max_k |xn|, 1e-5)                 (fp32)
+ *   q       = clip(round(xn * s_m), -128, 127)            (int8, ties even)
+ *   acc     = sum_k (w=+1: +q, w=-1: -q, w=0: skip)       (int32, exact)
+ *   y[m][n] = float(acc) * (gamma / s_m)                  (fp32)
+ * The pages print none of these formulas; the readings (divide rather than
+ * multiply by the mean, symmetric 127 scale, the 1e-5 guards, fp64 sums) are
+ * the library's, chosen as the plainest ones consistent with the pages.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to caller-owned memory; the library
+ *     allocates nothing and keeps no device state.  All matrices are
+ *     row-major and densely packed (row stride = row length).
+ *   - x and h are bf16 stored as uint16 bit patterns.  W and rms weights are
+ *     fp32.  gamma is a device fp32 scalar (no host round trip).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return; nothing synchronises the host.
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Return value: BITLINEAR_OK (0) or a bitlinear_status; on error nothing
+ *     was launched (argument and workspace checks run before any launch)
+ *     unless the status is BITLINEAR_ERR_HIP, and bitlinear_last_error()
+ *     returns a message (per calling thread).
+ *   - Checked before launch: non-NULL pointers for non-empty tensors; sizes
+ *     >= 0 with K > 0; K (and D, F for the GLU) multiples of 16; row counts
+ *     and K at most BITLINEAR_MAX_DIM; 16-byte alignment of every pointer
+ *     and 256-byte alignment of the workspace; workspace size; eps > 0 and
+ *     finite.  M = 0 or N = 0 is a valid empty call that does nothing.
+ *   - Inputs are read-only; outputs are fully overwritten; outputs, inputs
+ *     and workspace must not overlap.  NaN/Inf inputs are outside the
+ *     contract.
+ *   - Workspace: caller-provided device scratch of at least the size the
+ *     matching *_workspace_bytes() query returns for the same sizes.  Its
+ *     contents are undefined after a call; calls that share a workspace must
+ *     be ordered on one stream.
+ *   - Entry points are reentrant and thread-safe.
+ *
+ * Packed ternary format (the pages print none; this is the library's own):
+ *   - row n of the [N][K] ternary matrix occupies K/4 bytes, rows back to
+ *     back, so the packed matrix is [N][K/4] bytes; K % 16 == 0;
+ *   - along a row, weights go in groups of 16, one little-endian 32-bit word
+ *     per group (k = 16*grp + j -> word grp of the row);
+ *   - weight j = 4*i + t of a group sits in byte t of the word, bits
+ *     2i+1..2i (so (word >> 2i) & 0x03030303 yields weights 4i..4i+3 of the
+ *     group, one per byte, in order);
+ *   - the 2-bit code is w + 1: 0 -> -1, 1 -> 0, 2 -> +1; code 3 is never
+ *     written (bitlinear_unpack_weights decodes it to 2).
+ *   The offset code lets the kernels feed masked codes c = w + 1 straight
+ *   into int8 dot products and MFMA, since sum_k q w = sum_k q c - sum_k q,
+ *   with sum_k q computed once per token.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BITLINEAR_OK = 0,
+    BITLINEAR_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or eps   */
+    BITLINEAR_ERR_WORKSPACE = 2,   /* workspace missing or too small        */
+    BITLINEAR_ERR_UNSUPPORTED = 3, /* no GPU of the supported kind          */
+    BITLINEAR_ERR_HIP = 4          /* a HIP call or launch failed           */
+} bitlinear_status;
+
+/* Largest M, N, K, B*M, D or F accepted (keeps every in-kernel row index and
+ * every row length in 32 bits). */
+#define BITLINEAR_MAX_DIM ((int64_t)1 << 30)
+
+/* Kernel choice for bitlinear_forward_ex. */
+typedef enum {
+    BITLINEAR_KERNEL_AUTO = 0, /* by token count M (what bitlinear_forward does) */
+    BITLINEAR_KERNEL_GEMV = 1, /* weight-streaming GEMV (decode-shaped)          */
+    BITLINEAR_KERNEL_MFMA = 2  /* int8 MFMA tiles (prefill-shaped)               */
+} bitlinear_kernel;
+
+/* Version of this ABI (bumped on any incompatible change). */
+int bitlinear_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* bitlinear_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Weights.  [datacamp, "Thay MatMul bằng các phép toán tam phân"]: absmean
+ * ternarisation -- the matrix is scaled by its mean absolute value and each
+ * element rounded to the nearest of -1, 0, +1 ([ld246, "三值权重的应用"]).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the packed [N][K/4] matrix (0 when K % 16 != 0 or a size is
+ * negative). */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes for bitlinear_pack_weights (fp64 partial sums of |W|). */
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+
+/* W: device fp32 [N][K].  Writes packed (device, [N][K/4] bytes) and *gamma
+ * (device fp32 scalar, the mean |W|).  The fp64 sum of |W| is reduced in a
+ * fixed order, so the result is deterministic.  N >= 1. */
+int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                           float* gamma, void* ws, size_t ws_bytes, void* stream);
+
+/* Test/inspection: decode packed [N][K/4] into int8 [N][K] as code - 1.
+ * Valid codes give -1, 0, +1; the unused code 3 decodes to 2, outside the
+ * ternary set, so that a corrupted matrix is visible to a check of w. */
+int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* w,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Forward.  [jiqizhixin, "具有三值权重的 MatMul-free 密集层", Algorithm 1] and
+ * [ld246, "融合 BitLinear 层的创新"]: RMSNorm and activation quantisation
+ * fused in front of the ternary product; [datacamp, "Các thành phần lõi:
+ * MLGRU và GLU", panels "RMS norm" and "MatMul vs scaled ternary
+ * accumulation"]: normalise, quantise, accumulate with +/-, rescale.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes for bitlinear_forward / bitlinear_forward_ex (int8 codes
+ * [M][K rounded up to 64], per-token scale and code sum). */
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* x: bf16 [M][K]; rms_weight: fp32 [K]; packed: [N][K/4] (from
+ * bitlinear_pack_weights); gamma: device fp32 scalar; y: fp32 [M][N].
+ * Dispatches on M between the GEMV and the MFMA kernels. */
+int bitlinear_forward(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                      const float* gamma, int64_t M, int64_t N, int64_t K, float eps,
+                      float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* bitlinear_forward with an explicit kernel choice (results are identical
+ * for every choice; used to test and time each kernel on the same shape). */
+int bitlinear_forward_ex(const uint16_t* x, const float* rms_weight,
+                         const uint8_t* packed, const float* gamma, int64_t M, int64_t N,
+                         int64_t K, float eps, float* y, void* ws, size_t ws_bytes,
+                         void* stream, int kernel);
+
+/* B independent layers of the same shape in one launch sequence, e.g. one
+ * decode step through a stack of layers that do not depend on each other:
+ * x bf16 [B][M][K], rms_weight fp32 [B][K], packed [B][N][K/4], gamma fp32
+ * [B] (device), y fp32 [B][M][N].  Layer b computes exactly what
+ * bitlinear_forward computes on its slices.  B*M <= BITLINEAR_MAX_DIM. */
+size_t bitlinear_forward_batched_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K);
+int bitlinear_forward_batched(const uint16_t* x, const float* rms_weight,
+                              const uint8_t* packed, const float* gamma, int64_t B,
+                              int64_t M, int64_t N, int64_t K, float eps, float* y,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * GLU channel mixer.  [datacamp, "Các thành phần lõi: MLGRU và GLU"]: two
+ * BitLinear projections of the input, SiLU on one, element-wise product with
+ * the other, then a third BitLinear; [jiqizhixin, "MatMul-free 语言模型架构"].
+ * Readings: gate and up are one fused [2F][D] packed matrix with one gamma
+ * (rows 0..F-1 gate, F..2F-1 up); SiLU(v) = v / (1 + exp(-v)) in fp32; the
+ * product h is rounded to bf16 (the layer-boundary activation type) before
+ * the down projection, which applies its own RMSNorm and quantisation.
+ * ------------------------------------------------------------------------- */
+
+size_t bitlinear_glu_workspace_bytes(int64_t M, int64_t D, int64_t F);
+
+/* x: bf16 [M][D]; rms_w_gu: fp32 [D]; packed_gu: [2F][D/4]; gamma_gu:
+ * device scalar; rms_w_down: fp32 [F]; packed_down: [D][F/4]; gamma_down:
+ * device scalar; y: fp32 [M][D]. */
+int bitlinear_glu_forward(const uint16_t* x, const float* rms_w_gu,
+                          const uint8_t* packed_gu, const float* gamma_gu,
+                          const float* rms_w_down, const uint8_t* packed_down,
+                          const float* gamma_down, int64_t M, int64_t D, int64_t F,
+                          float eps, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* First half of the mixer alone: h = bf16(SiLU(gate) * up), h bf16 [M][F].
+ * Workspace: bitlinear_forward_workspace_bytes(M, 2F, D). */
+int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu,
+                         const uint8_t* packed_gu, const float* gamma_gu, int64_t M,
+                         int64_t D, int64_t F, float eps, uint16_t* h, void* ws,
+                         size_t ws_bytes, void* stream, int kernel);
+
+/* ---------------------------------------------------------------------------
+ * Stages (exposed so that each step can be compared on its own).
+ * ------------------------------------------------------------------------- */
+
+/* RMSNorm + per-token absmax quantisation: q int8 [M][K] and s fp32 [M]
+ * (q ~= s * RMSNorm(x)). */
+int bitlinear_quantize(const uint16_t* x, const float* rms_weight, int64_t M, int64_t K,
+                       float eps, int8_t* q, float* s, void* stream);
+
+/* Ternary accumulation alone: acc int32 [M][N] = sum_k q[m][k] * w[n][k]
+ * from int8 q [M][K] and packed [N][K/4].  Workspace:
+ * bitlinear_forward_workspace_bytes(M, N, K). */
+int bitlinear_ternary_matmul_i32(const int8_t* q, const uint8_t* packed, int64_t M,
+                                 int64_t N, int64_t K, int32_t* acc, void* ws,
+                                 size_t ws_bytes, void* stream, int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,107 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/bitlinear.h declares, sizes buffers as documented and rejects bad
+arguments before any launch (every call here fails validation or is an empty
+call, so no HIP work is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bitlinear_layer_amd as bl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # 16- and 256-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bl.lib()
+    decl = declared_functions()
+    assert len(decl) >= 15
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(bl.exported_symbols()) == decl
+
+
+def test_abi_version():
+    assert bl.bitlinear_abi_version() == 1
+
+
+def test_sizes():
+    assert bl.bitlinear_packed_bytes(2048, 2048) == 2048 * 512
+    assert bl.bitlinear_packed_bytes(7, 48) == 7 * 12
+    assert bl.bitlinear_packed_bytes(7, 12) == 0
+    assert bl.bitlinear_packed_bytes(-1, 16) == 0
+    fw = bl.bitlinear_forward_workspace_bytes(8192, 2048, 2048)
+    assert fw >= 8192 * 2048 + 2 * 8192 * 4 and fw % 256 == 0
+    assert bl.bitlinear_forward_workspace_bytes(0, 16, 16) == 0
+    assert bl.bitlinear_forward_batched_workspace_bytes(4, 1, 64, 64) == bl.bitlinear_forward_workspace_bytes(4, 64, 64)
+    gw = bl.bitlinear_glu_workspace_bytes(4096, 2048, 5632)
+    assert gw >= 4096 * 2048 + 4096 * 5632 * 2 + 4096 * 5632
+    assert bl.bitlinear_pack_workspace_bytes(2048, 2048) % 256 == 0
+
+
+def _fwd(x=FAKE, g=FAKE, p=FAKE, gamma=FAKE, M=4, N=64, K=64, eps=1e-6, y=FAKE, ws=FAKE,
+         ws_bytes=1 << 20, kernel=0):
+    return bl.lib().bitlinear_forward_ex(x, g, p, gamma, M, N, K, eps, y, ws, ws_bytes, None, kernel)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(y=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(gamma=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(x=MISALIGNED), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(K=12), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(K=0), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(M=-1), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(N=-5), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(M=1 << 31), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(eps=0.0), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(ws=None), bl.BITLINEAR_ERR_WORKSPACE),
+    (dict(ws_bytes=100), bl.BITLINEAR_ERR_WORKSPACE),
+    (dict(ws=MISALIGNED), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(kernel=7), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(kernel=1, M=9), bl.BITLINEAR_ERR_INVALID_ARG),
+])
+def test_forward_rejects(kwargs, status):
+    assert _fwd(**kwargs) == status
+    assert bl.bitlinear_last_error() != ""
+
+
+def test_forward_empty_is_ok():
+    assert _fwd(M=0, x=None, y=None, ws=None) == bl.BITLINEAR_OK
+    assert _fwd(N=0, x=None, y=None, ws=None) == bl.BITLINEAR_OK
+
+
+def test_other_entry_points_reject():
+    L = bl.lib()
+    assert L.bitlinear_pack_weights(FAKE, 64, 12, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_pack_weights(FAKE, 0, 16, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_pack_weights(FAKE, 64, 64, FAKE, FAKE, None, 0, None) == bl.BITLINEAR_ERR_WORKSPACE
+    assert L.bitlinear_unpack_weights(None, 4, 64, FAKE, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_forward_batched(FAKE, FAKE, FAKE, FAKE, 0, 1, 64, 64, 1e-6, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_forward_batched(FAKE, FAKE, FAKE, FAKE, 70000, 1, 64, 64, 1e-6, FAKE, FAKE, 1 << 30, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_glu_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 40, 1e-6, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_glu_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 1e-6, FAKE, FAKE, 16, None) == bl.BITLINEAR_ERR_WORKSPACE
+    assert L.bitlinear_glu_hidden(FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 1e-6, FAKE, FAKE, 16, None, 0) == bl.BITLINEAR_ERR_WORKSPACE
+    assert L.bitlinear_quantize(FAKE, FAKE, 4, 30, 1e-6, FAKE, FAKE, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_quantize(FAKE, FAKE, 4, 32, -1.0, FAKE, FAKE, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_ternary_matmul_i32(FAKE, FAKE, 4, 64, 64, FAKE, FAKE, 8, None, 0) == bl.BITLINEAR_ERR_WORKSPACE
+    assert L.bitlinear_ternary_matmul_i32(FAKE, None, 4, 64, 64, FAKE, FAKE, 1 << 20, None, 0) == bl.BITLINEAR_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(bl, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(bl, "_lib", None)
+    with pytest.raises(RuntimeError):
+        bl.lib()

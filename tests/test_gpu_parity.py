@@ -1,0 +1,346 @@
+"""Parity of the HIP library with the CPU oracle, element by element, on the
+same seeded inputs.  Every call goes through the C ABI (ctypes binding).
+
+Bars: packed bytes, gamma, int8 codes and int32 accumulations bit-exact
+(codes: at most 0.1% of elements one step off where an fp32 reduction-order
+tie flips); fp32 outputs within 1e-2 of the row maximum (and within the fp32
+rescale's 2^-22 relative on rows whose codes match); GLU hidden bf16 equal
+except rare one-ulp rounding flips.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_layer_amd as bl
+import workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+GEMV, MFMA = bl.BITLINEAR_KERNEL_GEMV, bl.BITLINEAR_KERNEL_MFMA
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------
+# weights
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(7, 48), (256, 256), (300, 2064), (2048, 2048), (11264, 2048),
+                                 (2048, 5632), (2560, 6912)])
+def test_pack_matches_oracle(N, K):
+    _say("pack", N, K)
+    W = wl.w_normal(N, K, seed=N + K)
+    packed, gamma = gu.pack_on_gpu(W)
+    g_ref = gu.orc().gamma(W)
+    w_ref = gu.orc().ternarize(W, g_ref)
+    assert gamma.cpu().numpy()[0] == g_ref
+    assert np.array_equal(packed.cpu().numpy(), gu.orc().pack(w_ref))
+    assert np.array_equal(bl.bitlinear_unpack_weights(packed, K).cpu().numpy(), w_ref)
+
+
+def test_pack_edge_cases():
+    _say("pack edge cases")
+    W = np.zeros((3, 32), np.float32)
+    packed, gamma = gu.pack_on_gpu(W)
+    assert gamma.item() == 0.0 and np.all(packed.cpu().numpy() == 0x55)
+    a = np.float32(0.25)
+    W = np.full((4, 64), a, np.float32)
+    W[1::2] *= -1
+    packed, gamma = gu.pack_on_gpu(W)
+    assert gamma.item() == a
+    w = bl.bitlinear_unpack_weights(packed, 64).cpu().numpy()
+    assert np.all(w[0::2] == 1) and np.all(w[1::2] == -1)
+    # exact rounding ties W/d = +-0.5 -> 0 and +-1.5 -> 2 -> 1 (ties to even)
+    W = wl.w_normal(16, 64, seed=9)
+    g_ref = gu.orc().gamma(W)
+    d = np.float32(g_ref + np.float32(1e-5))
+    W[0, :4] = [np.float32(0.5) * d, np.float32(-0.5) * d, np.float32(1.5) * d, np.float32(2.5) * d]
+    g_ref = gu.orc().gamma(W)
+    packed, gamma = gu.pack_on_gpu(W)
+    assert gamma.item() == g_ref
+    w_ref = gu.orc().ternarize(W, g_ref)
+    assert np.array_equal(bl.bitlinear_unpack_weights(packed, 64).cpu().numpy(), w_ref)
+
+
+def test_unpack_marks_unused_code():
+    p = torch.full((2, 4), 0xFF, dtype=torch.uint8, device=gu.DEV)
+    w = bl.bitlinear_unpack_weights(p, 16).cpu().numpy()
+    assert np.all(w == 2)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm + absmax quantisation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,recipe", [(1, 16, "normal"), (16, 256, "normal"), (5, 2048, "student_t3"),
+                                        (3, 5632, "normal"), (2, 6912, "normal"),
+                                        (4, 20000, "normal"), (300, 2048, "normal")])
+def test_quantize(M, K, recipe):
+    _say("quantize", M, K, recipe)
+    x = wl.make_x(M, K, recipe, seed=M * 7 + K, outlier_frac=0.01, outlier_scale=20.0)
+    g = wl.rms_weight(K, "random", seed=K)
+    q_ref, s_ref = gu.orc().rmsnorm_quant(x, g)
+    q, s = bl.bitlinear_quantize(gu.to_dev_bf16(x), gu.to_dev(g))
+    gu.assert_q_parity(q.cpu().numpy(), q_ref, s.cpu().numpy(), s_ref)
+
+
+def test_quantize_edge_rows():
+    _say("quantize edge rows")
+    K = 64
+    x = wl.x_normal(6, K, seed=3)
+    x[0] = 0                                    # zero row
+    x[1] = 0x3FC0                               # constant 1.5
+    x[2] = wl.f32_to_bf16_bits(np.full(K, 3e-4, np.float32))  # eps-dominated
+    x[3, 5] = 0x4B00                            # one huge outlier
+    x[4] = x[3] ^ np.uint16(0x8000)             # negated row
+    g = wl.rms_weight(K, "random", seed=1)
+    q_ref, s_ref = gu.orc().rmsnorm_quant(x, g, 1e-6)
+    q, s = bl.bitlinear_quantize(gu.to_dev_bf16(x), gu.to_dev(g), 1e-6)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+
+
+# --------------------------------------------------------------------------
+# ternary accumulation (int32, bit-exact)
+# --------------------------------------------------------------------------
+
+MATMUL = [(M, N, K) for M in (1, 3, 8, 130, 257) for (N, K) in ((7, 16), (129, 48), (300, 2064))]
+
+
+@pytest.mark.parametrize("M,N,K", MATMUL)
+def test_ternary_matmul_bit_exact(M, N, K):
+    r = wl.rng(M * 1000 + N, 0)
+    q = r.integers(-128, 128, size=(M, K)).astype(np.int8)
+    w = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    acc_ref = gu.orc().accumulate(q, w)
+    packed = gu.to_dev(gu.orc().pack(w))
+    kernels = [MFMA] + ([GEMV] if M <= 8 else [])
+    for kern in kernels:
+        _say("matmul", M, N, K, "kernel", kern)
+        acc = bl.bitlinear_ternary_matmul_i32(gu.to_dev(q), packed, kernel=kern).cpu().numpy()
+        assert np.array_equal(acc, acc_ref), (kern, int(np.abs(acc - acc_ref).max()))
+
+
+def test_ternary_matmul_extremes():
+    """All -128 codes against all -1 / all +1 weights at the largest K of the
+    workloads: the accumulator reaches +-128*6912 exactly."""
+    K, M, N = 6912, 8, 32
+    q = np.full((M, K), -128, np.int8)
+    w = np.ones((N, K), np.int8)
+    w[::2] = -1
+    acc_ref = gu.orc().accumulate(q, w)
+    packed = gu.to_dev(gu.orc().pack(w))
+    for kern in (GEMV, MFMA):
+        acc = bl.bitlinear_ternary_matmul_i32(gu.to_dev(q), packed, kernel=kern).cpu().numpy()
+        assert np.array_equal(acc, acc_ref)
+
+
+# --------------------------------------------------------------------------
+# end-to-end forward
+# --------------------------------------------------------------------------
+
+FORWARD = [
+    (16, 256, 256, "normal", 0.01, 20.0),   # single layer, 1% outliers x20
+    (1, 2048, 2048, "normal", 0.0, 1.0),    # decode, hidden 2048
+    (8, 2048, 2048, "normal", 0.0, 1.0),
+    (3, 129, 48, "student_t3", 0.0, 1.0),
+    (130, 300, 2064, "normal", 0.005, 50.0),
+    (257, 7, 16, "normal", 0.0, 1.0),
+]
+
+
+def _forward_case(M, N, K, recipe, of, os_, kernel, g_kind="random", seed=0):
+    x, W, g = gu.oracle_inputs(M, N, K, seed, recipe, of, os_, g_kind)
+    ref = gu.orc().bitlinear(x, g, W)
+    packed, gamma = gu.pack_on_gpu(W)
+    xd, gd = gu.to_dev_bf16(x), gu.to_dev(g)
+    y = bl.bitlinear_forward(xd, gd, packed, gamma, kernel=kernel).cpu().numpy()
+    q, s = bl.bitlinear_quantize(xd, gd)
+    q = q.cpu().numpy()
+    gu.assert_q_parity(q, ref["q"], s.cpu().numpy(), ref["s"])
+    rows_eq = np.all(q == ref["q"], axis=1)
+    return gu.assert_y_parity(y, ref["y"], rows_eq)
+
+
+@pytest.mark.parametrize("M,N,K,recipe,of,os_", FORWARD)
+def test_forward(M, N, K, recipe, of, os_):
+    kernels = [bl.BITLINEAR_KERNEL_AUTO, MFMA] + ([GEMV] if M <= 8 else [])
+    for kern in kernels:
+        _say("forward", M, N, K, recipe, "kernel", kern)
+        _forward_case(M, N, K, recipe, of, os_, kern)
+
+
+def test_forward_parity_config_ones_gain():
+    """The single-layer workload exactly as stated: gain 1, seed 0."""
+    _say("forward parity config")
+    _forward_case(16, 256, 256, "normal", 0.01, 20.0, bl.BITLINEAR_KERNEL_AUTO, g_kind="ones")
+
+
+def test_forward_batched():
+    B, N, K = 5, 256, 512
+    for M in (1, 3, 20):
+        _say("batched", B, M, N, K)
+        xs = [wl.x_normal(M, K, seed=10 + b) for b in range(B)]
+        Ws = [wl.w_normal(N, K, seed=20 + b) for b in range(B)]
+        gs = [wl.rms_weight(K, "random", seed=30 + b) for b in range(B)]
+        packs = [gu.pack_on_gpu(W) for W in Ws]
+        x = torch.stack([gu.to_dev_bf16(a) for a in xs])
+        g = torch.stack([gu.to_dev(a) for a in gs])
+        packed = torch.stack([p for p, _ in packs])
+        gamma = torch.cat([gm for _, gm in packs])
+        y = bl.bitlinear_forward_batched(x, g, packed, gamma).cpu().numpy()
+        for b in range(B):
+            ref = gu.orc().bitlinear(xs[b], gs[b], Ws[b])
+            gu.assert_y_parity(y[b], ref["y"])
+
+
+def test_forward_structural_zeros():
+    """A zero activation row gives a zero output row; a zero weight row gives
+    a zero output column; an all-zero matrix (gamma = 0) gives zeros."""
+    M, N, K = 12, 96, 128
+    x, W, g = gu.oracle_inputs(M, N, K, seed=4)
+    x[3] = 0
+    W[5] = 0
+    packed, gamma = gu.pack_on_gpu(W)
+    for kern in (GEMV, MFMA):
+        xs = x[:8] if kern == GEMV else x
+        y = bl.bitlinear_forward(gu.to_dev_bf16(xs), gu.to_dev(g), packed, gamma, kernel=kern).cpu().numpy()
+        assert np.all(y[3] == 0) and np.all(y[:, 5] == 0)
+    packed0, gamma0 = gu.pack_on_gpu(np.zeros((N, K), np.float32))
+    y = bl.bitlinear_forward(gu.to_dev_bf16(x), gu.to_dev(g), packed0, gamma0).cpu().numpy()
+    assert np.all(y == 0)
+
+
+def test_forward_empty_and_deterministic():
+    N, K = 64, 128
+    x, W, g = gu.oracle_inputs(40, N, K, seed=5)
+    packed, gamma = gu.pack_on_gpu(W)
+    xe = torch.empty((0, K), dtype=torch.int16, device=gu.DEV)
+    y = bl.bitlinear_forward(xe, gu.to_dev(g), packed, gamma)
+    assert y.shape == (0, N)
+    xd, gd = gu.to_dev_bf16(x), gu.to_dev(g)
+    y1 = bl.bitlinear_forward(xd, gd, packed, gamma).cpu().numpy()
+    y2 = bl.bitlinear_forward(xd, gd, packed, gamma).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_forward_rejects_bad_workspace():
+    N, K = 64, 128
+    x, W, g = gu.oracle_inputs(4, N, K, seed=6)
+    packed, gamma = gu.pack_on_gpu(W)
+    small = torch.empty(64, dtype=torch.uint8, device=gu.DEV)
+    with pytest.raises(bl.BitlinearError) as e:
+        bl.bitlinear_forward(gu.to_dev_bf16(x), gu.to_dev(g), packed, gamma, ws=small)
+    assert e.value.status == bl.BITLINEAR_ERR_WORKSPACE
+
+
+# --------------------------------------------------------------------------
+# GLU channel mixer
+# --------------------------------------------------------------------------
+
+def _glu_inputs(M, D, F, seed=0):
+    x = wl.x_normal(M, D, seed=seed)
+    g_gu = wl.rms_weight(D, "random", seed=seed + 1)
+    g_dn = wl.rms_weight(F, "random", seed=seed + 2)
+    W_gu = wl.w_normal(2 * F, D, seed=seed)
+    W_dn = wl.w_normal(D, F, seed=seed, stream=wl.STREAM_W2)
+    return x, g_gu, W_gu, g_dn, W_dn
+
+
+def assert_h_parity(h_gpu, h_ref):
+    """bf16 hidden: equal except rare one-ulp rounding flips (the oracle forms
+    SiLU(gate)*up in fp64, the kernel in fp32)."""
+    diff = np.abs(h_gpu.view(np.int16).astype(np.int32) - h_ref.view(np.int16).astype(np.int32))
+    assert diff.max(initial=0) <= 1 and np.mean(diff != 0) <= 1e-3, (diff.max(), np.mean(diff != 0))
+
+
+@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (5, 256, 320), (130, 256, 320), (3, 2048, 5632)])
+def test_glu_hidden(M, D, F):
+    x, g_gu, W_gu, g_dn, W_dn = _glu_inputs(M, D, F, seed=M)
+    ref = gu.orc().glu(x, g_gu, W_gu, g_dn, W_dn)
+    packed, gamma = gu.pack_on_gpu(W_gu)
+    kernels = [MFMA] + ([GEMV] if M <= 8 else [])
+    for kern in kernels:
+        _say("glu hidden", M, D, F, "kernel", kern)
+        h = bl.bitlinear_glu_hidden(gu.to_dev_bf16(x), gu.to_dev(g_gu), packed, gamma, kernel=kern)
+        assert_h_parity(gu.from_dev_bf16(h), ref["h"])
+
+
+@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (7, 256, 320), (200, 256, 320)])
+def test_glu_forward(M, D, F):
+    _say("glu forward", M, D, F)
+    x, g_gu, W_gu, g_dn, W_dn = _glu_inputs(M, D, F, seed=M + 100)
+    ref = gu.orc().glu(x, g_gu, W_gu, g_dn, W_dn)
+    pgu, ggu = gu.pack_on_gpu(W_gu)
+    pdn, gdn = gu.pack_on_gpu(W_dn)
+    y = bl.bitlinear_glu_forward(gu.to_dev_bf16(x), gu.to_dev(g_gu), pgu, ggu, gu.to_dev(g_dn), pdn,
+                                 gdn).cpu().numpy()
+    gu.assert_y_parity(y, ref["y"])
+
+
+# --------------------------------------------------------------------------
+# workloads at full size (oracle on sampled rows; rows are independent)
+# --------------------------------------------------------------------------
+
+def _sample_rows(M, n, seed):
+    r = wl.rng(seed, 9)
+    rows = set(r.choice(M, size=min(n, M), replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_full_decode_2048(M):
+    _say("full decode", M)
+    x, W, g = gu.oracle_inputs(M, 2048, 2048, seed=0, g_kind="ones")
+    ref = gu.orc().bitlinear(x, g, W)
+    packed, gamma = gu.pack_on_gpu(W)
+    y = bl.bitlinear_forward(gu.to_dev_bf16(x), gu.to_dev(g), packed, gamma).cpu().numpy()
+    gu.assert_y_parity(y, ref["y"], np.ones(M, bool))
+
+
+def _full_sampled(M, N, K, recipe, of, os_, nrows, kernel=bl.BITLINEAR_KERNEL_AUTO):
+    x, W, g = gu.oracle_inputs(M, N, K, seed=0, recipe=recipe, outlier_frac=of, outlier_scale=os_,
+                               g_kind="ones")
+    packed, gamma = gu.pack_on_gpu(W)
+    xd, gd = gu.to_dev_bf16(x), gu.to_dev(g)
+    y = bl.bitlinear_forward(xd, gd, packed, gamma, kernel=kernel).cpu().numpy()
+    q, s = bl.bitlinear_quantize(xd, gd)
+    rows = _sample_rows(M, nrows, M + N + K)
+    ref = gu.orc().bitlinear(x[rows], g, W)
+    assert gamma.item() == ref["gamma"]
+    qr = q.cpu().numpy()[rows]
+    gu.assert_q_parity(qr, ref["q"], s.cpu().numpy()[rows], ref["s"])
+    gu.assert_y_parity(y[rows], ref["y"], np.all(qr == ref["q"], axis=1))
+
+
+def test_full_prefill_8192():
+    _say("full prefill 8192x2048x2048")
+    _full_sampled(8192, 2048, 2048, "student_t3", 0.0, 1.0, 48)
+
+
+@pytest.mark.parametrize("M", [1, 64, 512, 4096])
+@pytest.mark.parametrize("K,N", [(2560, 2560), (2560, 6912), (6912, 2560)])
+def test_full_sweep_2560(M, K, N):
+    _say("sweep", M, K, N)
+    _full_sampled(M, N, K, "normal", 0.005, 50.0, 12)
+
+
+@pytest.mark.parametrize("M", [1, 4096])
+def test_full_glu_2048_5632(M):
+    _say("full glu", M)
+    D, F = 2048, 5632
+    x, g_gu, W_gu, g_dn, W_dn = _glu_inputs(M, D, F, seed=0)
+    g_gu = np.ones(D, np.float32)
+    g_dn = np.ones(F, np.float32)
+    pgu, ggu = gu.pack_on_gpu(W_gu)
+    pdn, gdn = gu.pack_on_gpu(W_dn)
+    xd = gu.to_dev_bf16(x)
+    y = bl.bitlinear_glu_forward(xd, gu.to_dev(g_gu), pgu, ggu, gu.to_dev(g_dn), pdn, gdn).cpu().numpy()
+    h = gu.from_dev_bf16(bl.bitlinear_glu_hidden(xd, gu.to_dev(g_gu), pgu, ggu))
+    rows = _sample_rows(M, 8, 77)
+    ref = gu.orc().glu(x[rows], g_gu, W_gu, g_dn, W_dn)
+    assert_h_parity(h[rows], ref["h"])
+    gu.assert_y_parity(y[rows], ref["y"])
