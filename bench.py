@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused BitLinear layer on one MI355X.
+
+Headline ("HBM GB/s at M=1"): one decode step through `--layers`
+independent BitLinear layers of the decode shape (M = 1 token, K = N = 2048,
+x bf16 ~ N(0,1), W ~ N(0, 0.02^2) ternarised and packed), issued as one
+bitlinear_forward_batched call.  1024 layers hold 1 GiB of packed weights,
+four times the 256 MB Infinity Cache, so the weights stream from HBM.
+value = algorithmic bytes moved per step / wall time per step, where the
+algorithmic bytes of one layer are N*K/4 (packed W) + 2*M*K (x) + 4*K (RMSNorm
+weight) + 4*M*N (y) + 4 (gamma).
+
+Also reported (`secondary`): the literal single-layer call at M=1, the M=8
+decode step, the 8192-token prefill (int8 TOPS of the MFMA product kernel,
+timed apart from the quantisation kernel), and the GLU mixer at M=1 and
+M=4096.  `roofline` is for the headline's dominant kernel, timed with HIP
+events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
+bounded sample of the headline workload on this host.
+
+One GPU only: `--gpus N` with N > 1 exits with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12        # B/s, MI355X HBM3E
+I8_PEAK = 5.0e15         # dense int8 MFMA ops/s, MI355X
+DEV = "cuda:0"
+
+
+def layer_bytes(M, N, K):
+    return N * K // 4 + 2 * M * K + 4 * K + 4 * M * N + 4
+
+
+def glu_bytes(M, D, F):
+    return layer_bytes(M, 2 * F, D) - 4 * M * 2 * F + layer_bytes(M, D, F) - 2 * M * F
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class EventTimer:
+    """HIP events around each call, on the stream the library launches on."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self.pairs = []
+
+    def __enter__(self):
+        self.start = self.torch.cuda.Event(enable_timing=True)
+        self.end = self.torch.cuda.Event(enable_timing=True)
+        self.start.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.end.record(self.stream)
+        self.pairs.append((self.start, self.end))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
+
+
+def timed_loop(torch, fn, steps, warmup, stream):
+    """Run fn warmup times, then exactly `steps` times between device
+    synchronisations.  Returns (wall ms per step, event ms per call)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    timer = EventTimer(torch, stream)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        with timer:
+            fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, timer.mean_ms()
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bitlinear_layer_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_file, digest):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_" + kernel_file.replace(".hip", "") + ".txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != digest:
+        return None
+    try:
+        return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+def make_decode_layers(torch, bl, wl, L, M, N, K, seed=0):
+    x = torch.from_numpy(wl.x_normal(L * M, K, seed=seed).view("int16")).to(DEV).view(L, M, K)
+    g = torch.ones((L, K), dtype=torch.float32, device=DEV)
+    packed = torch.empty((L, N, K // 4), dtype=torch.uint8, device=DEV)
+    gamma = torch.empty(L, dtype=torch.float32, device=DEV)
+    ws = torch.empty(bl.bitlinear_pack_workspace_bytes(N, K), dtype=torch.uint8, device=DEV)
+    for layer in range(L):
+        W = wl.w_normal_device(N, K, seed=seed, layer=layer, device=DEV)
+        bl.bitlinear_pack_weights(W, packed=packed[layer], gamma=gamma[layer:layer + 1], ws=ws)
+        del W
+    y = torch.empty((L, M, N), dtype=torch.float32, device=DEV)
+    wsf = torch.empty(bl.bitlinear_forward_batched_workspace_bytes(L, M, N, K), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    return x, g, packed, gamma, y, wsf
+
+
+def bench_decode(torch, bl, wl, L, M, N, K, steps, warmup, stream):
+    x, g, packed, gamma, y, ws = make_decode_layers(torch, bl, wl, L, M, N, K)
+
+    def step():
+        bl.bitlinear_forward_batched(x, g, packed, gamma, y=y, ws=ws)
+
+    wall, ev = timed_loop(torch, step, steps, warmup, stream)
+    nbytes = L * layer_bytes(M, N, K)
+    del x, g, packed, gamma, y, ws
+    torch.cuda.empty_cache()
+    return dict(layers=L, M=M, N=N, K=K, bytes_per_step=nbytes, wall_ms=wall, event_ms=ev,
+                gbps=nbytes / (wall * 1e-3) / 1e9, kernel_gbps=nbytes / (ev * 1e-3) / 1e9)
+
+
+def bench_single_layer(torch, bl, wl, M, N, K, steps, stream):
+    x, g, packed, gamma, y, ws = make_decode_layers(torch, bl, wl, 1, M, N, K, seed=1)
+    x, g, y = x[0], g[0], y[0]
+
+    def step():
+        bl.bitlinear_forward(x, g, packed[0], gamma[:1], y=y, ws=ws)
+
+    wall, ev = timed_loop(torch, step, steps, 20, stream)
+    nbytes = layer_bytes(M, N, K)
+    return dict(M=M, N=N, K=K, us_per_call_wall=wall * 1e3, us_per_call_event=ev * 1e3,
+                implied_gbps=nbytes / (ev * 1e-3) / 1e9)
+
+
+def bench_prefill(torch, bl, wl, M, N, K, steps, warmup, stream):
+    x = torch.from_numpy(wl.x_student_t(M, K, seed=0).view("int16")).to(DEV)
+    g = torch.ones(K, dtype=torch.float32, device=DEV)
+    packed, gamma = bl.bitlinear_pack_weights(torch.from_numpy(wl.w_normal(N, K, seed=0)).to(DEV))
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    ws = torch.empty(bl.bitlinear_forward_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    ops = 2.0 * M * N * K
+    wall_q, ev_q = timed_loop(torch, lambda: bl.bitlinear_prepare_activations(x, g, ws=ws), steps, warmup, stream)
+    wall_p, ev_p = timed_loop(torch, lambda: bl.bitlinear_forward_prepared(ws, packed, gamma, M, y=y),
+                              steps, warmup, stream)
+    wall_f, ev_f = timed_loop(torch, lambda: bl.bitlinear_forward(x, g, packed, gamma, y=y, ws=ws),
+                              steps, warmup, stream)
+    return dict(M=M, N=N, K=K, int8_ops=ops, quant_us=ev_q * 1e3, product_us=ev_p * 1e3,
+                product_tops=ops / (ev_p * 1e-3) / 1e12, product_frac_i8_peak=ops / (ev_p * 1e-3) / I8_PEAK,
+                forward_us=wall_f * 1e3, forward_tops=ops / (wall_f * 1e-3) / 1e12,
+                forward_bytes=layer_bytes(M, N, K))
+
+
+def bench_glu(torch, bl, wl, M, D, F, steps, warmup, stream):
+    x = torch.from_numpy(wl.x_normal(M, D, seed=0).view("int16")).to(DEV)
+    g_gu = torch.ones(D, dtype=torch.float32, device=DEV)
+    g_dn = torch.ones(F, dtype=torch.float32, device=DEV)
+    pgu, ggu = bl.bitlinear_pack_weights(wl.w_normal_device(2 * F, D, seed=0, layer=0, device=DEV))
+    pdn, gdn = bl.bitlinear_pack_weights(wl.w_normal_device(D, F, seed=0, layer=1, device=DEV))
+    y = torch.empty((M, D), dtype=torch.float32, device=DEV)
+    ws = torch.empty(bl.bitlinear_glu_workspace_bytes(M, D, F), dtype=torch.uint8, device=DEV)
+    wall, ev = timed_loop(torch, lambda: bl.bitlinear_glu_forward(x, g_gu, pgu, ggu, g_dn, pdn, gdn, y=y, ws=ws),
+                          steps, warmup, stream)
+    ops = 2.0 * M * D * F * 3
+    nbytes = glu_bytes(M, D, F)
+    return dict(M=M, D=D, F=F, us=wall * 1e3, gbps=nbytes / (wall * 1e-3) / 1e9,
+                tops=ops / (wall * 1e-3) / 1e12, bytes=nbytes, int8_ops=ops)
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline
+# --------------------------------------------------------------------------
+
+def cpu_baseline(wl, M, N, K, seconds):
+    import numpy as np
+    import oracle
+
+    orc = oracle.Oracle()
+    pool = []
+    for i in range(4):
+        x = wl.x_normal(M, K, seed=100 + i)
+        W = wl.w_normal(N, K, seed=100 + i)
+        gm = orc.gamma(W)
+        pool.append((x, orc.ternarize(W, gm), gm))
+    g = np.ones(K, np.float32)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        x, w, gm = pool[n % len(pool)]
+        orc.bitlinear_ternary(x, g, w, gm)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and n >= 4:
+            break
+    nbytes = n * layer_bytes(M, N, K)
+    return dict(value=nbytes / el / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"{n} layers of the M={M} K={K} N={N} decode workload (4 seeded layers cycled), "
+                       f"single thread, {el:.1f} s", seconds=el)
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the layer is measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bitlinear_layer_amd as bl
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    bl.lib()
+    stream = torch.cuda.current_stream()
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=DEV)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    M, N, K = 1, 2048, 2048
+    log(f"[bench] decode M={M} K={K} N={N} x {args.layers} layers: {args.steps} steps")
+    head = bench_decode(torch, bl, wl, args.layers, M, N, K, args.steps, args.warmup, stream)
+    log(f"[bench] decode: {head['gbps']:.1f} GB/s wall, {head['kernel_gbps']:.1f} GB/s by events")
+
+    secondary = {}
+    if not args.no_secondary:
+        log("[bench] single layer M=1")
+        secondary["decode_m1_single_layer"] = bench_single_layer(torch, bl, wl, 1, N, K, 200, stream)
+        log("[bench] decode M=8")
+        secondary["decode_m8_layers"] = bench_decode(torch, bl, wl, args.layers, 8, N, K, max(5, args.steps // 2),
+                                                     args.warmup, stream)
+        log("[bench] prefill 8192")
+        secondary["prefill_8192"] = bench_prefill(torch, bl, wl, 8192, 2048, 2048, max(10, args.steps // 2),
+                                                  args.warmup, stream)
+        log("[bench] glu")
+        secondary["glu_m1"] = bench_glu(torch, bl, wl, 1, 2048, 5632, 100, args.warmup, stream)
+        secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
+                                           args.warmup, stream)
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] cpu oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(wl, M, N, K, args.cpu_seconds)
+        cpu.pop("seconds")
+
+    kernels = ["gemv.hip", "quant.hip"]
+    digest = source_digest(*kernels)
+    traffic = read_traffic("gemv.hip", digest)
+    achieved = head["bytes_per_step"] / (head["event_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": "fused BitLinear: HBM GB/s at M=1 and int8 TOPS at M=8192 (% of roofline)",
+        "value": round(head["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"decode step M=1 K=2048 N=2048 through {args.layers} independent layers",
+                   "M": M, "K": K, "N": N, "layers": args.layers,
+                   "bytes_per_step": head["bytes_per_step"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / (HBM_PEAK / 1e9), 4),
+                     "traffic": None if traffic is None else traffic * 1.0,
+                     "kernel": "decode step (batched layers)", "source_sha256_16": digest},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "bitlinear_forward_workspace_bytes": (_S, [_I, _I, _I]),
     "bitlinear_forward": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P]),
     "bitlinear_forward_ex": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P, _INT]),
+    "bitlinear_prepare_activations": (_INT, [_P, _P, _I, _I, _F, _P, _S, _P]),
+    "bitlinear_forward_prepared": (_INT, [_P, _P, _I, _I, _I, _P, _P, _S, _P, _INT]),
     "bitlinear_forward_batched_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "bitlinear_forward_batched": (_INT, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
     "bitlinear_glu_workspace_bytes": (_S, [_I, _I, _I]),
@@ -194,6 +196,31 @@ def bitlinear_forward(x, rms_weight, packed, gamma, eps=1e-6, y=None, ws=None, s
     _check(lib().bitlinear_forward_ex(_ptr(x), _ptr(rms_weight), _ptr(packed), _ptr(gamma), M, N, K,
                                       float(eps), _ptr(y), _ptr(ws), nbytes, _stream(stream),
                                       int(kernel)))
+    return y
+
+
+def bitlinear_prepare_activations(x, rms_weight, eps=1e-6, N=0, ws=None, stream=None):
+    """Quantise x [M, K] into a workspace (returned) for bitlinear_forward_prepared."""
+    _dev(x, "x", _BF16, 2)
+    _dev(rms_weight, "rms_weight", (torch.float32,), 1)
+    M, K = x.shape
+    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, N, K), ws, x.device)
+    _check(lib().bitlinear_prepare_activations(_ptr(x), _ptr(rms_weight), M, K, float(eps), _ptr(ws),
+                                               nbytes, _stream(stream)))
+    return ws
+
+
+def bitlinear_forward_prepared(ws, packed, gamma, M, y=None, stream=None,
+                               kernel=BITLINEAR_KERNEL_AUTO):
+    """Ternary product + rescale from a prepared workspace -> y fp32 [M, N]."""
+    _dev(packed, "packed", (torch.uint8,), 2)
+    _dev(gamma, "gamma", (torch.float32,))
+    N, K = packed.shape[0], packed.shape[1] * 4
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=packed.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().bitlinear_forward_prepared(_ptr(packed), _ptr(gamma), M, N, K, _ptr(y), _ptr(ws),
+                                            nbytes, _stream(stream), int(kernel)))
     return y
 
 

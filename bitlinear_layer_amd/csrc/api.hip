@@ -221,6 +221,40 @@ int bitlinear_forward_ex(const uint16_t* x, const float* rms_weight, const uint8
                         kernel);
 }
 
+int bitlinear_prepare_activations(const uint16_t* x, const float* rms_weight, int64_t M, int64_t K,
+                                  float eps, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_rows(M, "M"));
+    TRY(check_k(K, "K"));
+    TRY(check_eps(eps));
+    CHECK(M * K <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    if (M == 0) return BITLINEAR_OK;
+    CHECK_PTR(x);
+    CHECK_PTR(rms_weight);
+    TRY(check_ws(ws, ws_bytes, bl::act_stage_bytes(M, K)));
+    bl::ActStage act = bl::act_stage_carve(ws, M, K);
+    return hip_status(bl::launch_quant(x, rms_weight, M, M, (int)K, eps, act, as_stream(stream)),
+                      "quantise launch");
+}
+
+int bitlinear_forward_prepared(const uint8_t* packed, const float* gamma, int64_t M, int64_t N,
+                               int64_t K, float* y, void* ws, size_t ws_bytes, void* stream,
+                               int kernel) {
+    TRY(check_rows(M, "M"));
+    TRY(check_rows(N, "N"));
+    TRY(check_k(K, "K"));
+    CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems,
+          BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    TRY(check_kernel(kernel, M));
+    if (M == 0 || N == 0) return BITLINEAR_OK;
+    CHECK_PTR(packed);
+    CHECK_SCALAR(gamma);
+    CHECK_PTR(y);
+    TRY(check_ws(ws, ws_bytes, bl::act_stage_bytes(M, K)));
+    bl::ActStage act = bl::act_stage_carve(ws, M, K);
+    return run_product(act, packed, gamma, M, N, K, 1, y, bl::Epilogue::kF32, kernel,
+                       as_stream(stream));
+}
+
 int bitlinear_forward_batched(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
                               const float* gamma, int64_t B, int64_t M, int64_t N, int64_t K,
                               float eps, float* y, void* ws, size_t ws_bytes, void* stream) {

@@ -162,6 +162,21 @@ int bitlinear_forward_ex(const uint16_t* x, const float* rms_weight,
                          int64_t K, float eps, float* y, void* ws, size_t ws_bytes,
                          void* stream, int kernel);
 
+/* The two halves of bitlinear_forward, for callers that feed one input to
+ * several weight matrices (quantise once, multiply many times) or that time
+ * the halves apart.  bitlinear_prepare_activations runs RMSNorm + absmax
+ * quantisation of x [M][K] into the workspace (a private layout, sized by
+ * bitlinear_forward_workspace_bytes(M, N, K)); bitlinear_forward_prepared
+ * then runs the ternary product and rescale from that workspace into y
+ * [M][N].  The workspace must not be modified in between; the pair computes
+ * exactly what bitlinear_forward computes. */
+int bitlinear_prepare_activations(const uint16_t* x, const float* rms_weight, int64_t M,
+                                  int64_t K, float eps, void* ws, size_t ws_bytes,
+                                  void* stream);
+int bitlinear_forward_prepared(const uint8_t* packed, const float* gamma, int64_t M,
+                               int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
+                               void* stream, int kernel);
+
 /* B independent layers of the same shape in one launch sequence, e.g. one
  * decode step through a stack of layers that do not depend on each other:
  * x bf16 [B][M][K], rms_weight fp32 [B][K], packed [B][N][K/4], gamma fp32

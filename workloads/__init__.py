@@ -83,3 +83,14 @@ def make_x(M, K, recipe="normal", seed=0, outlier_frac=0.0, outlier_scale=1.0):
     if recipe == "student_t3":
         return x_student_t(M, K, 3, seed)
     raise ValueError(recipe)
+
+
+def w_normal_device(N, K, sigma=0.02, seed=0, layer=0, device="cuda"):
+    """fp32 [N, K] ~ N(0, sigma^2) drawn on the GPU with torch's seeded
+    generator (Philox), for benchmarks that need many distinct layers; layer
+    selects an independent stream."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1_000_003 + int(layer) * 7919 + STREAM_W)
+    return torch.randn((N, K), generator=gen, device=device, dtype=torch.float32) * sigma
