@@ -289,9 +289,8 @@ def main():
         cpu = cpu_baseline(wl, M, N, K, args.cpu_seconds)
         cpu.pop("seconds")
 
-    kernels = ["gemv.hip", "quant.hip"]
-    digest = source_digest(*kernels)
-    traffic = read_traffic("gemv.hip", digest)
+    digest = source_digest("decode.hip")
+    traffic = read_traffic("decode.hip", digest)
     achieved = head["bytes_per_step"] / (head["event_ms"] * 1e-3) / 1e9
     out = {
         "metric": "fused BitLinear: HBM GB/s at M=1 and int8 TOPS at M=8192 (% of roofline)",
@@ -312,7 +311,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / (HBM_PEAK / 1e9), 4),
                      "traffic": None if traffic is None else traffic * 1.0,
-                     "kernel": "decode step (batched layers)", "source_sha256_16": digest},
+                     "kernel": "bl::decode_kernel (fused quantise + GEMV, one launch per step)", "source_sha256_16": digest},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

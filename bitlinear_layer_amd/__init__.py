@@ -31,6 +31,7 @@ BITLINEAR_ERR_HIP = 4
 BITLINEAR_KERNEL_AUTO = 0
 BITLINEAR_KERNEL_GEMV = 1
 BITLINEAR_KERNEL_MFMA = 2
+BITLINEAR_KERNEL_DECODE = 3
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -40,6 +41,7 @@ _INT = ctypes.c_int
 
 _SIGNATURES = {
     "bitlinear_abi_version": (_INT, []),
+    "bitlinear_decode_supported": (_INT, [_I, _I]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
     "bitlinear_packed_bytes": (_S, [_I, _I]),
     "bitlinear_pack_workspace_bytes": (_S, [_I, _I]),
@@ -89,6 +91,10 @@ def exported_symbols():
 
 def bitlinear_abi_version():
     return lib().bitlinear_abi_version()
+
+
+def bitlinear_decode_supported(M, K):
+    return bool(lib().bitlinear_decode_supported(M, K))
 
 
 def bitlinear_last_error():

@@ -86,19 +86,48 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Kernel for the product from a quantised stage: the GEMV up to 4 tokens,
+// the MFMA tiles above (or whatever the caller forces).
 bool use_gemv(int64_t M, int kernel) {
     if (kernel == BITLINEAR_KERNEL_GEMV) return true;
     if (kernel == BITLINEAR_KERNEL_MFMA) return false;
     return M <= 4;
 }
 
-int check_kernel(int kernel, int64_t M) {
+// Whether a full forward runs as the single fused decode kernel.
+bool use_decode(int64_t M, int64_t K, int kernel) {
+    if (kernel == BITLINEAR_KERNEL_DECODE) return true;
+    return kernel == BITLINEAR_KERNEL_AUTO && bl::decode_supported((int)M, (int)K);
+}
+
+int check_kernel(int kernel, int64_t M, int64_t K, bool fused_allowed) {
     CHECK(kernel == BITLINEAR_KERNEL_AUTO || kernel == BITLINEAR_KERNEL_GEMV ||
-              kernel == BITLINEAR_KERNEL_MFMA,
-          BITLINEAR_ERR_INVALID_ARG, "unknown kernel choice %d", kernel);
+              kernel == BITLINEAR_KERNEL_MFMA || (fused_allowed && kernel == BITLINEAR_KERNEL_DECODE),
+          BITLINEAR_ERR_INVALID_ARG, "kernel choice %d not available here", kernel);
     CHECK(kernel != BITLINEAR_KERNEL_GEMV || M <= bl::kGemvMaxM, BITLINEAR_ERR_INVALID_ARG,
           "the GEMV kernel takes M <= %d (got %lld)", bl::kGemvMaxM, (long long)M);
+    CHECK(kernel != BITLINEAR_KERNEL_DECODE || M == 0 || bl::decode_supported((int)M, (int)K),
+          BITLINEAR_ERR_INVALID_ARG, "the fused decode kernel does not take M=%lld, K=%lld",
+          (long long)M, (long long)K);
     return BITLINEAR_OK;
+}
+
+int run_decode(const uint16_t* x, const float* g, int64_t g_stride, const uint8_t* packed,
+               const float* gamma, int64_t B, int64_t M, int64_t N, int64_t K, float eps, void* out,
+               bl::Epilogue ep, hipStream_t stream) {
+    bl::DecodeArgs d;
+    d.x = x;
+    d.g = g;
+    d.g_stride = g_stride;
+    d.packed = packed;
+    d.gamma = gamma;
+    d.M = (int)M;
+    d.N = (int)N;
+    d.K = (int)K;
+    d.batch = (int)B;
+    d.eps = eps;
+    d.out = out;
+    return hip_status(bl::launch_decode(d, ep, stream), "fused decode launch");
 }
 
 // Ternary product + epilogue for `batch` problems whose activation stage is
@@ -134,7 +163,7 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
     CHECK(B * M <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "B*M exceeds BITLINEAR_MAX_DIM");
     CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems,
           BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    TRY(check_kernel(kernel, M));
+    TRY(check_kernel(kernel, M, K, true));
     if (M == 0 || N == 0) return BITLINEAR_OK;
     CHECK_PTR(x);
     CHECK_PTR(rms_weight);
@@ -144,6 +173,9 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
     const size_t need = bl::act_stage_bytes(B * M, K);
     TRY(check_ws(ws, ws_bytes, need));
     hipStream_t st = as_stream(stream);
+    if (use_decode(M, K, kernel))
+        return run_decode(x, rms_weight, B > 1 ? K : 0, packed, gamma, B, M, N, K, eps, y,
+                          bl::Epilogue::kF32, st);
     bl::ActStage act = bl::act_stage_carve(ws, B * M, K);
     TRY(hip_status(bl::launch_quant(x, rms_weight, B * M, M, (int)K, eps, act, st), "quantise launch"));
     return run_product(act, packed, gamma, M, N, K, B, y, bl::Epilogue::kF32, kernel, st);
@@ -154,6 +186,11 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
 extern "C" {
 
 int bitlinear_abi_version(void) { return 1; }
+
+int bitlinear_decode_supported(int64_t M, int64_t K) {
+    if (M < 1 || K < 1 || M > BITLINEAR_MAX_DIM || K > BITLINEAR_MAX_DIM) return 0;
+    return bl::decode_supported((int)M, (int)K) ? 1 : 0;
+}
 
 const char* bitlinear_last_error(void) { return g_last_error.c_str(); }
 
@@ -244,7 +281,7 @@ int bitlinear_forward_prepared(const uint8_t* packed, const float* gamma, int64_
     TRY(check_k(K, "K"));
     CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems,
           BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    TRY(check_kernel(kernel, M));
+    TRY(check_kernel(kernel, M, K, false));
     if (M == 0 || N == 0) return BITLINEAR_OK;
     CHECK_PTR(packed);
     CHECK_SCALAR(gamma);
@@ -278,7 +315,7 @@ int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu, const uint8_t
     TRY(check_eps(eps));
     CHECK(M * D <= kMaxElems && 2 * F * D <= kMaxElems && M * F <= kMaxElems,
           BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    TRY(check_kernel(kernel, M));
+    TRY(check_kernel(kernel, M, D, true));
     if (M == 0) return BITLINEAR_OK;
     CHECK_PTR(x);
     CHECK_PTR(rms_w_gu);
@@ -287,6 +324,9 @@ int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu, const uint8_t
     CHECK_PTR(h);
     TRY(check_ws(ws, ws_bytes, bl::act_stage_bytes(M, D)));
     hipStream_t st = as_stream(stream);
+    if (use_decode(M, D, kernel))
+        return run_decode(x, rms_w_gu, 0, packed_gu, gamma_gu, 1, M, F, D, eps, h,
+                          bl::Epilogue::kGluBf16, st);
     bl::ActStage act = bl::act_stage_carve(ws, M, D);
     TRY(hip_status(bl::launch_quant(x, rms_w_gu, M, M, (int)D, eps, act, st), "quantise launch"));
     return run_product(act, packed_gu, gamma_gu, M, F, D, 1, h, bl::Epilogue::kGluBf16, kernel, st);
@@ -319,9 +359,16 @@ int bitlinear_glu_forward(const uint16_t* x, const float* rms_w_gu, const uint8_
     uint16_t* h = reinterpret_cast<uint16_t*>(base);
     base += bl::round_up(M * F * 2, 256);
     bl::ActStage act_h = bl::act_stage_carve(base, M, F);
-    TRY(hip_status(bl::launch_quant(x, rms_w_gu, M, M, (int)D, eps, act_x, st), "quantise launch"));
-    TRY(run_product(act_x, packed_gu, gamma_gu, M, F, D, 1, h, bl::Epilogue::kGluBf16,
-                    BITLINEAR_KERNEL_AUTO, st));
+    if (use_decode(M, D, BITLINEAR_KERNEL_AUTO)) {
+        TRY(run_decode(x, rms_w_gu, 0, packed_gu, gamma_gu, 1, M, F, D, eps, h, bl::Epilogue::kGluBf16, st));
+    } else {
+        TRY(hip_status(bl::launch_quant(x, rms_w_gu, M, M, (int)D, eps, act_x, st), "quantise launch"));
+        TRY(run_product(act_x, packed_gu, gamma_gu, M, F, D, 1, h, bl::Epilogue::kGluBf16,
+                        BITLINEAR_KERNEL_AUTO, st));
+    }
+    if (use_decode(M, F, BITLINEAR_KERNEL_AUTO))
+        return run_decode(h, rms_w_down, 0, packed_down, gamma_down, 1, M, D, F, eps, y,
+                          bl::Epilogue::kF32, st);
     TRY(hip_status(bl::launch_quant(h, rms_w_down, M, M, (int)F, eps, act_h, st), "quantise launch"));
     return run_product(act_h, packed_down, gamma_down, M, D, F, 1, y, bl::Epilogue::kF32,
                        BITLINEAR_KERNEL_AUTO, st);
@@ -356,7 +403,7 @@ int bitlinear_ternary_matmul_i32(const int8_t* q, const uint8_t* packed, int64_t
     TRY(check_k(K, "K"));
     CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems,
           BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    TRY(check_kernel(kernel, M));
+    TRY(check_kernel(kernel, M, K, false));
     if (M == 0 || N == 0) return BITLINEAR_OK;
     CHECK_PTR(q);
     CHECK_PTR(packed);

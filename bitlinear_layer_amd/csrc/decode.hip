@@ -1,0 +1,331 @@
+// decode.hip -- fused decode-shaped BitLinear: one launch per call.
+//
+// For a handful of tokens (M <= 4) the layer is bound by streaming the
+// packed weights from HBM (N*K/4 bytes against 2*M*N*K int8 operations), so
+// everything else is folded into the one kernel that streams them:
+//   1. each block quantises the M token rows itself ([ld246, "融合 BitLinear
+//      层的创新"]: activations read once, normalised and quantised on chip):
+//      fp64 sum of squares, fp32 absmax and the int8 codes go to LDS; the
+//      block's reductions use a fixed order, so every block computes the
+//      same codes as the stand-alone quantisation kernel, bit for bit;
+//   2. each lane copies the codes of the k-columns it owns into registers;
+//   3. the block streams its share of the weight rows: LPR lanes share a
+//      row, each loading 16 bytes (64 weights) per step with U rows in
+//      flight per wave, expanding the 2-bit codes with shifts and masks and
+//      accumulating with v_dot4 ([ld246, "三值权重的应用"]: +1 adds, -1
+//      subtracts, 0 skips -- here as sum q*(w+1) - sum q);
+//   4. a butterfly over the LPR lanes gives each row's sum; one lane per row
+//      rescales ([datacamp, "Các thành phần lõi: MLGRU và GLU"]: scaled
+//      ternary accumulation) or, for the GLU, forms bf16(SiLU(gate) * up).
+// B independent problems of the same shape run in one launch (grid.y).
+#include "epilogue.h"
+
+namespace bl {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+// Block-cooperative RMSNorm + absmax int8 of one token row into LDS; the
+// same arithmetic and reduction order as quant_kernel, so the codes agree.
+__device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__ xr,
+                                                    const float* __restrict__ gr, int K, float eps,
+                                                    int8_t* __restrict__ qrow, double* dscr,
+                                                    float* fscr, int32_t* iscr, float& scale_out,
+                                                    int32_t& sumq_out) {
+    const int nchunks = K / 8;
+    double ss = 0.0;
+    for (int i = threadIdx.x; i < nchunks; i += kThreads) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(xr + 8 * i);
+        const uint32_t p[4] = {raw.x, raw.y, raw.z, raw.w};
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16_lo(p[j]);
+            v[2 * j + 1] = bf16_hi(p[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += (double)v[j] * (double)v[j];
+    }
+    ss = block_sum(ss, dscr);
+    const float ms = (float)(ss / (double)K);
+    const float r = 1.0f / sqrtf(ms + eps);
+    float amax = 0.0f;
+    for (int i = threadIdx.x; i < nchunks; i += kThreads) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(xr + 8 * i);
+        const uint32_t p[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float4 g0 = *reinterpret_cast<const float4*>(gr + 8 * i);
+        const float4 g1 = *reinterpret_cast<const float4*>(gr + 8 * i + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float xv = (j & 1) ? bf16_hi(p[j >> 1]) : bf16_lo(p[j >> 1]);
+            amax = fmaxf(amax, fabsf((xv * r) * gv[j]));
+        }
+    }
+    amax = block_max(amax, fscr);
+    const float scale = 127.0f / fmaxf(amax, 1e-5f);
+    int32_t qsum = 0;
+    for (int i = threadIdx.x; i < nchunks; i += kThreads) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(xr + 8 * i);
+        const uint32_t p[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float4 g0 = *reinterpret_cast<const float4*>(gr + 8 * i);
+        const float4 g1 = *reinterpret_cast<const float4*>(gr + 8 * i + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float xv = (j & 1) ? bf16_hi(p[j >> 1]) : bf16_lo(p[j >> 1]);
+            const float t = fminf(fmaxf(rintf(((xv * r) * gv[j]) * scale), -128.0f), 127.0f);
+            const int32_t qi = (int32_t)t;
+            qsum += qi;
+            packed[j >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (j & 3));
+        }
+        *reinterpret_cast<uint2*>(qrow + 8 * i) = make_uint2(packed[0], packed[1]);
+    }
+    qsum = block_sum(qsum, iscr);
+    scale_out = scale;
+    sumq_out = qsum;
+}
+
+template <int MAXM, int S, int U, int LPR, Epilogue EP>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows_per_block) {
+    constexpr bool kGlu = EP == Epilogue::kGluBf16;
+    constexpr int RW = kWave / LPR;     // rows per wave-wide load
+    constexpr int kSpread = LPR / U;    // lanes holding one finished row sum
+    extern __shared__ __attribute__((aligned(16))) int8_t qlds[];  // [M][K]
+    __shared__ double dscr[kWaves];
+    __shared__ float fscr[kWaves];
+    __shared__ int32_t iscr[kWaves];
+    __shared__ float s_scale[MAXM];
+    __shared__ int32_t s_sumq[MAXM];
+
+    const int b = blockIdx.y;
+    const int M = a.M, N = a.N, K = a.K;
+    const int nwords = K / 16;
+    const int nchunks = K / 64;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int lr = lane & (LPR - 1);
+    const int grp = lane / LPR;
+
+    const int64_t nrows = kGlu ? 2 * (int64_t)N : (int64_t)N;
+    const uint32_t* P = reinterpret_cast<const uint32_t*>(a.packed) + (int64_t)b * nrows * nwords;
+    const int n0 = blockIdx.x * rows_per_block;
+    const int n_end = min(N, n0 + rows_per_block);
+    const int step = kWaves * U * RW;
+
+    uint4 wa[U][S], wb[U][S], ua[U][S], ub[U][S];
+    // Weights of rows base + u*RW + grp, this lane's chunks.  Loads are
+    // unconditional from clamped addresses: a row past the end is computed
+    // and never stored, and a chunk past the end of K meets zero codes in
+    // qreg, so it adds nothing.
+    auto load = [&](uint4 (&w)[U][S], uint4 (&wu)[U][S], int base) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t n = min(base + u * RW + grp, n_end - 1);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int c = min(lr + s * LPR, nchunks - 1);
+                w[u][s] = load_stream16(P + n * nwords + 4 * c);
+                if (kGlu) wu[u][s] = load_stream16(P + ((int64_t)N + n) * nwords + 4 * c);
+            }
+        }
+    };
+    // Issue the first weight loads before quantising: they do not depend on it.
+    const int base0 = n0 + wave * U * RW;
+    load(wa, ua, base0);
+
+    // 1. quantise the block's token rows into LDS
+    const uint16_t* X = a.x + (int64_t)b * M * K;
+    const float* G = a.g + (int64_t)b * a.g_stride;
+    for (int m = 0; m < M; ++m) {
+        float sc;
+        int32_t sq;
+        quantise_row_to_lds(X + (int64_t)m * K, G, K, a.eps, qlds + (int64_t)m * K, dscr, fscr, iscr, sc, sq);
+        if (threadIdx.x == 0) {
+            s_scale[m] = sc;
+            s_sumq[m] = sq;
+        }
+    }
+    __syncthreads();
+
+    // 2. this lane's codes: chunk c = lr + s*LPR covers k in [64c, 64c + 64)
+    int4 qreg[MAXM][S][4];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = lr + s * LPR;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                qreg[m][s][j] = make_int4(0, 0, 0, 0);
+                if (m < M && c < nchunks)
+                    qreg[m][s][j] = *reinterpret_cast<const int4*>(qlds + (int64_t)m * K + 64 * c + 16 * j);
+            }
+        }
+    const float gamma = a.gamma[b];
+    float cs[MAXM];
+    int32_t sumq[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        cs[m] = m < M ? gamma / s_scale[m] : 0.0f;
+        sumq[m] = m < M ? s_sumq[m] : 0;
+    }
+
+    // 3. products of one buffered set of rows, 4. row sums and epilogue
+    auto dot_rows = [&](const uint4 (&w)[U][S], int32_t (&out)[MAXM][U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int32_t a1[MAXM], a4[MAXM], a16[MAXM];
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) a1[m] = a4[m] = a16[m] = 0;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const uint32_t ww[4] = {w[u][s].x, w[u][s].y, w[u][s].z, w[u][s].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    int32_t c0, c1, c2, c3;
+                    decode_codes_scaled(ww[j], c0, c1, c2, c3);
+#pragma unroll
+                    for (int m = 0; m < MAXM; ++m) {
+                        a1[m] = dot4(c0, qreg[m][s][j].x, a1[m]);
+                        a4[m] = dot4(c1, qreg[m][s][j].y, a4[m]);
+                        a16[m] = dot4(c2, qreg[m][s][j].z, a16[m]);
+                        a1[m] = dot4(c3, qreg[m][s][j].w, a1[m]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) out[m][u] = a1[m] + (a4[m] >> 2) + (a16[m] >> 4);
+        }
+    };
+    const int u_out = lr / kSpread;
+    const bool writer = (lr % kSpread) == 0;
+    auto finish = [&](const uint4 (&w)[U][S], const uint4 (&wu)[U][S], int base) {
+        int32_t part[MAXM][U], partu[MAXM][U];
+        dot_rows(w, part);
+        if (kGlu) dot_rows(wu, partu);
+        int32_t tot[MAXM], totu[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            tot[m] = group_row_sums<LPR, U>(part[m], lane);
+            totu[m] = kGlu ? group_row_sums<LPR, U>(partu[m], lane) : 0;
+        }
+        const int n = base + u_out * RW + grp;
+        if (writer && n < n_end) {
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                if (m >= M) continue;
+                const int64_t o = ((int64_t)b * M + m) * N + n;
+                if (kGlu)
+                    static_cast<uint16_t*>(a.out)[o] =
+                        glu_bf16(rescale(tot[m] - sumq[m], cs[m]), rescale(totu[m] - sumq[m], cs[m]));
+                else
+                    static_cast<float*>(a.out)[o] = rescale(tot[m] - sumq[m], cs[m]);
+            }
+        }
+    };
+
+    // Software pipeline: the loads of the next set are in flight while the
+    // current set is decoded and reduced.
+    for (int base = base0; base < n_end; base += 2 * step) {
+        load(wb, ub, base + step);
+        finish(wa, ua, base);
+        if (base + step >= n_end) break;
+        load(wa, ua, base + 2 * step);
+        finish(wb, ub, base + step);
+    }
+}
+
+struct Plan {
+    int lpr_log2 = -1;
+    int S = 0;
+};
+
+// Lanes per row (LPR) and 16-byte steps per lane (S) for a row of `nchunks`
+// 64-weight chunks: fewest idle lanes with at most 4 / MAXM code chunks
+// held per lane (64 registers), preferring wider rows on ties.
+Plan plan_for(int nchunks, int maxm) {
+    Plan best;
+    double best_idle = 2.0;
+    for (int l2 = 6; l2 >= 3; --l2) {
+        const int lpr = 1 << l2;
+        const int s = (nchunks + lpr - 1) / lpr;
+        if (s < 1 || s * maxm > 4) continue;
+        const double idle = 1.0 - (double)nchunks / (double)(s * lpr);
+        if (idle < best_idle - 1e-9) {
+            best_idle = idle;
+            best.lpr_log2 = l2;
+            best.S = s;
+        }
+    }
+    return best;
+}
+
+template <int MAXM, int S, int LPR, Epilogue EP>
+hipError_t launch_msl(const DecodeArgs& a, hipStream_t stream) {
+    constexpr int kBufRows = 8 / (EP == Epilogue::kGluBf16 ? 2 : 1) / (S >= 3 ? 4 : S);
+    constexpr int U = kBufRows < 1 ? 1 : (kBufRows > LPR ? LPR : kBufRows);
+    constexpr int RW = kWave / LPR;
+    const int64_t total_rows = (int64_t)a.N * a.batch;
+    int64_t rpb = (total_rows + 1023) / 1024;  // about 1024 blocks
+    rpb = round_up(rpb < 1 ? 1 : rpb, (int64_t)kWaves * RW);
+    if (rpb > a.N) rpb = round_up(a.N, (int64_t)kWaves * RW);
+    const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
+    const size_t lds = (size_t)a.M * a.K;
+    decode_kernel<MAXM, S, U, LPR, EP><<<grid, kThreads, lds, stream>>>(a, (int)rpb);
+    return hipGetLastError();
+}
+
+template <int MAXM, int S, Epilogue EP>
+hipError_t launch_ms(const DecodeArgs& a, const Plan& p, hipStream_t stream) {
+    switch (p.lpr_log2) {
+        case 3: return launch_msl<MAXM, S, 8, EP>(a, stream);
+        case 4: return launch_msl<MAXM, S, 16, EP>(a, stream);
+        case 5: return launch_msl<MAXM, S, 32, EP>(a, stream);
+        case 6: return launch_msl<MAXM, S, 64, EP>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int MAXM, Epilogue EP>
+hipError_t launch_m(const DecodeArgs& a, const Plan& p, hipStream_t stream) {
+    // plan_for keeps S * MAXM <= 4, so only those instantiations exist.
+    switch (p.S) {
+        case 1: return launch_ms<MAXM, 1, EP>(a, p, stream);
+        case 2: if constexpr (MAXM <= 2) return launch_ms<MAXM, 2, EP>(a, p, stream); break;
+        case 3: if constexpr (MAXM == 1) return launch_ms<MAXM, 3, EP>(a, p, stream); break;
+        case 4: if constexpr (MAXM == 1) return launch_ms<MAXM, 4, EP>(a, p, stream); break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <Epilogue EP>
+hipError_t launch_ep(const DecodeArgs& a, hipStream_t stream) {
+    const int maxm = a.M <= 1 ? 1 : (a.M <= 2 ? 2 : 4);
+    const Plan p = plan_for(a.K / 64, maxm);
+    if (maxm == 1) return launch_m<1, EP>(a, p, stream);
+    if (maxm == 2) return launch_m<2, EP>(a, p, stream);
+    return launch_m<4, EP>(a, p, stream);
+}
+
+}  // namespace
+
+bool decode_supported(int M, int K) {
+    if (M < 1 || M > kDecodeMaxM || K % 64 != 0) return false;
+    const int maxm = M <= 1 ? 1 : (M <= 2 ? 2 : 4);
+    return plan_for(K / 64, maxm).S > 0;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, Epilogue ep, hipStream_t stream) {
+    if (!decode_supported(a.M, a.K)) return hipErrorInvalidValue;
+    switch (ep) {
+        case Epilogue::kF32: return launch_ep<Epilogue::kF32>(a, stream);
+        case Epilogue::kGluBf16: return launch_ep<Epilogue::kGluBf16>(a, stream);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bl

@@ -26,6 +26,26 @@ __device__ __forceinline__ void decode_codes(uint32_t w, int32_t& c0, int32_t& c
     c3 = (int32_t)((w >> 6) & 0x03030303u);
 }
 
+// The same codes, each scaled by 4^i instead of shifted down, for i = 0..2
+// (byte values 0..32, still valid int8), plus the fourth word shifted:
+// 5 VALU ops per 16 weights instead of 7.  Products against q must then be
+// accumulated separately per scale and recombined as a1 + a4/4 + a16/16;
+// each partial sum is an exact multiple of its scale.
+__device__ __forceinline__ void decode_codes_scaled(uint32_t w, int32_t& c0, int32_t& c1x4,
+                                                    int32_t& c2x16, int32_t& c3) {
+    c0 = (int32_t)(w & 0x03030303u);
+    c1x4 = (int32_t)(w & 0x0C0C0C0Cu);
+    c2x16 = (int32_t)(w & 0x30303030u);
+    c3 = (int32_t)((w >> 6) & 0x03030303u);
+}
+
+// 16-byte load of data read once (non-temporal hint: do not keep in cache).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint32_t* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Signed 4 x int8 dot product accumulated into an int32 (v_dot4c_i32_i8).
 __device__ __forceinline__ int32_t dot4(int32_t a, int32_t b, int32_t acc) {
     return __builtin_amdgcn_sdot4(a, b, acc, false);
@@ -61,6 +81,73 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
     return v;
+}
+
+// ---------------------------------------------------------------------------
+// Row sums over groups of LPR lanes without LDS.  Each exchange level pairs
+// every lane with one partner that differs in bit log2(O) of the lane index:
+//   O = 32, 16 -> v_permlane32_swap / v_permlane16_swap (gfx950);
+//   O = 8, 4   -> DPP row_mirror / row_half_mirror (partner lane ^ 15, ^ 7);
+//   O = 2, 1   -> DPP quad_perm (partner lane ^ 2, ^ 1).
+// The XOR masks 32, 16, 15, 7, 2, 1 span all lane bits, so the levels form a
+// hypercube and every group total counts each lane exactly once.
+// ---------------------------------------------------------------------------
+template <int O>
+__device__ __forceinline__ int32_t dpp_partner(int32_t v) {
+    constexpr int ctrl = O == 8 ? 0x140 : (O == 4 ? 0x141 : (O == 2 ? 0x4E : 0xB1));
+    return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+}
+
+// Reduce-scatter step: lanes with bit log2(O) clear keep lo + partner's lo,
+// lanes with it set keep hi + partner's hi.
+template <int O>
+__device__ __forceinline__ int32_t scatter_level(int32_t lo, int32_t hi, int lane) {
+    if constexpr (O == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+        return (int32_t)r[0] + (int32_t)r[1];
+    } else if constexpr (O == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+        return (int32_t)r[0] + (int32_t)r[1];
+    } else {
+        const bool up = (lane & O) != 0;
+        const int32_t keep = up ? hi : lo;
+        const int32_t send = up ? lo : hi;
+        return keep + dpp_partner<O>(send);
+    }
+}
+
+// All-reduce step over the same pairs.
+template <int O>
+__device__ __forceinline__ int32_t allreduce_level(int32_t v) {
+    if constexpr (O == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (int32_t)r[0] + (int32_t)r[1];
+    } else if constexpr (O == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (int32_t)r[0] + (int32_t)r[1];
+    } else {
+        return v + dpp_partner<O>(v);
+    }
+}
+
+// v[0..U) are this lane's partial sums for U rows; lanes in aligned groups
+// of LPR share the rows.  Returns the full sum of row
+// (lane % LPR) >> log2(LPR / U); it is complete in every lane, and lanes with
+// (lane % LPR) % (LPR / U) == 0 hold distinct rows.
+template <int LPR, int U, int O = LPR / 2>
+__device__ __forceinline__ int32_t group_row_sums(int32_t (&v)[U], int lane) {
+    static_assert(U >= 1 && U <= LPR && (U & (U - 1)) == 0, "U must be a power of two <= LPR");
+    if constexpr (O == 0) {
+        return v[0];
+    } else if constexpr (U > 1) {
+        int32_t h[U / 2];
+#pragma unroll
+        for (int i = 0; i < U / 2; ++i) h[i] = scatter_level<O>(v[i], v[i + U / 2], lane);
+        return group_row_sums<LPR, U / 2, O / 2>(h, lane);
+    } else {
+        int32_t r[1] = {allreduce_level<O>(v[0])};
+        return group_row_sums<LPR, 1, O / 2>(r, lane);
+    }
 }
 
 // Block reductions: every thread returns the block-wide result.  `scratch`

@@ -69,4 +69,22 @@ hipError_t launch_gemm_mfma(const ProductArgs& a, Epilogue ep, hipStream_t strea
 // Largest M the GEMV kernel takes.
 constexpr int kGemvMaxM = 8;
 
+// Fused decode (quantisation + product in one kernel) for M <= kDecodeMaxM:
+// x bf16 [batch][M][K], g fp32 at g + b * g_stride (g_stride 0 = shared),
+// packed [batch][Nrows][K/4], gamma [batch], out [batch][M][N].
+constexpr int kDecodeMaxM = 4;
+struct DecodeArgs {
+    const uint16_t* x;
+    const float* g;
+    int64_t g_stride;
+    const uint8_t* packed;
+    const float* gamma;
+    int M, N, K;
+    int batch;
+    float eps;
+    void* out;
+};
+bool decode_supported(int M, int K);
+hipError_t launch_decode(const DecodeArgs& a, Epilogue ep, hipStream_t stream);
+
 }  // namespace bl

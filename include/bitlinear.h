@@ -100,10 +100,16 @@ typedef enum {
 
 /* Kernel choice for bitlinear_forward_ex. */
 typedef enum {
-    BITLINEAR_KERNEL_AUTO = 0, /* by token count M (what bitlinear_forward does) */
-    BITLINEAR_KERNEL_GEMV = 1, /* weight-streaming GEMV (decode-shaped)          */
-    BITLINEAR_KERNEL_MFMA = 2  /* int8 MFMA tiles (prefill-shaped)               */
+    BITLINEAR_KERNEL_AUTO = 0,   /* by token count M (what bitlinear_forward does)  */
+    BITLINEAR_KERNEL_GEMV = 1,   /* quantise, then weight-streaming GEMV (M <= 8)   */
+    BITLINEAR_KERNEL_MFMA = 2,   /* quantise, then int8 MFMA tiles                  */
+    BITLINEAR_KERNEL_DECODE = 3  /* one fused quantise+GEMV kernel; takes M <= 4
+                                    with K % 64 == 0 and K <= 16384 (M = 1),
+                                    8192 (M = 2) or 4096 (M = 3, 4)             */
 } bitlinear_kernel;
+
+/* 1 when the fused decode kernel takes M tokens of length K, else 0. */
+int bitlinear_decode_supported(int64_t M, int64_t K);
 
 /* Version of this ABI (bumped on any incompatible change). */
 int bitlinear_abi_version(void);

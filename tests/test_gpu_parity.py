@@ -17,7 +17,18 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-GEMV, MFMA = bl.BITLINEAR_KERNEL_GEMV, bl.BITLINEAR_KERNEL_MFMA
+GEMV, MFMA, DECODE = bl.BITLINEAR_KERNEL_GEMV, bl.BITLINEAR_KERNEL_MFMA, bl.BITLINEAR_KERNEL_DECODE
+
+
+def kernels_for(M, K):
+    """Every kernel that takes this shape: AUTO, MFMA, the GEMV (M <= 8) and
+    the fused decode kernel where it applies."""
+    ks = [bl.BITLINEAR_KERNEL_AUTO, MFMA]
+    if M <= 8:
+        ks.append(GEMV)
+    if bl.bitlinear_decode_supported(M, K):
+        ks.append(DECODE)
+    return ks
 
 
 def _say(*a):
@@ -149,6 +160,11 @@ FORWARD = [
     (3, 129, 48, "student_t3", 0.0, 1.0),
     (130, 300, 2064, "normal", 0.005, 50.0),
     (257, 7, 16, "normal", 0.0, 1.0),
+    (2, 300, 6912, "normal", 0.005, 50.0),   # decode, two 16-byte steps per lane
+    (1, 129, 5632, "normal", 0.0, 1.0),      # decode, three steps per lane
+    (4, 65, 4096, "student_t3", 0.0, 1.0),
+    (1, 1000, 16384, "normal", 0.0, 1.0),    # decode, four steps per lane
+    (3, 77, 192, "normal", 0.0, 1.0),
 ]
 
 
@@ -167,8 +183,7 @@ def _forward_case(M, N, K, recipe, of, os_, kernel, g_kind="random", seed=0):
 
 @pytest.mark.parametrize("M,N,K,recipe,of,os_", FORWARD)
 def test_forward(M, N, K, recipe, of, os_):
-    kernels = [bl.BITLINEAR_KERNEL_AUTO, MFMA] + ([GEMV] if M <= 8 else [])
-    for kern in kernels:
+    for kern in kernels_for(M, K):
         _say("forward", M, N, K, recipe, "kernel", kern)
         _forward_case(M, N, K, recipe, of, os_, kern)
 
@@ -179,8 +194,9 @@ def test_forward_parity_config_ones_gain():
     _forward_case(16, 256, 256, "normal", 0.01, 20.0, bl.BITLINEAR_KERNEL_AUTO, g_kind="ones")
 
 
-def test_forward_batched():
-    B, N, K = 5, 256, 512
+@pytest.mark.parametrize("K", [512, 528])
+def test_forward_batched(K):
+    B, N = 5, 256
     for M in (1, 3, 20):
         _say("batched", B, M, N, K)
         xs = [wl.x_normal(M, K, seed=10 + b) for b in range(B)]
@@ -205,8 +221,8 @@ def test_forward_structural_zeros():
     x[3] = 0
     W[5] = 0
     packed, gamma = gu.pack_on_gpu(W)
-    for kern in (GEMV, MFMA):
-        xs = x[:8] if kern == GEMV else x
+    for kern in (GEMV, MFMA, DECODE):
+        xs = x[:8] if kern == GEMV else (x[:4] if kern == DECODE else x)
         y = bl.bitlinear_forward(gu.to_dev_bf16(xs), gu.to_dev(g), packed, gamma, kernel=kern).cpu().numpy()
         assert np.all(y[3] == 0) and np.all(y[:, 5] == 0)
     packed0, gamma0 = gu.pack_on_gpu(np.zeros((N, K), np.float32))
@@ -257,19 +273,19 @@ def assert_h_parity(h_gpu, h_ref):
     assert diff.max(initial=0) <= 1 and np.mean(diff != 0) <= 1e-3, (diff.max(), np.mean(diff != 0))
 
 
-@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (5, 256, 320), (130, 256, 320), (3, 2048, 5632)])
+@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (5, 256, 320), (130, 256, 320), (3, 2048, 5632),
+                                   (2, 208, 96)])
 def test_glu_hidden(M, D, F):
     x, g_gu, W_gu, g_dn, W_dn = _glu_inputs(M, D, F, seed=M)
     ref = gu.orc().glu(x, g_gu, W_gu, g_dn, W_dn)
     packed, gamma = gu.pack_on_gpu(W_gu)
-    kernels = [MFMA] + ([GEMV] if M <= 8 else [])
-    for kern in kernels:
+    for kern in kernels_for(M, D):
         _say("glu hidden", M, D, F, "kernel", kern)
         h = bl.bitlinear_glu_hidden(gu.to_dev_bf16(x), gu.to_dev(g_gu), packed, gamma, kernel=kern)
         assert_h_parity(gu.from_dev_bf16(h), ref["h"])
 
 
-@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (7, 256, 320), (200, 256, 320)])
+@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (7, 256, 320), (200, 256, 320), (4, 512, 1024)])
 def test_glu_forward(M, D, F):
     _say("glu forward", M, D, F)
     x, g_gu, W_gu, g_dn, W_dn = _glu_inputs(M, D, F, seed=M + 100)
