@@ -2,16 +2,23 @@
 //
 // At large token counts the ternary product is a dense contraction
 // (2*M*N*K int8 operations against (M+N/4)*K bytes), so it runs on
-// v_mfma_i32_16x16x64_i8.  The packed weights are the B operand: one packed
-// 32-bit word holds the 16 codes of one 16-weight group, and a lane's
-// 16-byte B fragment of a 16x16x64 step is exactly one such group, so each
-// lane loads one word per step and expands it in registers (shift + mask,
-// 7 VALU ops per 16 weights).  The int8 activations (A operand) are staged
-// through LDS and shared by the waves of the block.
+// v_mfma_i32_16x16x64_i8 ([jiqizhixin, "具有三值权重的 MatMul-free 密集层"]: the
+// ternary product is an add/subtract accumulation; on the matrix cores it
+// is the same integer sum, exactly).
 //
+// Block tile BM x BN (tokens x packed rows), 8 waves as WM x WN, each wave
+// owning a (BM/WM) x (BN/WN) tile of 16x16 accumulators.  K advances in
+// stages of 128 (two MFMA steps of 64), double-buffered in LDS:
+//   A: int8 codes q, BM rows x 128 bytes per stage (row pitch padded by 16
+//      bytes so that the 16-byte fragment reads of 8 lanes hit distinct banks);
+//   B: packed weights, BN rows x 32 bytes per stage -- a quarter of the
+//      int8 operand -- expanded in registers: a lane's 16-byte B fragment of
+//      one 16x16x64 step is one packed 32-bit word (16 weights), 7 VALU ops.
 // Operand pairing: lane l of A supplies row l%16, k = 16*(l/16) + 0..15 of
-// the 64-wide step; lane l of B supplies column l%16 at the same k.  The
-// accumulator holds D[4*(l/16) + v][l%16] in element v.
+// the step; lane l of B supplies column l%16 at the same k.  The
+// accumulator element v of lane l holds D[4*(l/16) + v][l%16].
+#include <type_traits>
+
 #include "epilogue.h"
 
 namespace bl {
@@ -19,115 +26,185 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 waves as 2 x 2
-constexpr int kBM = 128;       // tokens per block
-constexpr int kBN = 128;       // packed weight rows per block (64 f for the GLU)
-constexpr int kBK = 64;        // k per MFMA step
-constexpr int kLdsPitch = kBK + 16;
+constexpr int kBK = 128;                 // k per LDS stage
+constexpr int kAPitch = kBK + 16;        // bytes per A row in LDS
+constexpr int kBWords = kBK / 16;        // packed words per B row per stage (8)
+constexpr int kBPitch = kBWords + 4;     // words per B row in LDS (16-byte aligned)
 
-template <Epilogue EP>
-__global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(ProductArgs a) {
-    constexpr bool kGlu = EP == Epilogue::kGluBf16;
-    __shared__ __attribute__((aligned(16))) int8_t As[kBM * kLdsPitch];
+template <int BM, int BN, int WM, int WN, Epilogue EP>
+struct Tile {
+    static constexpr int kThreads = WM * WN * kWave;
+    static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+    static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 fragments per wave
+    static constexpr bool kGlu = EP == Epilogue::kGluBf16;
+    static constexpr int kCols = kGlu ? BN / 2 : BN;  // output columns per block
+    static constexpr int kAChunks = BM * (kBK / 16) / kThreads;  // 16-byte A loads per thread
+    static constexpr int kBChunks = BN * (kBK / 64) / kThreads;  // 16-byte B loads per thread
+    static_assert(kAChunks >= 1 && kBChunks >= 1, "tile too small for the block");
+    static_assert(!kGlu || FN % 2 == 0, "GLU tiles pair gate and up fragments");
+    static constexpr int kLdsA = BM * kAPitch;          // bytes per stage
+    static constexpr int kLdsB = BN * kBPitch * 4;      // bytes per stage
+};
 
-    const int b = blockIdx.y;
-    const int cols_per_block = kGlu ? kBN / 2 : kBN;
-    const int ntiles_n = (a.N + cols_per_block - 1) / cols_per_block;
-    const int tile_n = blockIdx.x % ntiles_n;
-    const int tile_m = blockIdx.x / ntiles_n;
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wm = wave >> 1, wn = wave & 1;
+// Packed row (of the Nrows x K/4 matrix) that local B-tile row r of output
+// tile tn maps to.  Plain: rows tn*BN + r.  GLU: the first BN/2 local rows
+// are gate rows f0 + r, the rest the up rows F + f0 + r - BN/2, clamped.
+template <int BN, bool GLU>
+__device__ __forceinline__ int64_t b_row(int tn, int r, int N) {
+    if (GLU) {
+        const int f = tn * (BN / 2) + (r % (BN / 2));
+        return (r < BN / 2 ? 0 : (int64_t)N) + min(f, N - 1);
+    }
+    return min(tn * BN + r, N - 1);
+}
+
+// Workgroups are dispatched to the 8 XCDs round robin (block i -> XCD i % 8),
+// and each XCD has its own L2.  Renumber tiles so that XCD x gets the
+// contiguous range [x * T/8, (x+1) * T/8): with N-tiles fastest, an XCD then
+// owns whole rows of token tiles -- each A tile is fetched into one L2 only,
+// and the packed weights (small) stay resident in every L2.
+__device__ __forceinline__ int xcd_tile(int bid, int tiles) {
+    constexpr int kXcds = 8;
+    if (tiles % kXcds != 0) return bid;
+    return (bid % kXcds) * (tiles / kXcds) + bid / kXcds;
+}
+
+template <int BM, int BN, int WM, int WN, Epilogue EP>
+__global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(ProductArgs a) {
+    using T = Tile<BM, BN, WM, WN, EP>;
+    constexpr bool kGlu = T::kGlu;
+    __shared__ __attribute__((aligned(16))) int8_t As[2][T::kLdsA];
+    __shared__ __attribute__((aligned(16))) uint32_t Bs[2][T::kLdsB / 4];
+
     const int M = a.M, N = a.N, K = a.K;
     const int nwords = K / 16;
+    const int b = blockIdx.y;
+    const int ntn = (N + T::kCols - 1) / T::kCols;
+    const int t = xcd_tile(blockIdx.x, gridDim.x);
+    const int tn = t % ntn;
+    const int tm = t / ntn;
+    const int m0 = tm * BM;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+
     const int64_t nrows = kGlu ? 2 * (int64_t)N : (int64_t)N;
     const int8_t* Q = a.q + (int64_t)b * M * K;
     const uint32_t* P = reinterpret_cast<const uint32_t*>(a.packed) + (int64_t)b * nrows * nwords;
-    const int m0 = tile_m * kBM;
 
-    // Packed row feeding N-block bj of this lane (clamped in range; results
-    // for clamped rows are never stored).
-    const uint32_t* brow[4];
+    // Global -> register staging of one stage (k0 .. k0 + 127).
+    int4 ra[T::kAChunks];
+    uint4 rb[T::kBChunks];
+    auto load_stage = [&](int k0) {
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-        int64_t row;
-        if (kGlu) {
-            const int f = tile_n * (kBN / 2) + wn * 32 + (bj & 1) * 16 + (lane & 15);
-            row = (bj < 2 ? 0 : (int64_t)N) + min(f, N - 1);
-        } else {
-            const int n = tile_n * kBN + wn * 64 + bj * 16 + (lane & 15);
-            row = min(n, N - 1);
+        for (int i = 0; i < T::kAChunks; ++i) {
+            const int id = tid + i * T::kThreads;
+            const int r = id / (kBK / 16), c = id % (kBK / 16);
+            const int kk = k0 + 16 * c;
+            const int64_t row = min(m0 + r, M - 1);
+            ra[i] = kk < K ? *reinterpret_cast<const int4*>(Q + row * K + kk) : make_int4(0, 0, 0, 0);
         }
-        brow[bj] = P + row * nwords;
-    }
-
-    i32x4 acc[4][4];
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+        for (int i = 0; i < T::kBChunks; ++i) {
+            const int id = tid + i * T::kThreads;
+            const int r = id / (kBK / 64), c = id % (kBK / 64);
+            const int w0 = k0 / 16 + 4 * c;
+            const uint32_t* src = P + b_row<BN, kGlu>(tn, r, N) * nwords + w0;
+            if (w0 + 4 <= nwords) {
+                rb[i] = *reinterpret_cast<const uint4*>(src);
+            } else {  // tail of K: words past the row end meet zero codes in A
+                rb[i] = make_uint4(w0 < nwords ? src[0] : 0u, w0 + 1 < nwords ? src[1] : 0u,
+                                   w0 + 2 < nwords ? src[2] : 0u, 0u);
+            }
+        }
+    };
+    auto store_stage = [&](int buf) {
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = i32x4{0, 0, 0, 0};
+        for (int i = 0; i < T::kAChunks; ++i) {
+            const int id = tid + i * T::kThreads;
+            const int r = id / (kBK / 16), c = id % (kBK / 16);
+            *reinterpret_cast<int4*>(&As[buf][r * kAPitch + 16 * c]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < T::kBChunks; ++i) {
+            const int id = tid + i * T::kThreads;
+            const int r = id / (kBK / 64), c = id % (kBK / 64);
+            *reinterpret_cast<uint4*>(&Bs[buf][r * kBPitch + 4 * c]) = rb[i];
+        }
+    };
 
-    const int lrow = threadIdx.x >> 1;          // A tile row this thread loads
-    const int lcol = (threadIdx.x & 1) * 32;    // and its 32-byte half
-    const int64_t grow = min(m0 + lrow, M - 1);
-    for (int k0 = 0; k0 < K; k0 += kBK) {
+    i32x4 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+    const int nstages = (K + kBK - 1) / kBK;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int st = 0; st < nstages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nstages) load_stage((st + 1) * kBK);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 64; ++kk) {
+            i32x4 bfrag[T::FN];
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+                int r;
+                if (kGlu)  // gate fragments first, then the up fragments of the same f
+                    r = (j < T::FN / 2 ? 0 : BN / 2) + wn * (T::TN / 2) + (j % (T::FN / 2)) * 16 + (lane & 15);
+                else
+                    r = wn * T::TN + j * 16 + (lane & 15);
+                const uint32_t pw = Bs[buf][r * kBPitch + kk * 4 + (lane >> 4)];
+                int32_t c0, c1, c2, c3;
+                decode_codes(pw, c0, c1, c2, c3);
+                bfrag[j] = i32x4{c0, c1, c2, c3};
+            }
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i) {
+                const int r = wm * T::TM + i * 16 + (lane & 15);
+                const i32x4 afrag =
+                    *reinterpret_cast<const i32x4*>(&As[buf][r * kAPitch + kk * 64 + 16 * (lane >> 4)]);
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, bfrag[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (st + 1 < nstages) store_stage(buf ^ 1);
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int kk = k0 + lcol + 16 * j;
-            int4 v = make_int4(0, 0, 0, 0);
-            if (kk < K) v = *reinterpret_cast<const int4*>(Q + grow * K + kk);
-            *reinterpret_cast<int4*>(&As[lrow * kLdsPitch + lcol + 16 * j]) = v;
-        }
-        __syncthreads();
-
-        const int kw = k0 / 16 + (lane >> 4);
-        i32x4 bfrag[4];
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const uint32_t pw = kw < nwords ? brow[bj][kw] : 0u;
-            int32_t c0, c1, c2, c3;
-            decode_codes(pw, c0, c1, c2, c3);
-            bfrag[bj] = i32x4{c0, c1, c2, c3};
-        }
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi) {
-            const i32x4 afrag = *reinterpret_cast<const i32x4*>(
-                &As[(wm * 64 + bi * 16 + (lane & 15)) * kLdsPitch + 16 * (lane >> 4)]);
-#pragma unroll
-            for (int bj = 0; bj < 4; ++bj)
-                acc[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, bfrag[bj], acc[bi][bj], 0, 0, 0);
-        }
     }
 
     // Epilogue: subtract sum_k q, rescale (or form the GLU product), store.
     const float gamma = a.gamma ? a.gamma[b] : 0.0f;
     const int64_t tok0 = (int64_t)b * M;
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
+    for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int m = m0 + wm * 64 + bi * 16 + 4 * (lane >> 4) + v;
+            const int m = m0 + wm * T::TM + i * 16 + 4 * (lane >> 4) + v;
             if (m >= M) continue;
             const int64_t t = tok0 + m;
             const int32_t sq = a.sumq[t];
             const float cs = EP == Epilogue::kI32 ? 0.0f : gamma / a.s[t];
             if (kGlu) {
 #pragma unroll
-                for (int bj = 0; bj < 2; ++bj) {
-                    const int f = tile_n * (kBN / 2) + wn * 32 + bj * 16 + (lane & 15);
+                for (int j = 0; j < T::FN / 2; ++j) {
+                    const int f = tn * (BN / 2) + wn * (T::TN / 2) + j * 16 + (lane & 15);
                     if (f < N) {
-                        const float zg = rescale(acc[bi][bj][v] - sq, cs);
-                        const float zu = rescale(acc[bi][bj + 2][v] - sq, cs);
+                        const float zg = rescale(acc[i][j][v] - sq, cs);
+                        const float zu = rescale(acc[i][j + T::FN / 2][v] - sq, cs);
                         static_cast<uint16_t*>(a.out)[t * N + f] = glu_bf16(zg, zu);
                     }
                 }
             } else {
 #pragma unroll
-                for (int bj = 0; bj < 4; ++bj) {
-                    const int n = tile_n * kBN + wn * 64 + bj * 16 + (lane & 15);
+                for (int j = 0; j < T::FN; ++j) {
+                    const int n = tn * BN + wn * T::TN + j * 16 + (lane & 15);
                     if (n < N) {
-                        const int32_t val = acc[bi][bj][v] - sq;
+                        const int32_t val = acc[i][j][v] - sq;
                         if (EP == Epilogue::kI32)
                             static_cast<int32_t*>(a.out)[t * N + n] = val;
                         else
@@ -139,14 +216,524 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(ProductArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same product with the operands copied from global memory straight into
+// LDS (global_load_lds_dwordx4, no register staging), three stages deep, so
+// that two stages of loads are in flight while one is multiplied.  Requires
+// K % 128 == 0.  LDS rows are unpadded; bank conflicts are avoided by an XOR
+// swizzle of the 16-byte chunks instead (A: chunk ^ (row & 7); B: half ^
+// ((row >> 3) & 1)), which the DMA realises by choosing, per lane, which
+// global chunk lands in that lane's fixed LDS slot.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// 16 bytes per lane from gbase + voff into LDS at lds_addr + 16 * lane
+// (global_load_lds_dwordx4; the LDS address goes through M0).  Issued as
+// inline asm so that the compiler does not track these writes into LDS: its
+// conservative tracking would wait for every DMA in flight before each LDS
+// read.  The kernels order all DMA reuse of LDS themselves with explicit
+// s_waitcnt vmcnt(n) and barriers; the instruction has no register outputs
+// and reads its address operands at issue.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+constexpr int kStages = 3;
+
+#ifndef BIG_WM
+#define BIG_WM 4
+#define BIG_WN 2
+#endif
+
+template <int BM, int BN, int WM, int WN, Epilogue EP>
+__global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a) {
+    using T = Tile<BM, BN, WM, WN, EP>;
+    constexpr bool kGlu = T::kGlu;
+    constexpr int kWavesPerBlock = WM * WN;
+    constexpr int kAStage = BM * kBK;         // bytes
+    constexpr int kBStage = BN * (kBK / 4);   // bytes
+    constexpr int kADma = kAStage / 1024 / kWavesPerBlock;  // 1 KiB DMA instructions per wave
+    constexpr int kBDma = kBStage / 1024 / kWavesPerBlock;
+    static_assert(kADma >= 1 && kBDma >= 1 && kADma * 1024 * kWavesPerBlock == kAStage &&
+                      kBDma * 1024 * kWavesPerBlock == kBStage,
+                  "stage must split into whole 1 KiB DMA instructions per wave");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * (kAStage + kBStage)];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int nwords = K / 16;
+    const int b = blockIdx.y;
+    const int ntn = (N + T::kCols - 1) / T::kCols;
+    const int t = xcd_tile(blockIdx.x, gridDim.x);
+    const int tn = t % ntn;
+    const int tm = t / ntn;
+    const int m0 = tm * BM;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+
+    const int64_t nrows = kGlu ? 2 * (int64_t)N : (int64_t)N;
+    const int8_t* Q = a.q + (int64_t)b * M * K;
+    const uint32_t* P = reinterpret_cast<const uint32_t*>(a.packed) + (int64_t)b * nrows * nwords;
+
+    // Per-lane global sources (stage 0) and LDS slots of this wave's DMAs.
+    const int8_t* asrc[kADma];
+    const uint32_t* bsrc[kBDma];
+#pragma unroll
+    for (int i = 0; i < kADma; ++i) {
+        const int r = (wave * kADma + i) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ (r & 7);
+        asrc[i] = Q + (int64_t)min(m0 + r, M - 1) * K + 16 * chunk;
+    }
+#pragma unroll
+    for (int i = 0; i < kBDma; ++i) {
+        const int r = (wave * kBDma + i) * 32 + (lane >> 1);
+        const int half = (lane & 1) ^ ((r >> 3) & 1);
+        bsrc[i] = P + b_row<BN, kGlu>(tn, r, N) * nwords + 4 * half;
+    }
+    auto issue_stage = [&](int st) {
+        const int buf = st % kStages;
+        int8_t* abase = lds + buf * kAStage;
+        int8_t* bbase = lds + kStages * kAStage + buf * kBStage;
+#pragma unroll
+        for (int i = 0; i < kADma; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[i] + st * kBK),
+                                             (lds_void_t*)(abase + (wave * kADma + i) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kBDma; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[i] + st * (kBK / 16)),
+                                             (lds_void_t*)(bbase + (wave * kBDma + i) * 1024), 16, 0, 0);
+    };
+
+    i32x4 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+    const int nstages = K / kBK;
+    issue_stage(0);
+    if (nstages > 1) issue_stage(1);
+    for (int st = 0; st < nstages; ++st) {
+        // Stage st has landed once at most the next stage's DMAs are pending.
+        if (st + 1 < nstages)
+            __builtin_amdgcn_s_waitcnt((kADma + kBDma) | (7 << 4) | (15 << 8));
+        else
+            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+        // Every wave's DMAs have landed and stage st-1's buffer is free.  A bare
+        // s_barrier: __syncthreads() would add a release fence that waits for
+        // all outstanding DMAs, including the stage still in flight.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (st + 2 < nstages) issue_stage(st + 2);
+        const int buf = st % kStages;
+        const int8_t* abase = lds + buf * kAStage;
+        const uint32_t* bbase = reinterpret_cast<const uint32_t*>(lds + kStages * kAStage + buf * kBStage);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 64; ++kk) {
+            i32x4 bfrag[T::FN];
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+                int r;
+                if (kGlu)
+                    r = (j < T::FN / 2 ? 0 : BN / 2) + wn * (T::TN / 2) + (j % (T::FN / 2)) * 16 + (lane & 15);
+                else
+                    r = wn * T::TN + j * 16 + (lane & 15);
+                const int half = kk ^ ((r >> 3) & 1);
+                const uint32_t pw = bbase[r * 8 + half * 4 + (lane >> 4)];
+                int32_t c0, c1, c2, c3;
+                decode_codes(pw, c0, c1, c2, c3);
+                bfrag[j] = i32x4{c0, c1, c2, c3};
+            }
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i) {
+                const int r = wm * T::TM + i * 16 + (lane & 15);
+                const int chunk = (kk * 4 + (lane >> 4)) ^ (r & 7);
+                const i32x4 afrag = *reinterpret_cast<const i32x4*>(abase + r * kBK + 16 * chunk);
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, bfrag[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+
+    const float gamma = a.gamma ? a.gamma[b] : 0.0f;
+    const int64_t tok0 = (int64_t)b * M;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + wm * T::TM + i * 16 + 4 * (lane >> 4) + v;
+            if (m >= M) continue;
+            const int64_t t = tok0 + m;
+            const int32_t sq = a.sumq[t];
+            const float cs = EP == Epilogue::kI32 ? 0.0f : gamma / a.s[t];
+            if (kGlu) {
+#pragma unroll
+                for (int j = 0; j < T::FN / 2; ++j) {
+                    const int f = tn * (BN / 2) + wn * (T::TN / 2) + j * 16 + (lane & 15);
+                    if (f < N) {
+                        const float zg = rescale(acc[i][j][v] - sq, cs);
+                        const float zu = rescale(acc[i][j + T::FN / 2][v] - sq, cs);
+                        static_cast<uint16_t*>(a.out)[t * N + f] = glu_bf16(zg, zu);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j) {
+                    const int n = tn * BN + wn * T::TN + j * 16 + (lane & 15);
+                    if (n < N) {
+                        const int32_t val = acc[i][j][v] - sq;
+                        if (EP == Epilogue::kI32)
+                            static_cast<int32_t*>(a.out)[t * N + n] = val;
+                        else
+                            static_cast<float*>(a.out)[t * N + n] = rescale(val, cs);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large-tile kernel on v_mfma_i32_32x32x32_i8.  On gfx950 this instruction
+// sustains the int8 peak with a few independent accumulators per wave,
+// while the 16x16x64 form needs many more chains than a tile can hold.
+//   block 256 x 256, 8 waves as WM x WN, wave tile (256/WM) x (256/WN) of
+//   32 x 32 fragments; lane l of A supplies row l%32, k = 16*(l/32)+0..15 of
+//   a 32-wide k step; lane l of B supplies column l%32 at the same k, which
+//   is exactly one packed 32-bit word; accumulator element v of lane l holds
+//   D[(v%4) + 8*(v/4) + 4*(l/32)][l%32].
+// K advances in 128-wide stages, three in flight through LDS by DMA as
+// above.  Fragments are read and the packed words expanded one 32-wide step
+// ahead of the MFMAs that use them; the per-stage barrier sits before the
+// last step of a stage, so the MFMA issue never waits on its own operands.
+// ---------------------------------------------------------------------------
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+template <int WM, int WN, Epilogue EP>
+__global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a) {
+    constexpr int BM = 256, BN = 256;
+    constexpr bool kGlu = EP == Epilogue::kGluBf16;
+    constexpr int kWavesPerBlock = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int kCols = kGlu ? BN / 2 : BN;
+    static_assert(!kGlu || FN % 2 == 0, "GLU tiles pair gate and up fragments");
+    constexpr int kAStage = BM * kBK;
+    constexpr int kBStage = BN * (kBK / 4);
+    constexpr int kADma = kAStage / 1024 / kWavesPerBlock;
+    constexpr int kBDma = kBStage / 1024 / kWavesPerBlock;
+    constexpr int kDma = kADma + kBDma;
+    static_assert(kADma * 1024 * kWavesPerBlock == kAStage && kBDma * 1024 * kWavesPerBlock == kBStage,
+                  "stage must split into whole 1 KiB DMA instructions per wave");
+    static_assert(kStages == 3, "the stage loop below is unrolled by three");
+    constexpr int KS = kBK / 32;  // 32-wide k steps per stage
+    // One LDS object per stage buffer: with distinct objects the compiler can
+    // tell that the DMA into one buffer does not feed the reads of another, so
+    // it does not wait for every DMA in flight before each LDS read.
+    __shared__ __attribute__((aligned(1024))) int8_t lds_a0[kAStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds_a1[kAStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds_a2[kAStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds_b0[kBStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds_b1[kBStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds_b2[kBStage];
+    // Per-token epilogue constants of the block's rows (gamma / s, sum q),
+    // staged in LDS so that the epilogue issues no global load between its
+    // stores (a load would wait for every earlier store: one memory counter).
+    __shared__ float row_scale[BM];
+    __shared__ int32_t row_sumq[BM];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int nwords = K / 16;
+    const int b = blockIdx.y;
+    const int ntn = (N + kCols - 1) / kCols;
+    const int t = xcd_tile(blockIdx.x, gridDim.x);
+    const int tn = t % ntn;
+    const int tm = t / ntn;
+    const int m0 = tm * BM;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+
+    const int64_t nrows = kGlu ? 2 * (int64_t)N : (int64_t)N;
+    const int8_t* Q = a.q + (int64_t)b * M * K;
+    const uint32_t* P = reinterpret_cast<const uint32_t*>(a.packed) + (int64_t)b * nrows * nwords;
+
+    // DMA sources as 32-bit offsets from per-block bases.
+    const int8_t* qbase = Q + (int64_t)m0 * K;
+    uint32_t aoffs[kADma], boffs[kBDma];
+#pragma unroll
+    for (int i = 0; i < kADma; ++i) {
+        const int r = (wave * kADma + i) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ (r & 7);
+        aoffs[i] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + 16 * chunk);
+    }
+    const int64_t brow0 = b_row<BN, kGlu>(tn, 0, N);
+#pragma unroll
+    for (int i = 0; i < kBDma; ++i) {
+        const int r = (wave * kBDma + i) * 32 + (lane >> 1);
+        const int half = (lane & 1) ^ ((r >> 3) & 1);
+        boffs[i] = (uint32_t)((b_row<BN, kGlu>(tn, r, N) - brow0) * nwords + 4 * half);
+    }
+    const uint32_t* pbase = P + brow0 * nwords;
+    const int nstages = K / kBK;
+
+    auto abuf = [&](auto bufc) -> int8_t* {
+        constexpr int B_ = decltype(bufc)::value;
+        return B_ == 0 ? lds_a0 : (B_ == 1 ? lds_a1 : lds_a2);
+    };
+    auto bbuf = [&](auto bufc) -> int8_t* {
+        constexpr int B_ = decltype(bufc)::value;
+        return B_ == 0 ? lds_b0 : (B_ == 1 ? lds_b1 : lds_b2);
+    };
+    // Byte offsets of B sources (relative to pbase) for the asm DMA.
+#pragma unroll
+    for (int i = 0; i < kBDma; ++i) boffs[i] *= 4;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // DMA d (0 <= d < kDma: first the A pieces, then the B pieces) of stage st.
+    auto issue_dma = [&](auto bufc, int st, int d) {
+        if (d < kADma) {
+            const uint32_t abase = lds_address(abuf(bufc)) + wave_u * kADma * 1024;
+            dma16(qbase + st * kBK, aoffs[d], abase + d * 1024);
+        } else {
+            const uint32_t bbase = lds_address(bbuf(bufc)) + wave_u * kBDma * 1024;
+            dma16(reinterpret_cast<const int8_t*>(pbase) + st * (kBK / 4), boffs[d - kADma],
+                  bbase + (d - kADma) * 1024);
+        }
+    };
+    auto issue_stage = [&](auto bufc, int st) {
+#pragma unroll
+        for (int d = 0; d < kDma; ++d) issue_dma(bufc, st, d);
+    };
+
+    // Fragment rows in LDS: A row wm*TM + i*32 + lane%32 (128 bytes a row),
+    // B row per fragment j (32 bytes a row).  Swizzle terms depend on the lane.
+    const int arow0 = (wm * TM + (lane & 31)) * kBK;
+    const int aswz = lane & 7;
+    const int bswz = (lane >> 3) & 1;
+    int brow[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        if (kGlu)
+            brow[j] = ((j < FN / 2 ? 0 : BN / 2) + wn * (TN / 2) + (j % (FN / 2)) * 32 + (lane & 31)) * 32;
+        else
+            brow[j] = (wn * TN + j * 32 + (lane & 31)) * 32;
+    }
+
+    struct Frags {
+        i32x4 a[FM];
+        uint32_t w[FN];  // packed B words, expanded just before use
+    };
+    // Operands of 32-wide step ks of a stage: A 16-byte chunk 2*ks + lane/32
+    // of the row, B word 2*ks + lane/32 of the row (in half (2ks+lane/32)/4).
+    auto load_frags = [&](auto bufc, Frags& f, int ks) {
+        const int8_t* abase = abuf(bufc);
+        const int8_t* bbase = bbuf(bufc);
+        const int c = 2 * ks + (lane >> 5);
+        const int ach = (c ^ aswz) * 16;
+        const int bw = (((c >> 2) ^ bswz) * 4 + (c & 3)) * 4;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) f.w[j] = *reinterpret_cast<const uint32_t*>(bbase + brow[j] + bw);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f.a[i] = *reinterpret_cast<const i32x4*>(abase + arow0 + i * 32 * kBK + ach);
+    };
+    auto expand = [&](const Frags& f, i32x4 (&bq)[FN]) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            int32_t c0, c1, c2, c3;
+            decode_codes(f.w[j], c0, c1, c2, c3);
+            bq[j] = i32x4{c0, c1, c2, c3};
+        }
+    };
+
+    i32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = i32x16{};
+
+    static_assert(BM <= WM * WN * kWave, "one row constant per thread");
+    // Row constants are loaded first (they complete before the DMAs, which
+    // the memory counter retires in order) and parked in LDS after the loop.
+    int32_t my_sumq = 0;
+    float my_s = 1.0f;
+    if (tid < BM) {
+        const int64_t tk = (int64_t)b * M + min(m0 + tid, M - 1);
+        my_sumq = a.sumq[tk];
+        if (EP != Epilogue::kI32) my_s = a.s[tk];
+    }
+    const float gamma = a.gamma ? a.gamma[b] : 0.0f;
+
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    // Stages 0 and 1 now; stage st+2 is issued during stage st, its DMAs
+    // spread over the first steps so they do not all queue at one moment.
+    issue_stage(C0{}, 0);
+    if (nstages > 1) issue_stage(C1{}, 1);
+    if (nstages > 1)
+        __builtin_amdgcn_s_waitcnt(kDma | (7 << 4) | (15 << 8));
+    else
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    Frags cur, nxt;
+    i32x4 bcur[FN], bnxt[FN];
+    load_frags(C0{}, cur, 0);
+    expand(cur, bcur);
+
+    // One stage held in buffer BUF (= st % 3).
+    auto run_stage = [&](auto bufc, int st) {
+        constexpr int BUF = decltype(bufc)::value;
+        using Next = std::integral_constant<int, (BUF + 1) % 3>;
+        using Free = std::integral_constant<int, (BUF + 2) % 3>;  // released at the last barrier
+        constexpr int kPerStep = (kDma + KS - 2) / (KS - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bool more = ks < KS - 1 || st + 1 < nstages;
+            if (ks == KS - 1) {
+                // This wave's reads of the stage have returned; once every
+                // wave is here, stage st+1 has landed (its DMAs are older than
+                // the kDma of stage st+2) and this buffer may be refilled.
+                if (st + 1 < nstages) {
+                    if (st + 2 < nstages)
+                        __builtin_amdgcn_s_waitcnt(kDma | (7 << 4) | (0 << 8));
+                    else
+                        __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    load_frags(Next{}, nxt, 0);
+                }
+            } else {
+                if (st + 2 < nstages) {
+#pragma unroll
+                    for (int d = ks * kPerStep; d < (ks + 1) * kPerStep && d < kDma; ++d)
+                        issue_dma(Free{}, st + 2, d);
+                }
+                load_frags(bufc, nxt, ks + 1);
+            }
+            // Fixed issue order (sched_barrier fences): the next step's LDS
+            // reads were issued above; the MFMAs of this step follow, and the
+            // expansion of the next step's packed words is slotted between
+            // them once the reads have had two MFMAs (64 cycles) to return.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int idx = 0; idx < FM * FN; ++idx) {
+                const int i = idx / FN, j = idx % FN;
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], bcur[j], acc[i][j], 0, 0, 0);
+                const int jd = idx - 1;
+                if (more && jd >= 0 && jd < FN) {
+                    int32_t c0, c1, c2, c3;
+                    decode_codes(nxt.w[jd], c0, c1, c2, c3);
+                    bnxt[jd] = i32x4{c0, c1, c2, c3};
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            cur = nxt;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
+        }
+    };
+    for (int st = 0; st < nstages; st += 3) {
+        run_stage(C0{}, st);
+        if (st + 1 < nstages) run_stage(C1{}, st + 1);
+        if (st + 2 < nstages) run_stage(C2{}, st + 2);
+    }
+
+    // Epilogue: subtract sum_k q, rescale (or form the GLU product), store.
+    if (tid < BM) {
+        row_sumq[tid] = my_sumq;
+        row_scale[tid] = EP == Epilogue::kI32 ? 0.0f : gamma / my_s;
+    }
+    __syncthreads();
+    const int64_t tok0 = (int64_t)b * M;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = wm * TM + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * (lane >> 5);
+            const int m = m0 + r;
+            if (m >= M) continue;
+            const int64_t tk = tok0 + m;
+            const int32_t sq = row_sumq[r];
+            const float cs = row_scale[r];
+            if (kGlu) {
+#pragma unroll
+                for (int j = 0; j < FN / 2; ++j) {
+                    const int f = tn * (BN / 2) + wn * (TN / 2) + j * 32 + (lane & 31);
+                    if (f < N) {
+                        const float zg = rescale(acc[i][j][v] - sq, cs);
+                        const float zu = rescale(acc[i][j + FN / 2][v] - sq, cs);
+                        static_cast<uint16_t*>(a.out)[tk * N + f] = glu_bf16(zg, zu);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = tn * BN + wn * TN + j * 32 + (lane & 31);
+                    if (n < N) {
+                        const int32_t val = acc[i][j][v] - sq;
+                        if (EP == Epilogue::kI32)
+                            static_cast<int32_t*>(a.out)[tk * N + n] = val;
+                        else
+                            static_cast<float*>(a.out)[tk * N + n] = rescale(val, cs);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int WM, int WN, Epilogue EP>
+hipError_t launch_x32(const ProductArgs& a, hipStream_t stream) {
+    constexpr int kCols = EP == Epilogue::kGluBf16 ? 128 : 256;
+    const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + 255) / 256);
+    const dim3 grid((unsigned)tiles, (unsigned)a.batch);
+    gemm_x32_kernel<WM, WN, EP><<<grid, WM * WN * kWave, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, Epilogue EP>
+hipError_t launch_dma_tile(const ProductArgs& a, hipStream_t stream) {
+    using T = Tile<BM, BN, WM, WN, EP>;
+    const int64_t tiles = (int64_t)((a.N + T::kCols - 1) / T::kCols) * ((a.M + BM - 1) / BM);
+    const dim3 grid((unsigned)tiles, (unsigned)a.batch);
+    gemm_dma_kernel<BM, BN, WM, WN, EP><<<grid, T::kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, Epilogue EP>
+hipError_t launch_tile(const ProductArgs& a, hipStream_t stream) {
+    using T = Tile<BM, BN, WM, WN, EP>;
+    const int64_t tiles = (int64_t)((a.N + T::kCols - 1) / T::kCols) * ((a.M + BM - 1) / BM);
+    const dim3 grid((unsigned)tiles, (unsigned)a.batch);
+    gemm_kernel<BM, BN, WM, WN, EP><<<grid, T::kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 template <Epilogue EP>
 hipError_t launch_ep(const ProductArgs& a, hipStream_t stream) {
-    const int cols_per_block = EP == Epilogue::kGluBf16 ? kBN / 2 : kBN;
-    const int64_t tiles = (int64_t)((a.N + cols_per_block - 1) / cols_per_block) *
-                          ((a.M + kBM - 1) / kBM);
-    const dim3 grid((unsigned)tiles, (unsigned)a.batch);
-    gemm_mfma_kernel<EP><<<grid, kThreads, 0, stream>>>(a);
-    return hipGetLastError();
+    // Large problems: 256 x 256 tiles.  Small token counts: 64-token tiles so
+    // that fewer padded rows are computed.
+    const bool whole_stages = a.K % kBK == 0;
+    if (a.M > 128)
+        return whole_stages ? launch_x32<BIG_WM, BIG_WN, EP>(a, stream) : launch_tile<256, 256, 4, 2, EP>(a, stream);
+    return whole_stages ? launch_dma_tile<64, 256, 1, 8, EP>(a, stream)
+                        : launch_tile<64, 256, 1, 8, EP>(a, stream);
 }
 
 }  // namespace
