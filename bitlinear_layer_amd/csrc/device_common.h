@@ -150,6 +150,62 @@ __device__ __forceinline__ int32_t group_row_sums(int32_t (&v)[U], int lane) {
     }
 }
 
+// Wave-wide all-reduce over the same hypercube, without LDS: every lane
+// returns the total.  At each level a lane combines its value with its
+// partner's.  A permlane swap of a register with itself leaves the lane's own
+// value in one result and the partner's in the other, so combining the two
+// results needs no lane test; the combine is commutative, so both lanes of a
+// pair hold the same bits and the total is identical in all 64 lanes.
+template <int O>
+__device__ __forceinline__ void xor_pair_u32(uint32_t v, uint32_t& a, uint32_t& b) {
+    if constexpr (O == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        a = (uint32_t)r[0];
+        b = (uint32_t)r[1];
+    } else if constexpr (O == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        a = (uint32_t)r[0];
+        b = (uint32_t)r[1];
+    } else {
+        a = v;
+        b = (uint32_t)dpp_partner<O>((int32_t)v);
+    }
+}
+
+template <typename T, typename Combine, int O = 32>
+__device__ __forceinline__ T wave_allreduce(T v, Combine combine) {
+    if constexpr (O == 0) {
+        return v;
+    } else {
+        T a, b;
+        if constexpr (sizeof(T) == 8) {
+            const uint64_t u = __builtin_bit_cast(uint64_t, v);
+            uint32_t alo, blo, ahi, bhi;
+            xor_pair_u32<O>((uint32_t)u, alo, blo);
+            xor_pair_u32<O>((uint32_t)(u >> 32), ahi, bhi);
+            a = __builtin_bit_cast(T, ((uint64_t)ahi << 32) | alo);
+            b = __builtin_bit_cast(T, ((uint64_t)bhi << 32) | blo);
+        } else {
+            uint32_t ua, ub;
+            xor_pair_u32<O>(__builtin_bit_cast(uint32_t, v), ua, ub);
+            a = __builtin_bit_cast(T, ua);
+            b = __builtin_bit_cast(T, ub);
+        }
+        constexpr int next = O == 32 ? 16 : (O == 16 ? 8 : (O == 8 ? 4 : (O == 4 ? 2 : (O == 2 ? 1 : 0))));
+        return wave_allreduce<T, Combine, next>(combine(a, b), combine);
+    }
+}
+
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+    return wave_allreduce(v, [](double a, double b) { return a + b; });
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    return wave_allreduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ int32_t wave_sum_dpp(int32_t v) {
+    return wave_allreduce(v, [](int32_t a, int32_t b) { return a + b; });
+}
+
 // Block reductions: every thread returns the block-wide result.  `scratch`
 // holds at least blockDim.x / 64 elements; the helper synchronises before
 // reusing it, so consecutive calls may share one scratch array.

@@ -9,11 +9,14 @@
 //   xn = (x * r) * g,  s = 127 / max(max|xn|, 1e-5),  q = clip(rint(xn * s))
 // with every fp32 operation correctly rounded (no fast-math, no contraction).
 //
-// One 256-thread block per token row; each thread keeps its slice of the
-// row in registers (8 bf16 per 16-byte load), so x is read from HBM once and
-// q written once.  Three block reductions: fp64 sum of squares (fixed tree
-// order, deterministic), fp32 max, int32 sum of the codes (the sum the
-// offset-coded product subtracts).
+// Two layouts, same arithmetic: waves streaming over many rows (wave-wide
+// reductions, no barriers), one 256-thread block per row for few rows.  Each
+// thread keeps its slice of the row in registers (8 bf16 per 16-byte load),
+// so x is read from HBM once and q written once.  Three reductions: fp64
+// sum of squares (fixed tree order, deterministic), fp32 max, int32 sum of
+// the codes (the sum the offset-coded product subtracts).
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -101,6 +104,262 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __
     }
 }
 
+// Streaming layout for many rows: each wave walks the rows
+// wave_id, wave_id + W, ... (W = waves in the grid) and loads the next row's
+// x while it reduces and stores the current one, so HBM reads and writes
+// overlap across the whole pass.  Lane l owns the 8-element chunks
+// l, l + 64, ... of a row; the three reductions are wave-wide over
+// permlane/DPP (no LDS, no barrier).  The row index is wave-uniform, so
+// addressing runs on the scalar unit.
+//
+// The pass is VALU-bound unless each element costs few instructions
+// (a wave64 VALU op takes 4 cycles on a 16-lane SIMD), so the arithmetic is
+// written to need about nine per element while staying bit-identical to the
+// definition above:
+//   * x^2 of a bf16 value is exact in fp64, so fma(x, x, ss) equals ss + x*x;
+//   * |xn * s| <= 127 * (1 + 2^-22) by construction (|xn| <= amax, s is the
+//     correctly rounded 127 / max(amax, 1e-5)), so the clip never binds;
+//   * for |y| < 2^22, fl(y + 1.5 * 2^23) = 1.5 * 2^23 + rint(y) (ties to
+//     even), so the bit pattern of that sum minus 0x4B400000 is the integer
+//     code: its low byte is the int8 code and integer sums of the patterns
+//     give the code sum.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
+
+// FULL: the row is exactly CPL * 64 chunks, so no lane needs a bounds test.
+template <int CPL, bool FULL>
+__device__ __forceinline__ void load_x_row(const uint16_t* __restrict__ xr, uint32_t lane, int nchunks,
+                                           uint4 (&dst)[CPL]) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const uint32_t idx = lane + (uint32_t)c * kWave;
+        if (FULL) {
+            dst[c] = load_stream16(reinterpret_cast<const uint32_t*>(xr + 8 * idx));
+        } else {
+            dst[c] = make_uint4(0u, 0u, 0u, 0u);
+            if (idx < (uint32_t)nchunks)
+                dst[c] = load_stream16(reinterpret_cast<const uint32_t*>(xr + 8 * idx));
+        }
+    }
+}
+
+template <int CPL, bool FULL>
+__device__ __forceinline__ void load_g_row(const float* __restrict__ gr, uint32_t lane, int nchunks,
+                                           float4 (&dst)[CPL][2]) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const uint32_t idx = lane + (uint32_t)c * kWave;
+        if (FULL || idx < (uint32_t)nchunks) {
+            dst[c][0] = *reinterpret_cast<const float4*>(gr + 8 * idx);
+            dst[c][1] = *reinterpret_cast<const float4*>(gr + 8 * idx + 4);
+        } else {
+            dst[c][0] = dst[c][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+// RMSNorm + quantisation of one row held in registers (xc: bf16 pairs);
+// gfetch(c, lo, hi) yields the RMSNorm weight of this lane's chunk c (zero
+// past the row end).  Lane 0 writes s and the code sum.
+template <int CPL, bool FULL, typename GFetch>
+__device__ __forceinline__ void quant_row_regs(const uint4 (&xc)[CPL], GFetch gfetch, int64_t row,
+                                               uint32_t lane, int K, float eps,
+                                               int8_t* __restrict__ q, float* __restrict__ s,
+                                               int32_t* __restrict__ sumq) {
+    const int nchunks = K / 8;
+    float v[CPL][8];
+    double ss0 = 0.0, ss1 = 0.0;  // two chains halve the fma latency stall
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const uint32_t p[4] = {xc[c].x, xc[c].y, xc[c].z, xc[c].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[c][2 * j] = bf16_lo(p[j]);
+            v[c][2 * j + 1] = bf16_hi(p[j]);
+            ss0 = fma((double)v[c][2 * j], (double)v[c][2 * j], ss0);
+            ss1 = fma((double)v[c][2 * j + 1], (double)v[c][2 * j + 1], ss1);
+        }
+    }
+    const double ss = wave_sum_dpp(ss0 + ss1);
+    const float ms = (float)(ss / (double)K);
+    const float r = 1.0f / sqrtf(ms + eps);
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        // Compiler-only fence: keeps the weight reads of each group of four
+        // chunks next to their use instead of all hoisted up front (which
+        // spills for long rows).
+        if (CPL > 8 && c % 4 == 0) asm volatile("" ::: "memory");
+        float4 g0, g1;
+        gfetch(c, g0, g1);
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v[c][j] = (v[c][j] * r) * gg[j];
+            amax = fmaxf(amax, fabsf(v[c][j]));
+        }
+    }
+    amax = wave_max_dpp(amax);
+    const float scale = 127.0f / fmaxf(amax, 1e-5f);
+
+    uint32_t bits_sum = 0;
+    int8_t* qr = q + row * K;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        uint32_t b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            b[j] = __float_as_uint(v[c][j] * scale + kRoundMagic);
+            bits_sum += b[j];
+        }
+        // low bytes of b[0..3] and b[4..7] -> two words of int8 codes
+        const uint32_t w0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u),
+                                                  0x05040100u);
+        const uint32_t w1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
+                                                  0x05040100u);
+        const uint32_t idx = lane + (uint32_t)c * kWave;
+        if (FULL || idx < (uint32_t)nchunks)
+            *reinterpret_cast<uint2*>(qr + 8 * idx) = make_uint2(w0, w1);
+    }
+    if (sumq) {
+        // each lane summed CPL * 8 patterns (zeros past the row end give
+        // exactly the offset), so subtract that many offsets, mod 2^32
+        const int32_t lane_sum = (int32_t)(bits_sum - (uint32_t)(CPL * 8) * kRoundMagicBits);
+        const int32_t total = wave_sum_dpp(lane_sum);
+        if (lane == 0) sumq[row] = total;
+    }
+    if (lane == 0) s[row] = scale;
+}
+
+// Rows of at most 8 chunks per lane prefetch the next row's x (two buffers,
+// alternating, so no copies); longer rows skip the prefetch to stay within
+// the register file, leaving the other resident waves to cover the load
+// latency.  When one RMSNorm weight serves every row, each block stages it
+// once in LDS (low and high halves of each 8-element chunk in separate
+// arrays, so a wave's 16-byte reads are contiguous and bank-conflict free);
+// re-reading it from L2 per wave and row would move more bytes than x itself.
+// With a weight per group of rows it is loaded from memory per row.
+constexpr int kStreamThreads = 256;
+constexpr int64_t kStreamBlocks = 1024;  // 4 blocks (16 waves) per CU on 256 CUs
+
+template <int CPL>
+constexpr size_t stream_lds_bytes() { return 2 * CPL * kWave * sizeof(float4); }
+
+// SHARED_G: one weight for all rows (staged in LDS); otherwise a weight per
+// group of rows_per_g rows, loaded per row.
+template <int CPL, bool FULL, bool SHARED_G, bool PREFETCH = (SHARED_G && CPL <= 8)>
+__global__ __launch_bounds__(kStreamThreads) void quant_stream_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ g, int64_t rows_per_g, int64_t rows,
+    int K, float eps, int8_t* __restrict__ q, float* __restrict__ s, int32_t* __restrict__ sumq) {
+    extern __shared__ float4 g_lds[];  // [2][CPL * 64]: low halves, then high halves
+    constexpr int kSpan = CPL * kWave;
+    constexpr int kWavesPerBlock = kStreamThreads / kWave;
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    const int nchunks = K / 8;
+
+    if constexpr (SHARED_G) {
+        for (int i = threadIdx.x; i < kSpan; i += kStreamThreads) {
+            float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+            if (FULL || i < nchunks) {
+                lo = *reinterpret_cast<const float4*>(g + 8 * i);
+                hi = *reinterpret_cast<const float4*>(g + 8 * i + 4);
+            }
+            g_lds[i] = lo;
+            g_lds[kSpan + i] = hi;
+        }
+        __syncthreads();
+    }
+    int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (row >= rows) return;
+
+    if constexpr (SHARED_G) {
+        auto from_lds = [&](int c, float4& lo, float4& hi) {
+            const uint32_t idx = lane + (uint32_t)c * kWave;
+            lo = g_lds[idx];
+            hi = g_lds[kSpan + idx];
+        };
+        if constexpr (PREFETCH) {
+            uint4 xa[CPL], xb[CPL];
+            auto step = [&](const uint4 (&cur)[CPL], uint4 (&nxt)[CPL]) {
+                if (row + stride < rows) load_x_row<CPL, FULL>(x + (row + stride) * K, lane, nchunks, nxt);
+                quant_row_regs<CPL, FULL>(cur, from_lds, row, lane, K, eps, q, s, sumq);
+                row += stride;
+            };
+            load_x_row<CPL, FULL>(x + row * K, lane, nchunks, xa);
+            for (;;) {
+                step(xa, xb);
+                if (row >= rows) break;
+                step(xb, xa);
+                if (row >= rows) break;
+            }
+        } else {
+            uint4 xc[CPL];
+            for (; row < rows; row += stride) {
+                load_x_row<CPL, FULL>(x + row * K, lane, nchunks, xc);
+                quant_row_regs<CPL, FULL>(xc, from_lds, row, lane, K, eps, q, s, sumq);
+            }
+        }
+    } else if constexpr (CPL <= 8) {
+        uint4 xc[CPL];
+        float4 gv[CPL][2];
+        auto from_regs = [&](int c, float4& lo, float4& hi) {
+            lo = gv[c][0];
+            hi = gv[c][1];
+        };
+        for (; row < rows; row += stride) {
+            load_x_row<CPL, FULL>(x + row * K, lane, nchunks, xc);
+            load_g_row<CPL, FULL>(g + (row / rows_per_g) * K, lane, nchunks, gv);
+            quant_row_regs<CPL, FULL>(xc, from_regs, row, lane, K, eps, q, s, sumq);
+        }
+    } else {
+        // long rows: read the weight where it is used, four chunks at a time
+        uint4 xc[CPL];
+        for (; row < rows; row += stride) {
+            const float* gr = g + (row / rows_per_g) * K;
+            auto from_global = [&](int c, float4& lo, float4& hi) {
+                const uint32_t idx = lane + (uint32_t)c * kWave;
+                lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (FULL || idx < (uint32_t)nchunks) {
+                    lo = *reinterpret_cast<const float4*>(gr + 8 * idx);
+                    hi = *reinterpret_cast<const float4*>(gr + 8 * idx + 4);
+                }
+            };
+            load_x_row<CPL, FULL>(x + row * K, lane, nchunks, xc);
+            quant_row_regs<CPL, FULL>(xc, from_global, row, lane, K, eps, q, s, sumq);
+        }
+    }
+}
+
+// Ragged long rows with a weight per group of rows do not fit the register
+// file in the streaming layout; they take the block-per-row kernels.
+constexpr bool stream_per_row_g_ok(int cpl, bool full) { return full || cpl <= 12; }
+
+template <int CPL, bool FULL>
+void launch_stream_g(dim3 grid, hipStream_t stream, const uint16_t* x, const float* g,
+                     int64_t rows_per_g, int64_t rows, int K, float eps, const ActStage& out) {
+    if (rows_per_g >= rows) {
+        quant_stream_kernel<CPL, FULL, true><<<grid, kStreamThreads, stream_lds_bytes<CPL>(), stream>>>(
+            x, g, rows_per_g, rows, K, eps, out.q, out.s, out.sumq);
+    } else if constexpr (stream_per_row_g_ok(CPL, FULL)) {
+        quant_stream_kernel<CPL, FULL, false><<<grid, kStreamThreads, 0, stream>>>(
+            x, g, rows_per_g, rows, K, eps, out.q, out.s, out.sumq);
+    }
+}
+
+template <int CPL>
+void launch_stream(dim3 grid, hipStream_t stream, const uint16_t* x, const float* g, int64_t rows_per_g,
+                   int64_t rows, int K, float eps, const ActStage& out) {
+    if (K == CPL * kWave * 8)
+        launch_stream_g<CPL, true>(grid, stream, x, g, rows_per_g, rows, K, eps, out);
+    else
+        launch_stream_g<CPL, false>(grid, stream, x, g, rows_per_g, rows, K, eps, out);
+}
+
 // Rows longer than 8 * 8 * 256 elements: same arithmetic, re-reading x and g
 // from memory (L2) in each of the three passes instead of holding the row.
 __global__ __launch_bounds__(kQuantThreads) void quant_long_kernel(
@@ -170,7 +429,35 @@ ActStage act_stage_carve(void* base, int64_t rows, int64_t K) {
 
 hipError_t launch_quant(const uint16_t* x, const float* g, int64_t rows, int64_t rows_per_g, int K,
                         float eps, ActStage out, hipStream_t stream) {
-    const int cpt = (K / 8 + kQuantThreads - 1) / kQuantThreads;
+    const int nchunks = K / 8;
+    const int cpl = (nchunks + kWave - 1) / kWave;  // chunks per lane, one wave per row
+    const bool full = K == cpl * kWave * 8;
+    if (rows >= 64 && cpl <= 16 && (rows_per_g >= rows || stream_per_row_g_ok(cpl, full))) {
+        const int64_t waves_per_block = kStreamThreads / kWave;
+        const dim3 grid((unsigned)std::min<int64_t>((rows + waves_per_block - 1) / waves_per_block,
+                                                    kStreamBlocks));
+        switch (cpl) {
+            case 1: launch_stream<1>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 2: launch_stream<2>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 3: launch_stream<3>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 4: launch_stream<4>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 5: launch_stream<5>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 6: launch_stream<6>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 7: launch_stream<7>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 8: launch_stream<8>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 9: launch_stream<9>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 10: launch_stream<10>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 11: launch_stream<11>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 12: launch_stream<12>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 13: launch_stream<13>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 14: launch_stream<14>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            case 15: launch_stream<15>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+            default: launch_stream<16>(grid, stream, x, g, rows_per_g, rows, K, eps, out); break;
+        }
+        return hipGetLastError();
+    }
+    // Few rows: one block per row spreads each row over more lanes.
+    const int cpt = (nchunks + kQuantThreads - 1) / kQuantThreads;
     const dim3 grid((unsigned)rows);
     if (cpt <= 1)
         quant_kernel<1><<<grid, kQuantThreads, 0, stream>>>(x, g, rows_per_g, K, eps, out.q, out.s, out.sumq);

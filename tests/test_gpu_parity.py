@@ -98,6 +98,21 @@ def test_quantize(M, K, recipe):
     gu.assert_q_parity(q.cpu().numpy(), q_ref, s.cpu().numpy(), s_ref)
 
 
+# Many rows take the streaming layout (a wave per row); K picks the chunks
+# per lane (1..16), exact multiples of 512 skip the bounds tests, and K above
+# 8192 falls back to a block per row.
+@pytest.mark.parametrize("K", [16, 512, 528, 2080, 4096, 5632, 6912, 8192, 8208])
+def test_quantize_many_rows(K):
+    M = 96
+    _say("quantize many rows", M, K)
+    x = wl.make_x(M, K, "student_t3", seed=K, outlier_frac=0.01, outlier_scale=20.0)
+    x[7] = 0                                    # zero row inside the stream
+    g = wl.rms_weight(K, "random", seed=K + 1)
+    q_ref, s_ref = gu.orc().rmsnorm_quant(x, g)
+    q, s = bl.bitlinear_quantize(gu.to_dev_bf16(x), gu.to_dev(g))
+    gu.assert_q_parity(q.cpu().numpy(), q_ref, s.cpu().numpy(), s_ref)
+
+
 def test_quantize_edge_rows():
     _say("quantize edge rows")
     K = 64
@@ -211,6 +226,26 @@ def test_forward_batched(K):
         for b in range(B):
             ref = gu.orc().bitlinear(xs[b], gs[b], Ws[b])
             gu.assert_y_parity(y[b], ref["y"])
+
+
+# Batched with a weight per slice and enough rows for the streaming layout:
+# long exact rows, long ragged rows and ragged rows past the register budget.
+@pytest.mark.parametrize("K", [4160, 5632, 6912])
+def test_forward_batched_long_rows(K):
+    B, M, N = 4, 20, 64
+    _say("batched long rows", B, M, N, K)
+    xs = [wl.x_normal(M, K, seed=40 + b) for b in range(B)]
+    Ws = [wl.w_normal(N, K, seed=50 + b) for b in range(B)]
+    gs = [wl.rms_weight(K, "random", seed=60 + b) for b in range(B)]
+    packs = [gu.pack_on_gpu(W) for W in Ws]
+    x = torch.stack([gu.to_dev_bf16(a) for a in xs])
+    g = torch.stack([gu.to_dev(a) for a in gs])
+    packed = torch.stack([p for p, _ in packs])
+    gamma = torch.cat([gm for _, gm in packs])
+    y = bl.bitlinear_forward_batched(x, g, packed, gamma).cpu().numpy()
+    for b in range(B):
+        ref = gu.orc().bitlinear(xs[b], gs[b], Ws[b])
+        gu.assert_y_parity(y[b], ref["y"])
 
 
 def test_forward_structural_zeros():
