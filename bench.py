@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -90,11 +91,19 @@ def timed_loop(torch, fn, steps, warmup, stream):
 DECODE_SOURCES = ("decode.hip", "device_common.h", "epilogue.h", "launch.h")
 
 
+def _code_only(text):
+    """Source text without comments and blank space, so that editing a
+    comment does not mark stored counters stale (any code change does)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(*names):
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "bitlinear_layer_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "bitlinear_layer_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

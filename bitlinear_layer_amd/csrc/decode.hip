@@ -7,7 +7,8 @@
 //      层的创新"]: activations read once, normalised and quantised on chip):
 //      fp64 sum of squares, fp32 absmax and the int8 codes go to LDS; the
 //      block's reductions use a fixed order, so every block computes the
-//      same codes as the stand-alone quantisation kernel, bit for bit;
+//      same codes, bit for bit, as the block-per-row quantisation kernel
+//      (the layout the stand-alone pass uses below 64 rows);
 //   2. each lane copies the codes of the k-columns it owns into registers;
 //   3. the block streams its share of the weight rows: LPR lanes share a
 //      row, each loading 16 bytes (64 weights) per step with U rows in
@@ -27,7 +28,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
 // Block-cooperative RMSNorm + absmax int8 of one token row into LDS; the
-// same arithmetic and reduction order as quant_kernel, so the codes agree.
+// same arithmetic and reduction order as the block-per-row quant_kernel, so
+// the codes agree with it.
 __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__ xr,
                                                     const float* __restrict__ gr, int K, float eps,
                                                     int8_t* __restrict__ qrow, double* dscr,
