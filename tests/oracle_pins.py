@@ -353,6 +353,41 @@ def pin_glu_step(orc):
     assert np.all(out0["y"] == 0.0)
 
 
+def pin_glu_silu_invariants(orc):
+    """SiLU and the gate/up split pinned by properties rather than by the
+    formula: since sigmoid(v) + sigmoid(-v) = 1, SiLU(v) - SiLU(-v) = v, so
+    negating the gate rows of W (which negates gate exactly and leaves up)
+    must change h by gate * up, up to bf16 rounding; far out on either side
+    SiLU(v) -> v and SiLU(v) -> 0.  Scaling the RMSNorm weight by 2^12
+    scales z = [gate, up] by exactly 2^12 (the per-token scale absorbs it),
+    which pushes most gates past |30|."""
+    M, D, F = 4, 64, 40
+    x = wl.x_normal(M, D, seed=93)
+    g_gu = wl.rms_weight(D, "random", seed=93)
+    g_dn = wl.rms_weight(F, "random", seed=94)
+    W_gu = wl.w_normal(2 * F, D, seed=93)
+    W_dn = wl.w_normal(D, F, seed=94)
+    W_neg = W_gu.copy()
+    W_neg[:F] = -W_neg[:F]
+    z1 = orc.bitlinear(x, g_gu, W_gu)["y"]
+    for c in (1.0, 4096.0):
+        gc = (g_gu * np.float32(c)).astype(np.float32)
+        z = orc.bitlinear(x, gc, W_gu)["y"]
+        assert np.array_equal(z, z1 * c)
+        gate, up = z[:, :F], z[:, F:]
+        zn = orc.bitlinear(x, gc, W_neg)["y"]
+        assert np.array_equal(zn[:, :F], -gate) and np.array_equal(zn[:, F:], up)
+        hp = wl.bf16_bits_to_f32(orc.glu(x, gc, W_gu, g_dn, W_dn)["h"]).astype(np.float64)
+        hm = wl.bf16_bits_to_f32(orc.glu(x, gc, W_neg, g_dn, W_dn)["h"]).astype(np.float64)
+        assert np.all(np.abs(hp - hm - gate * up) <= 2.0 ** -8 * (np.abs(hp) + np.abs(hm)) + 1e-30)
+        if c > 1.0:
+            pos, neg = gate > 30.0, gate < -30.0
+            assert pos.sum() >= 10 and neg.sum() >= 10
+            prod = np.array([orc.double_to_bf16(v) for v in (gate * up)[pos]], np.uint16)
+            assert np.array_equal(wl.bf16_bits_to_f32(prod).astype(np.float64), hp[pos])
+            assert np.all(np.abs(hp[neg]) <= 1e-11 * np.abs(up[neg]))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
