@@ -247,10 +247,7 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 
 constexpr int kStages = 3;
 
-#ifndef BIG_WM
-#define BIG_WM 4
-#define BIG_WN 2
-#endif
+
 
 template <int BM, int BN, int WM, int WN, Epilogue EP>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a) {
@@ -419,9 +416,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
 // ---------------------------------------------------------------------------
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
-template <int WM, int WN, Epilogue EP>
+template <int BM, int WM, int WN, Epilogue EP>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a) {
-    constexpr int BM = 256, BN = 256;
+    constexpr int BN = 256;
     constexpr bool kGlu = EP == Epilogue::kGluBf16;
     constexpr int kWavesPerBlock = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -698,12 +695,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     }
 }
 
-template <int WM, int WN, Epilogue EP>
+template <int BM, int WM, int WN, Epilogue EP>
 hipError_t launch_x32(const ProductArgs& a, hipStream_t stream) {
     constexpr int kCols = EP == Epilogue::kGluBf16 ? 128 : 256;
-    const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + 255) / 256);
+    const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + BM - 1) / BM);
     const dim3 grid((unsigned)tiles, (unsigned)a.batch);
-    gemm_x32_kernel<WM, WN, EP><<<grid, WM * WN * kWave, 0, stream>>>(a);
+    gemm_x32_kernel<BM, WM, WN, EP><<<grid, WM * WN * kWave, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -730,8 +727,14 @@ hipError_t launch_ep(const ProductArgs& a, hipStream_t stream) {
     // Large problems: 256 x 256 tiles.  Small token counts: 64-token tiles so
     // that fewer padded rows are computed.
     const bool whole_stages = a.K % kBK == 0;
-    if (a.M > 128)
-        return whole_stages ? launch_x32<BIG_WM, BIG_WN, EP>(a, stream) : launch_tile<256, 256, 4, 2, EP>(a, stream);
+    if (a.M > 128) {
+        if (!whole_stages) return launch_tile<256, 256, 4, 2, EP>(a, stream);
+        // 256 x 256 tiles (8 waves of 64 x 128) unless they would leave at
+        // least half of the 256 CUs idle; then 128 x 256 (8 waves of 64 x 64).
+        constexpr int kCols = EP == Epilogue::kGluBf16 ? 128 : 256;
+        const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + 255) / 256) * a.batch;
+        return tiles > 128 ? launch_x32<256, 4, 2, EP>(a, stream) : launch_x32<128, 2, 4, EP>(a, stream);
+    }
     return whole_stages ? launch_dma_tile<64, 256, 1, 8, EP>(a, stream)
                         : launch_tile<64, 256, 1, 8, EP>(a, stream);
 }
