@@ -233,13 +233,21 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 // inline asm so that the compiler does not track these writes into LDS: its
 // conservative tracking would wait for every DMA in flight before each LDS
 // read.  The kernels order all DMA reuse of LDS themselves with explicit
-// s_waitcnt vmcnt(n) and barriers; the instruction has no register outputs
-// and reads its address operands at issue.
+// s_waitcnt vmcnt(n) and barriers.  The instruction has no register outputs
+// and takes its address operands and M0 at issue, so M0 is restored right
+// after it (M0 is reserved to the compiler); one wait state separates the
+// M0 write from the DMA that reads it.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_addr), "v"(voff), "s"(gbase)
-                 : "memory", "m0");
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "s"(lds_addr), "v"(voff), "s"(gbase)
+        : "memory");
 }
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -411,8 +419,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
 //   D[(v%4) + 8*(v/4) + 4*(l/32)][l%32].
 // K advances in 128-wide stages, three in flight through LDS by DMA as
 // above.  Fragments are read and the packed words expanded one 32-wide step
-// ahead of the MFMAs that use them; the per-stage barrier sits before the
-// last step of a stage, so the MFMA issue never waits on its own operands.
+// ahead of the MFMAs that use them; the per-stage barrier follows the MFMAs
+// of the last step of a stage, which run while the wave waits there.
 // ---------------------------------------------------------------------------
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
 #pragma unroll
     for (int i = 0; i < kBDma; ++i) {
         const int r = (wave * kBDma + i) * 32 + (lane >> 1);
-        const int half = (lane & 1) ^ ((r >> 3) & 1);
+        const int half = (lane & 1) ^ ((r >> 2) & 1);
         boffs[i] = (uint32_t)((b_row<BN, kGlu>(tn, r, N) - brow0) * nwords + 4 * half);
     }
     const uint32_t* pbase = P + brow0 * nwords;
@@ -513,11 +521,18 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
         for (int d = 0; d < kDma; ++d) issue_dma(bufc, st, d);
     };
 
-    // Fragment rows in LDS: A row wm*TM + i*32 + lane%32 (128 bytes a row),
-    // B row per fragment j (32 bytes a row).  Swizzle terms depend on the lane.
+    // Order of k inside a stage: step ks multiplies the 16-byte A chunks and
+    // packed B words ks (lanes 0..31) and 4 + ks (lanes 32..63), so over a
+    // stage a lane touches one 16-byte half of each B row only: it reads that
+    // half once per stage (ds_read_b128) and expands one word per step.  The
+    // integer sum does not depend on the order of k.
+    // Fragment rows in LDS: A row wm*TM + i*32 + lane%32 (128 bytes a row;
+    // chunk c stored at c ^ (row & 7)), B row per fragment j (32 bytes a row;
+    // half h stored at h ^ ((row >> 2) & 1), so that the eight lanes of each
+    // 128-byte read phase cover all 32 banks).
     const int arow0 = (wm * TM + (lane & 31)) * kBK;
     const int aswz = lane & 7;
-    const int bswz = (lane >> 3) & 1;
+    const int bhalf = ((lane >> 5) ^ ((lane >> 2) & 1)) * 16;
     int brow[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -529,29 +544,26 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
 
     struct Frags {
         i32x4 a[FM];
-        uint32_t w[FN];  // packed B words, expanded just before use
     };
-    // Operands of 32-wide step ks of a stage: A 16-byte chunk 2*ks + lane/32
-    // of the row, B word 2*ks + lane/32 of the row (in half (2ks+lane/32)/4).
     auto load_frags = [&](auto bufc, Frags& f, int ks) {
         const int8_t* abase = abuf(bufc);
-        const int8_t* bbase = bbuf(bufc);
-        const int c = 2 * ks + (lane >> 5);
-        const int ach = (c ^ aswz) * 16;
-        const int bw = (((c >> 2) ^ bswz) * 4 + (c & 3)) * 4;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) f.w[j] = *reinterpret_cast<const uint32_t*>(bbase + brow[j] + bw);
+        const int ach = ((ks + 4 * (lane >> 5)) ^ aswz) * 16;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             f.a[i] = *reinterpret_cast<const i32x4*>(abase + arow0 + i * 32 * kBK + ach);
     };
-    auto expand = [&](const Frags& f, i32x4 (&bq)[FN]) {
+    auto load_words = [&](auto bufc, uint4 (&wb)[FN]) {
+        const int8_t* bbase = bbuf(bufc);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            int32_t c0, c1, c2, c3;
-            decode_codes(f.w[j], c0, c1, c2, c3);
-            bq[j] = i32x4{c0, c1, c2, c3};
-        }
+        for (int j = 0; j < FN; ++j) wb[j] = *reinterpret_cast<const uint4*>(bbase + brow[j] + bhalf);
+    };
+    auto word_of = [](const uint4& v, int ks) -> uint32_t {
+        return ks == 0 ? v.x : (ks == 1 ? v.y : (ks == 2 ? v.z : v.w));
+    };
+    auto expand_one = [&](const uint4& v, int ks, i32x4& bq) {
+        int32_t c0, c1, c2, c3;
+        decode_codes(word_of(v, ks), c0, c1, c2, c3);
+        bq = i32x4{c0, c1, c2, c3};
     };
 
     i32x16 acc[FM][FN];
@@ -588,9 +600,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     asm volatile("" ::: "memory");
 
     Frags cur, nxt;
+    uint4 wb[FN];  // this stage's packed B words of the lane (one 16-byte half per row)
     i32x4 bcur[FN], bnxt[FN];
+    load_words(C0{}, wb);
     load_frags(C0{}, cur, 0);
-    expand(cur, bcur);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) expand_one(wb[j], 0, bcur[j]);
 
     // One stage held in buffer BUF (= st % 3).
     auto run_stage = [&](auto bufc, int st) {
@@ -600,11 +615,42 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
         constexpr int kPerStep = (kDma + KS - 2) / (KS - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bool more = ks < KS - 1 || st + 1 < nstages;
-            if (ks == KS - 1) {
-                // This wave's reads of the stage have returned; once every
-                // wave is here, stage st+1 has landed (its DMAs are older than
-                // the kDma of stage st+2) and this buffer may be refilled.
+            if (ks < KS - 1) {
+                if (st + 2 < nstages) {
+#pragma unroll
+                    for (int d = ks * kPerStep; d < (ks + 1) * kPerStep && d < kDma; ++d)
+                        issue_dma(Free{}, st + 2, d);
+                }
+                load_frags(bufc, nxt, ks + 1);
+                // Fixed issue order (sched_barrier fences): the next step's A
+                // reads were issued above; the MFMAs of this step follow, with
+                // the expansion of the next step's B words (already in
+                // registers) slotted between them.
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int idx = 0; idx < FM * FN; ++idx) {
+                    const int i = idx / FN, j = idx % FN;
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], bcur[j], acc[i][j], 0, 0, 0);
+                    if (idx < FN) expand_one(wb[idx], ks + 1, bnxt[idx]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                cur = nxt;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
+            } else {
+                // Last step: its MFMAs go first and keep the matrix core busy
+                // while the wave waits at the stage barrier.  Once this wave's
+                // reads of the stage have returned and every wave is at the
+                // barrier, stage st+1 has landed (its DMAs are older than the
+                // kDma of stage st+2) and this buffer may be refilled; then
+                // the first fragments of stage st+1 are read and expanded.
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int idx = 0; idx < FM * FN; ++idx) {
+                    const int i = idx / FN, j = idx % FN;
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], bcur[j], acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (st + 1 < nstages) {
                     if (st + 2 < nstages)
                         __builtin_amdgcn_s_waitcnt(kDma | (7 << 4) | (0 << 8));
@@ -613,36 +659,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    load_frags(Next{}, nxt, 0);
-                }
-            } else {
-                if (st + 2 < nstages) {
+                    load_words(Next{}, wb);
+                    load_frags(Next{}, cur, 0);
 #pragma unroll
-                    for (int d = ks * kPerStep; d < (ks + 1) * kPerStep && d < kDma; ++d)
-                        issue_dma(Free{}, st + 2, d);
+                    for (int j = 0; j < FN; ++j) expand_one(wb[j], 0, bcur[j]);
                 }
-                load_frags(bufc, nxt, ks + 1);
             }
-            // Fixed issue order (sched_barrier fences): the next step's LDS
-            // reads were issued above; the MFMAs of this step follow, and the
-            // expansion of the next step's packed words is slotted between
-            // them once the reads have had two MFMAs (64 cycles) to return.
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int idx = 0; idx < FM * FN; ++idx) {
-                const int i = idx / FN, j = idx % FN;
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], bcur[j], acc[i][j], 0, 0, 0);
-                const int jd = idx - 1;
-                if (more && jd >= 0 && jd < FN) {
-                    int32_t c0, c1, c2, c3;
-                    decode_codes(nxt.w[jd], c0, c1, c2, c3);
-                    bnxt[jd] = i32x4{c0, c1, c2, c3};
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            cur = nxt;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
         }
     };
     for (int st = 0; st < nstages; st += 3) {
