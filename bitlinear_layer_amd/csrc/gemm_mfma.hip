@@ -417,10 +417,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
 //   a 32-wide k step; lane l of B supplies column l%32 at the same k, which
 //   is exactly one packed 32-bit word; accumulator element v of lane l holds
 //   D[(v%4) + 8*(v/4) + 4*(l/32)][l%32].
-// K advances in 128-wide stages, three in flight through LDS by DMA as
-// above.  Fragments are read and the packed words expanded one 32-wide step
-// ahead of the MFMAs that use them; the per-stage barrier follows the MFMAs
-// of the last step of a stage, which run while the wave waits there.
+// K advances in 128-wide stages through four LDS buffers (all 160 KiB of
+// the CU for 256 x 256 tiles), filled by DMA as above and taken in pairs
+// with one barrier per pair.  Fragments are read and the packed words
+// expanded one 32-wide step ahead of the MFMAs that use them; the barrier
+// follows the MFMAs of the pair's last step, which run while the wave waits
+// there.
 // ---------------------------------------------------------------------------
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     constexpr int kDma = kADma + kBDma;
     static_assert(kADma * 1024 * kWavesPerBlock == kAStage && kBDma * 1024 * kWavesPerBlock == kBStage,
                   "stage must split into whole 1 KiB DMA instructions per wave");
-    static_assert(kStages == 3, "the stage loop below is unrolled by three");
+    constexpr int kXStages = 4;  // LDS buffers; stages run in pairs, one barrier per pair
     constexpr int KS = kBK / 32;  // 32-wide k steps per stage
     // One LDS object per stage buffer: with distinct objects the compiler can
     // tell that the DMA into one buffer does not feed the reads of another, so
@@ -448,14 +450,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     __shared__ __attribute__((aligned(1024))) int8_t lds_a0[kAStage];
     __shared__ __attribute__((aligned(1024))) int8_t lds_a1[kAStage];
     __shared__ __attribute__((aligned(1024))) int8_t lds_a2[kAStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds_a3[kAStage];
     __shared__ __attribute__((aligned(1024))) int8_t lds_b0[kBStage];
     __shared__ __attribute__((aligned(1024))) int8_t lds_b1[kBStage];
     __shared__ __attribute__((aligned(1024))) int8_t lds_b2[kBStage];
-    // Per-token epilogue constants of the block's rows (gamma / s, sum q),
-    // staged in LDS so that the epilogue issues no global load between its
-    // stores (a load would wait for every earlier store: one memory counter).
-    __shared__ float row_scale[BM];
-    __shared__ int32_t row_sumq[BM];
+    __shared__ __attribute__((aligned(1024))) int8_t lds_b3[kBStage];
 
     const int M = a.M, N = a.N, K = a.K;
     const int nwords = K / 16;
@@ -495,11 +494,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
 
     auto abuf = [&](auto bufc) -> int8_t* {
         constexpr int B_ = decltype(bufc)::value;
-        return B_ == 0 ? lds_a0 : (B_ == 1 ? lds_a1 : lds_a2);
+        return B_ == 0 ? lds_a0 : (B_ == 1 ? lds_a1 : (B_ == 2 ? lds_a2 : lds_a3));
     };
     auto bbuf = [&](auto bufc) -> int8_t* {
         constexpr int B_ = decltype(bufc)::value;
-        return B_ == 0 ? lds_b0 : (B_ == 1 ? lds_b1 : lds_b2);
+        return B_ == 0 ? lds_b0 : (B_ == 1 ? lds_b1 : (B_ == 2 ? lds_b2 : lds_b3));
     };
     // Byte offsets of B sources (relative to pbase) for the asm DMA.
 #pragma unroll
@@ -563,6 +562,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     auto expand_one = [&](const uint4& v, int ks, i32x4& bq) {
         int32_t c0, c1, c2, c3;
         decode_codes(word_of(v, ks), c0, c1, c2, c3);
+        // Pin the expanded codes in registers where they are computed: the
+        // register allocator would otherwise recompute these cheap shifts
+        // right before the MFMAs that read them, stalling their issue.
+        asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
         bq = i32x4{c0, c1, c2, c3};
     };
 
@@ -587,14 +590,15 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
-    // Stages 0 and 1 now; stage st+2 is issued during stage st, its DMAs
-    // spread over the first steps so they do not all queue at one moment.
+    using C3 = std::integral_constant<int, 3>;
+    // Stages go in pairs (2j, 2j+1) with one barrier per pair, at the end of
+    // the odd stage.  At that barrier both stages of the next pair have
+    // landed; their DMAs are issued during the even stage of the current pair
+    // into the two buffers the previous pair released, spread over its first
+    // steps.  Stages 0 and 1 are loaded here.
     issue_stage(C0{}, 0);
     if (nstages > 1) issue_stage(C1{}, 1);
-    if (nstages > 1)
-        __builtin_amdgcn_s_waitcnt(kDma | (7 << 4) | (15 << 8));
-    else
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -607,55 +611,73 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
 #pragma unroll
     for (int j = 0; j < FN; ++j) expand_one(wb[j], 0, bcur[j]);
 
-    // One stage held in buffer BUF (= st % 3).
+    // One stage held in buffer BUF (= st % 4); BUF is even for the first
+    // stage of a pair.
     auto run_stage = [&](auto bufc, int st) {
         constexpr int BUF = decltype(bufc)::value;
-        using Next = std::integral_constant<int, (BUF + 1) % 3>;
-        using Free = std::integral_constant<int, (BUF + 2) % 3>;  // released at the last barrier
-        constexpr int kPerStep = (kDma + KS - 2) / (KS - 1);
+        constexpr bool kFirstOfPair = BUF % 2 == 0;
+        using Next = std::integral_constant<int, (BUF + 1) % kXStages>;
+        constexpr int kPairDma = 2 * kDma;
+        constexpr int kPerStep = (kPairDma + KS - 2) / (KS - 1);
+        // DMA d of the pair (stage st+2 for d < kDma, else st+3) into the
+        // buffer two ahead of this one (released at the last barrier).
+        auto pair_dma = [&](int d) {
+            if (d < kDma) {
+                if (st + 2 < nstages)
+                    issue_dma(std::integral_constant<int, (BUF + 2) % kXStages>{}, st + 2, d);
+            } else {
+                if (st + 3 < nstages)
+                    issue_dma(std::integral_constant<int, (BUF + 3) % kXStages>{}, st + 3, d - kDma);
+            }
+        };
+        // The MFMAs of one step, with the expansion of the next step's B
+        // words (words w of wsrc) slotted between them.
+        auto mfma_step = [&](const uint4 (&wsrc)[FN], int w, bool expand_next) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int idx = 0; idx < FM * FN; ++idx) {
+                const int i = idx / FN, j = idx % FN;
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], bcur[j], acc[i][j], 0, 0, 0);
+                if (expand_next && idx < FN) expand_one(wsrc[idx], w, bnxt[idx]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks < KS - 1) {
-                if (st + 2 < nstages) {
+                if (kFirstOfPair) {
 #pragma unroll
-                    for (int d = ks * kPerStep; d < (ks + 1) * kPerStep && d < kDma; ++d)
-                        issue_dma(Free{}, st + 2, d);
+                    for (int d = ks * kPerStep; d < (ks + 1) * kPerStep && d < kPairDma; ++d) pair_dma(d);
                 }
+                // the next step's A reads first, then this step's MFMAs
                 load_frags(bufc, nxt, ks + 1);
-                // Fixed issue order (sched_barrier fences): the next step's A
-                // reads were issued above; the MFMAs of this step follow, with
-                // the expansion of the next step's B words (already in
-                // registers) slotted between them.
-                __builtin_amdgcn_sched_barrier(0);
+                mfma_step(wb, ks + 1, true);
+                cur = nxt;
 #pragma unroll
-                for (int idx = 0; idx < FM * FN; ++idx) {
-                    const int i = idx / FN, j = idx % FN;
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], bcur[j], acc[i][j], 0, 0, 0);
-                    if (idx < FN) expand_one(wb[idx], ks + 1, bnxt[idx]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
+            } else if (kFirstOfPair) {
+                // Last step of the first stage of a pair: stage st+1 landed
+                // before the last barrier, so its first operands are read
+                // ahead of this step's MFMAs, as within a stage (its B words
+                // replace this stage's, which are all expanded by now).  When
+                // st is the last stage these reads fetch a stale buffer that
+                // nothing uses and no DMA writes; taking this path without a
+                // test on st keeps the register allocation of the loop tight.
+                load_words(Next{}, wb);
+                load_frags(Next{}, nxt, 0);
+                mfma_step(wb, 0, true);
                 cur = nxt;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
             } else {
-                // Last step: its MFMAs go first and keep the matrix core busy
-                // while the wave waits at the stage barrier.  Once this wave's
-                // reads of the stage have returned and every wave is at the
-                // barrier, stage st+1 has landed (its DMAs are older than the
-                // kDma of stage st+2) and this buffer may be refilled; then
-                // the first fragments of stage st+1 are read and expanded.
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int idx = 0; idx < FM * FN; ++idx) {
-                    const int i = idx / FN, j = idx % FN;
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], bcur[j], acc[i][j], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                // Last step of a pair: its MFMAs go first and keep the matrix
+                // core busy while the wave waits at the barrier.  Once this
+                // wave's DMAs and reads are done and every wave is there, the
+                // next pair has landed and this pair's buffers are released;
+                // then the first operands of stage st+1 are read and expanded.
+                mfma_step(wb, 0, false);
                 if (st + 1 < nstages) {
-                    if (st + 2 < nstages)
-                        __builtin_amdgcn_s_waitcnt(kDma | (7 << 4) | (0 << 8));
-                    else
-                        __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+                    __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
@@ -667,13 +689,21 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
             }
         }
     };
-    for (int st = 0; st < nstages; st += 3) {
+    for (int st = 0; st < nstages; st += kXStages) {
         run_stage(C0{}, st);
         if (st + 1 < nstages) run_stage(C1{}, st + 1);
         if (st + 2 < nstages) run_stage(C2{}, st + 2);
+        if (st + 3 < nstages) run_stage(C3{}, st + 3);
     }
 
     // Epilogue: subtract sum_k q, rescale (or form the GLU product), store.
+    // The per-token constants of the block's rows (gamma / s, sum q) go to a
+    // stage buffer that every wave has finished with, so that the epilogue
+    // issues no global load between its stores (a load would wait for every
+    // earlier store: one memory counter).
+    __syncthreads();
+    int32_t* row_sumq = reinterpret_cast<int32_t*>(lds_a0);
+    float* row_scale = reinterpret_cast<float*>(lds_a0 + BM * sizeof(int32_t));
     if (tid < BM) {
         row_sumq[tid] = my_sumq;
         row_scale[tid] = EP == Epilogue::kI32 ? 0.0f : gamma / my_s;

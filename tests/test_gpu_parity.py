@@ -136,8 +136,9 @@ def test_quantize_edge_rows():
 MATMUL = [(M, N, K) for M in (1, 3, 8, 130, 257) for (N, K) in ((7, 16), (129, 48), (300, 2064))]
 # K % 128 == 0 with M > 128 runs the 32x32x32 MFMA kernel: 128-row tiles
 # when 256-row tiles would be few (first two), 256-row tiles otherwise; all
-# with ragged M and N, and more than three LDS stages.
-MATMUL += [(300, 520, 1024), (129, 256, 128), (2900, 3000, 512)]
+# with ragged M and N, and even and odd numbers of LDS stages (one, three,
+# four, five, eight).
+MATMUL += [(300, 520, 1024), (129, 256, 128), (2900, 3000, 512), (300, 520, 384), (2900, 3000, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", MATMUL)
