@@ -710,6 +710,46 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     }
     __syncthreads();
     const int64_t tok0 = (int64_t)b * M;
+    // Interior tiles (the common case) store without bounds tests, from a
+    // block-uniform base plus a 32-bit lane offset; edge tiles test each row
+    // and column.  Row r of the tile starts r * N elements after the base.
+    const int col0 = tn * kCols;
+    const bool interior = m0 + BM <= M && col0 + kCols <= N && (int64_t)BM * N <= ((int64_t)1 << 28);
+    if (interior) {
+        constexpr uint32_t kEsz = kGlu ? 2 : 4;  // bytes per output element
+        char* const obase = static_cast<char*>(a.out) + ((tok0 + m0) * N + col0) * kEsz;
+        const uint32_t lane_col = (kGlu ? wn * (TN / 2) : wn * TN) + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r0 = wm * TM + i * 32 + 4 * (lane >> 5);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = r0 + (v & 3) + 8 * (v >> 2);
+                const int32_t sq = row_sumq[r];
+                const float cs = row_scale[r];
+                // byte offset of this lane's first column in row r (< 2^31)
+                const uint32_t off = ((uint32_t)r * (uint32_t)N + lane_col) * kEsz;
+                if (kGlu) {
+#pragma unroll
+                    for (int j = 0; j < FN / 2; ++j) {
+                        const float zg = rescale(acc[i][j][v] - sq, cs);
+                        const float zu = rescale(acc[i][j + FN / 2][v] - sq, cs);
+                        *reinterpret_cast<uint16_t*>(obase + off + j * 32 * kEsz) = glu_bf16(zg, zu);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int32_t val = acc[i][j][v] - sq;
+                        if (EP == Epilogue::kI32)
+                            *reinterpret_cast<int32_t*>(obase + off + j * 32 * kEsz) = val;
+                        else
+                            *reinterpret_cast<float*>(obase + off + j * 32 * kEsz) = rescale(val, cs);
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
