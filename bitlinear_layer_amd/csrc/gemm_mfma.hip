@@ -834,6 +834,7 @@ hipError_t launch_ep(const ProductArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_gemm_mfma(const ProductArgs& a, Epilogue ep, hipStream_t stream) {
+    if (skinny_supported(a.M, a.K, ep)) return launch_skinny(a, ep, stream);
     switch (ep) {
         case Epilogue::kF32: return launch_ep<Epilogue::kF32>(a, stream);
         case Epilogue::kI32: return launch_ep<Epilogue::kI32>(a, stream);

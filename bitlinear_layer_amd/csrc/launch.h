@@ -66,6 +66,12 @@ struct ProductArgs {
 hipError_t launch_gemv(const ProductArgs& a, Epilogue ep, hipStream_t stream);
 hipError_t launch_gemm_mfma(const ProductArgs& a, Epilogue ep, hipStream_t stream);
 
+// Few-token product on the matrix cores (weights streamed into registers):
+// M <= kSkinnyMaxM, K % 256 == 0, F32 or I32 epilogue.
+constexpr int kSkinnyMaxM = 16;
+bool skinny_supported(int M, int K, Epilogue ep);
+hipError_t launch_skinny(const ProductArgs& a, Epilogue ep, hipStream_t stream);
+
 // Largest M the GEMV kernel takes.
 constexpr int kGemvMaxM = 8;
 

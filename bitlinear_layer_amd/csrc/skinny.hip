@@ -1,0 +1,164 @@
+// skinny.hip -- the ternary product for a few tokens (5..16) on the int8
+// matrix cores, streaming the packed weights from HBM into registers.
+//
+// With M <= 16 tokens the product is bound by reading the packed weights
+// (N*K/4 bytes against 2*M*N*K operations), and a 16 x 16 x 64 MFMA covers
+// all tokens of 16 weight rows at once ([jiqizhixin, "具有三值权重的 MatMul-free
+// 密集层"]: the ternary product is an add/subtract accumulation; on the
+// matrix cores it is the same integer sum, exactly):
+//   * the block stages the int8 codes q of its M tokens in LDS once, rows
+//     padded by 16 bytes so that the rows a read phase touches fall in
+//     distinct banks; MFMA rows past M take zeros;
+//   * each wave owns 16 * U weight rows and walks K in 256-wide chunks:
+//     lane l loads 16 bytes (64 weights) of row l % 16, the quarter l / 16 of
+//     the chunk, with plain vector loads double-buffered a few chunks ahead
+//     (each load instruction thus reads 64 contiguous bytes of 16 rows, which
+//     streams at about 5.3 TB/s, below the 512-byte runs of the one-token
+//     kernel: the main limit of this kernel);
+//   * step t (0..3) of a chunk multiplies word t of that quarter, i.e. the
+//     chunk's k in 16 * (4 * (l / 16) + t) + 0..15, against the codes of the
+//     same k read from LDS: MFMA lane l of A is token l % 16, of B weight row
+//     l % 16, and both take k-slice l / 16, so each step sums 64 distinct k
+//     and the four steps cover the chunk once (the order of k does not
+//     change the integer sum);
+//   * the accumulator of lane l holds tokens 4 * (l / 16) + v of weight row
+//     l % 16 over the whole K, so no cross-lane reduction is needed; the
+//     epilogue subtracts sum_k q (the weights are stored as w + 1) and
+//     rescales ([datacamp, "Các thành phần lõi: MLGRU và GLU"]: scaled
+//     ternary accumulation).
+#include "epilogue.h"
+
+namespace bl {
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSkinnyThreads = 256;
+constexpr int kSkinnyWaves = kSkinnyThreads / kWave;
+constexpr int kSkinnyU = 2;      // 16-row weight groups per wave
+constexpr int kChunkK = 256;     // k per chunk (64 packed bytes of a row)
+constexpr int kGroup = 4;        // chunks per load group (double-buffered)
+
+template <Epilogue EP>
+__global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(ProductArgs a) {
+    extern __shared__ int8_t qs[];  // [M][K + 16] int8 codes
+    const int M = a.M, N = a.N, K = a.K;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const int pitch = K + 16;
+    const int nchunks = K / kChunkK;
+    const int ngroups = (nchunks + kGroup - 1) / kGroup;
+    const int64_t row_bytes = K / 4;
+    const int n0 = (blockIdx.x * kSkinnyWaves + wave) * 16 * kSkinnyU;
+
+    // This lane's 16-byte quarter of each chunk of its weight rows (clamped
+    // rows past N are read but never stored).
+    const uint8_t* wrow[kSkinnyU];
+#pragma unroll
+    for (int u = 0; u < kSkinnyU; ++u)
+        wrow[u] = a.packed + ((int64_t)b * N + min(n0 + 16 * u + r, N - 1)) * row_bytes + 16 * g;
+
+    uint4 wv[2][kGroup][kSkinnyU];
+    auto load_group = [&](int grp, uint4 (&dst)[kGroup][kSkinnyU]) {
+#pragma unroll
+        for (int c = 0; c < kGroup; ++c) {
+            const int chunk = grp * kGroup + c;
+#pragma unroll
+            for (int u = 0; u < kSkinnyU; ++u) {
+                dst[c][u] = make_uint4(0u, 0u, 0u, 0u);
+                if (chunk < nchunks)
+                    dst[c][u] = load_stream16(reinterpret_cast<const uint32_t*>(wrow[u] + 64 * chunk));
+            }
+        }
+    };
+    // The first weights are requested before the codes are staged, so HBM
+    // is busy from the start.
+    load_group(0, wv[0]);
+
+    const int8_t* Q = a.q + (int64_t)b * M * K;
+    const int kq = K / 16;  // 16-byte pieces per row
+    for (int i = threadIdx.x; i < M * kq; i += kSkinnyThreads) {
+        const int row = i / kq, piece = i - row * kq;
+        *reinterpret_cast<int4*>(qs + row * pitch + 16 * piece) =
+            *reinterpret_cast<const int4*>(Q + (int64_t)row * K + 16 * piece);
+    }
+    __syncthreads();
+
+    i32x4 acc[kSkinnyU];
+#pragma unroll
+    for (int u = 0; u < kSkinnyU; ++u) acc[u] = i32x4{0, 0, 0, 0};
+    const bool token = r < M;  // MFMA row r is a real token
+    const int8_t* qrow = qs + min(r, M - 1) * pitch + 64 * g;
+
+    auto compute_group = [&](int grp, const uint4 (&src)[kGroup][kSkinnyU]) {
+#pragma unroll
+        for (int c = 0; c < kGroup; ++c) {
+            const int chunk = grp * kGroup + c;
+            if (chunk >= nchunks) break;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                i32x4 av = *reinterpret_cast<const i32x4*>(qrow + kChunkK * chunk + 16 * t);
+                if (!token) av = i32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int u = 0; u < kSkinnyU; ++u) {
+                    const uint32_t w = t == 0 ? src[c][u].x : (t == 1 ? src[c][u].y : (t == 2 ? src[c][u].z : src[c][u].w));
+                    int32_t c0, c1, c2, c3;
+                    decode_codes(w, c0, c1, c2, c3);
+                    acc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{c0, c1, c2, c3}, acc[u], 0, 0, 0);
+                }
+            }
+        }
+    };
+    for (int grp = 0; grp < ngroups; grp += 2) {
+        if (grp + 1 < ngroups) load_group(grp + 1, wv[1]);
+        compute_group(grp, wv[0]);
+        if (grp + 1 < ngroups) {
+            if (grp + 2 < ngroups) load_group(grp + 2, wv[0]);
+            compute_group(grp + 1, wv[1]);
+        }
+    }
+
+    // Epilogue: lane l holds tokens 4g + v of weight row n0 + 16u + r.
+    const float gamma = EP == Epilogue::kI32 ? 0.0f : a.gamma[b];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * g + v;
+        if (m >= M) continue;
+        const int64_t tk = (int64_t)b * M + m;
+        const int32_t sq = a.sumq[tk];
+        const float cs = EP == Epilogue::kI32 ? 0.0f : gamma / a.s[tk];
+#pragma unroll
+        for (int u = 0; u < kSkinnyU; ++u) {
+            const int n = n0 + 16 * u + r;
+            if (n >= N) continue;
+            const int32_t val = acc[u][v] - sq;
+            if (EP == Epilogue::kI32)
+                static_cast<int32_t*>(a.out)[tk * N + n] = val;
+            else
+                static_cast<float*>(a.out)[tk * N + n] = rescale(val, cs);
+        }
+    }
+}
+
+}  // namespace
+
+bool skinny_supported(int M, int K, Epilogue ep) {
+    return M >= 1 && M <= kSkinnyMaxM && K % kChunkK == 0 && ep != Epilogue::kGluBf16 &&
+           (size_t)M * (K + 16) <= 64 * 1024;
+}
+
+hipError_t launch_skinny(const ProductArgs& a, Epilogue ep, hipStream_t stream) {
+    if (!skinny_supported(a.M, a.K, ep)) return hipErrorInvalidValue;
+    constexpr int kRowsPerBlock = kSkinnyWaves * 16 * kSkinnyU;
+    const dim3 grid((unsigned)((a.N + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)a.batch);
+    const size_t lds = (size_t)a.M * (a.K + 16);
+    if (ep == Epilogue::kI32)
+        skinny_kernel<Epilogue::kI32><<<grid, kSkinnyThreads, lds, stream>>>(a);
+    else
+        skinny_kernel<Epilogue::kF32><<<grid, kSkinnyThreads, lds, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace bl
