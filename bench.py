@@ -11,9 +11,10 @@ algorithmic bytes of one layer are N*K/4 (packed W) + 2*M*K (x) + 4*K (RMSNorm
 weight) + 4*M*N (y) + 4 (gamma).
 
 Also reported (`secondary`): the literal single-layer call at M=1, the M=8
-decode step, the 8192-token prefill (int8 TOPS of the MFMA product kernel,
-timed apart from the quantisation kernel), and the GLU mixer at M=1 and
-M=4096.  `roofline` is for the headline's dominant kernel, timed with HIP
+decode step, the one-token decode step of the 2560/6912 layer shapes (each
+over about 1 GiB of cold weights), the 8192-token prefill (int8 TOPS of the
+MFMA product kernel, timed apart from the quantisation kernel), and the GLU
+mixer at M=1 (one call, and one step through 128 mixers) and M=4096.  `roofline` is for the headline's dominant kernel, timed with HIP
 events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
 bounded sample of the headline workload on this host.
 
@@ -208,6 +209,35 @@ def bench_glu(torch, bl, wl, M, D, F, steps, warmup, stream):
                 tops=ops / (wall * 1e-3) / 1e12, bytes=nbytes, int8_ops=ops)
 
 
+def bench_glu_layers(torch, bl, wl, L, M, D, F, steps, warmup, stream):
+    """One decode step through L independent GLU mixers (one batched call)."""
+    x = torch.from_numpy(wl.x_normal(L * M, D, seed=2).view("int16")).to(DEV).view(L, M, D)
+    g_gu = torch.ones((L, D), dtype=torch.float32, device=DEV)
+    g_dn = torch.ones((L, F), dtype=torch.float32, device=DEV)
+    pgu = torch.empty((L, 2 * F, D // 4), dtype=torch.uint8, device=DEV)
+    pdn = torch.empty((L, D, F // 4), dtype=torch.uint8, device=DEV)
+    ggu = torch.empty(L, dtype=torch.float32, device=DEV)
+    gdn = torch.empty(L, dtype=torch.float32, device=DEV)
+    ws_p = torch.empty(max(bl.bitlinear_pack_workspace_bytes(2 * F, D), bl.bitlinear_pack_workspace_bytes(D, F)),
+                       dtype=torch.uint8, device=DEV)
+    for layer in range(L):
+        W = wl.w_normal_device(2 * F, D, seed=2, layer=2 * layer, device=DEV)
+        bl.bitlinear_pack_weights(W, packed=pgu[layer], gamma=ggu[layer:layer + 1], ws=ws_p)
+        W = wl.w_normal_device(D, F, seed=2, layer=2 * layer + 1, device=DEV)
+        bl.bitlinear_pack_weights(W, packed=pdn[layer], gamma=gdn[layer:layer + 1], ws=ws_p)
+        del W
+    y = torch.empty((L, M, D), dtype=torch.float32, device=DEV)
+    ws = torch.empty(bl.bitlinear_glu_batched_workspace_bytes(L, M, D, F), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    wall, ev = timed_loop(torch, lambda: bl.bitlinear_glu_forward_batched(x, g_gu, pgu, ggu, g_dn, pdn, gdn,
+                                                                          y=y, ws=ws), steps, warmup, stream)
+    nbytes = L * glu_bytes(M, D, F)
+    del x, g_gu, g_dn, pgu, pdn, ggu, gdn, y, ws
+    torch.cuda.empty_cache()
+    return dict(layers=L, M=M, D=D, F=F, bytes_per_step=nbytes, wall_ms=wall, event_ms=ev,
+                gbps=nbytes / (wall * 1e-3) / 1e9, kernel_gbps=nbytes / (ev * 1e-3) / 1e9)
+
+
 # --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
@@ -291,7 +321,14 @@ def main():
         log("[bench] prefill 8192")
         secondary["prefill_8192"] = bench_prefill(torch, bl, wl, 8192, 2048, 2048, max(10, args.steps // 2),
                                                   args.warmup, stream)
+        for K2, N2 in ((2560, 2560), (2560, 6912), (6912, 2560)):
+            L2 = max(64, (1 << 30) // layer_bytes(1, N2, K2))  # about 1 GiB of weights, cold
+            log(f"[bench] decode M=1 K={K2} N={N2} x {L2} layers")
+            secondary[f"decode_m1_k{K2}_n{N2}_layers"] = bench_decode(
+                torch, bl, wl, L2, 1, N2, K2, max(5, args.steps // 2), args.warmup, stream)
         log("[bench] glu")
+        secondary["glu_m1_layers"] = bench_glu_layers(torch, bl, wl, 128, 1, 2048, 5632, max(5, args.steps // 2),
+                                                      args.warmup, stream)
         secondary["glu_m1"] = bench_glu(torch, bl, wl, 1, 2048, 5632, 100, args.warmup, stream)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)

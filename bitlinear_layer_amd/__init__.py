@@ -56,6 +56,9 @@ _SIGNATURES = {
     "bitlinear_forward_batched": (_INT, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
     "bitlinear_glu_workspace_bytes": (_S, [_I, _I, _I]),
     "bitlinear_glu_forward": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P]),
+    "bitlinear_glu_batched_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "bitlinear_glu_forward_batched": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _S,
+                                             _P]),
     "bitlinear_glu_hidden": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P, _INT]),
     "bitlinear_quantize": (_INT, [_P, _P, _I, _I, _F, _P, _P, _P]),
     "bitlinear_ternary_matmul_i32": (_INT, [_P, _P, _I, _I, _I, _P, _P, _S, _P, _INT]),
@@ -285,6 +288,38 @@ def bitlinear_glu_forward(x, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_d
     _check(lib().bitlinear_glu_forward(_ptr(x), _ptr(rms_w_gu), _ptr(packed_gu), _ptr(gamma_gu),
                                        _ptr(rms_w_down), _ptr(packed_down), _ptr(gamma_down), M, D, F,
                                        float(eps), _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def bitlinear_glu_batched_workspace_bytes(B, M, D, F):
+    return lib().bitlinear_glu_batched_workspace_bytes(B, M, D, F)
+
+
+def bitlinear_glu_forward_batched(x, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down,
+                                  eps=1e-6, y=None, ws=None, stream=None):
+    """B independent mixers: x [B, M, D], rms_w_gu [B, D], packed_gu [B, 2F, D/4],
+    gamma_gu [B], rms_w_down [B, F], packed_down [B, D, F/4], gamma_down [B]
+    -> y [B, M, D]."""
+    _dev(x, "x", _BF16, 3)
+    _dev(rms_w_gu, "rms_w_gu", (torch.float32,), 2)
+    _dev(packed_gu, "packed_gu", (torch.uint8,), 3)
+    _dev(gamma_gu, "gamma_gu", (torch.float32,), 1)
+    _dev(rms_w_down, "rms_w_down", (torch.float32,), 2)
+    _dev(packed_down, "packed_down", (torch.uint8,), 3)
+    _dev(gamma_down, "gamma_down", (torch.float32,), 1)
+    B, M, D = x.shape
+    F = packed_down.shape[2] * 4
+    if (packed_gu.shape != (B, 2 * F, D // 4) or packed_down.shape[:2] != (B, D)
+            or rms_w_gu.shape != (B, D) or rms_w_down.shape != (B, F)
+            or gamma_gu.shape != (B,) or gamma_down.shape != (B,)):
+        raise ValueError("batched GLU shapes disagree with x")
+    if y is None:
+        y = torch.empty((B, M, D), dtype=torch.float32, device=x.device)
+    ws, nbytes = _workspace(bitlinear_glu_batched_workspace_bytes(B, M, D, F), ws, x.device)
+    _check(lib().bitlinear_glu_forward_batched(_ptr(x), _ptr(rms_w_gu), _ptr(packed_gu), _ptr(gamma_gu),
+                                               _ptr(rms_w_down), _ptr(packed_down), _ptr(gamma_down), B,
+                                               M, D, F, float(eps), _ptr(y), _ptr(ws), nbytes,
+                                               _stream(stream)))
     return y
 
 

@@ -181,6 +181,54 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
     return run_product(act, packed, gamma, M, N, K, B, y, bl::Epilogue::kF32, kernel, st);
 }
 
+// B independent GLU mixers of one shape (B = 1 for bitlinear_glu_forward).
+int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
+             const float* gamma_gu, const float* rms_w_down, const uint8_t* packed_down,
+             const float* gamma_down, int64_t B, int64_t M, int64_t D, int64_t F, float eps,
+             float* y, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_rows(M, "M"));
+    TRY(check_k(D, "D"));
+    TRY(check_k(F, "F"));
+    TRY(check_eps(eps));
+    CHECK(B >= 1 && B <= kMaxBatch, BITLINEAR_ERR_INVALID_ARG, "batch must be in [1, %lld]",
+          (long long)kMaxBatch);
+    CHECK(B * M <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "B*M exceeds BITLINEAR_MAX_DIM");
+    CHECK(B * M * D <= kMaxElems && 2 * F * D <= kMaxElems && B * M * F <= kMaxElems,
+          BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    if (M == 0) return BITLINEAR_OK;
+    CHECK_PTR(x);
+    CHECK_PTR(rms_w_gu);
+    CHECK_PTR(packed_gu);
+    CHECK_SCALAR(gamma_gu);
+    CHECK_PTR(rms_w_down);
+    CHECK_PTR(packed_down);
+    CHECK_SCALAR(gamma_down);
+    CHECK_PTR(y);
+    const int64_t rows = B * M;
+    TRY(check_ws(ws, ws_bytes, bitlinear_glu_workspace_bytes(rows, D, F)));
+    hipStream_t st = as_stream(stream);
+    char* base = static_cast<char*>(ws);
+    bl::ActStage act_x = bl::act_stage_carve(base, rows, D);
+    base += bl::act_stage_bytes(rows, D);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base);
+    base += bl::round_up(rows * F * 2, 256);
+    bl::ActStage act_h = bl::act_stage_carve(base, rows, F);
+    if (use_decode(M, D, BITLINEAR_KERNEL_AUTO)) {
+        TRY(run_decode(x, rms_w_gu, B > 1 ? D : 0, packed_gu, gamma_gu, B, M, F, D, eps, h,
+                       bl::Epilogue::kGluBf16, st));
+    } else {
+        TRY(hip_status(bl::launch_quant(x, rms_w_gu, rows, M, (int)D, eps, act_x, st), "quantise launch"));
+        TRY(run_product(act_x, packed_gu, gamma_gu, M, F, D, B, h, bl::Epilogue::kGluBf16,
+                        BITLINEAR_KERNEL_AUTO, st));
+    }
+    if (use_decode(M, F, BITLINEAR_KERNEL_AUTO))
+        return run_decode(h, rms_w_down, B > 1 ? F : 0, packed_down, gamma_down, B, M, D, F, eps, y,
+                          bl::Epilogue::kF32, st);
+    TRY(hip_status(bl::launch_quant(h, rms_w_down, rows, M, (int)F, eps, act_h, st), "quantise launch"));
+    return run_product(act_h, packed_down, gamma_down, M, D, F, B, y, bl::Epilogue::kF32,
+                       BITLINEAR_KERNEL_AUTO, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,42 +384,23 @@ int bitlinear_glu_forward(const uint16_t* x, const float* rms_w_gu, const uint8_
                           const float* gamma_gu, const float* rms_w_down,
                           const uint8_t* packed_down, const float* gamma_down, int64_t M, int64_t D,
                           int64_t F, float eps, float* y, void* ws, size_t ws_bytes, void* stream) {
-    TRY(check_rows(M, "M"));
-    TRY(check_k(D, "D"));
-    TRY(check_k(F, "F"));
-    TRY(check_eps(eps));
-    CHECK(M * D <= kMaxElems && 2 * F * D <= kMaxElems && M * F <= kMaxElems,
-          BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    if (M == 0) return BITLINEAR_OK;
-    CHECK_PTR(x);
-    CHECK_PTR(rms_w_gu);
-    CHECK_PTR(packed_gu);
-    CHECK_SCALAR(gamma_gu);
-    CHECK_PTR(rms_w_down);
-    CHECK_PTR(packed_down);
-    CHECK_SCALAR(gamma_down);
-    CHECK_PTR(y);
-    TRY(check_ws(ws, ws_bytes, bitlinear_glu_workspace_bytes(M, D, F)));
-    hipStream_t st = as_stream(stream);
-    char* base = static_cast<char*>(ws);
-    bl::ActStage act_x = bl::act_stage_carve(base, M, D);
-    base += bl::act_stage_bytes(M, D);
-    uint16_t* h = reinterpret_cast<uint16_t*>(base);
-    base += bl::round_up(M * F * 2, 256);
-    bl::ActStage act_h = bl::act_stage_carve(base, M, F);
-    if (use_decode(M, D, BITLINEAR_KERNEL_AUTO)) {
-        TRY(run_decode(x, rms_w_gu, 0, packed_gu, gamma_gu, 1, M, F, D, eps, h, bl::Epilogue::kGluBf16, st));
-    } else {
-        TRY(hip_status(bl::launch_quant(x, rms_w_gu, M, M, (int)D, eps, act_x, st), "quantise launch"));
-        TRY(run_product(act_x, packed_gu, gamma_gu, M, F, D, 1, h, bl::Epilogue::kGluBf16,
-                        BITLINEAR_KERNEL_AUTO, st));
-    }
-    if (use_decode(M, F, BITLINEAR_KERNEL_AUTO))
-        return run_decode(h, rms_w_down, 0, packed_down, gamma_down, 1, M, D, F, eps, y,
-                          bl::Epilogue::kF32, st);
-    TRY(hip_status(bl::launch_quant(h, rms_w_down, M, M, (int)F, eps, act_h, st), "quantise launch"));
-    return run_product(act_h, packed_down, gamma_down, M, D, F, 1, y, bl::Epilogue::kF32,
-                       BITLINEAR_KERNEL_AUTO, st);
+    return glu_impl(x, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down, 1, M, D,
+                    F, eps, y, ws, ws_bytes, stream);
+}
+
+size_t bitlinear_glu_batched_workspace_bytes(int64_t B, int64_t M, int64_t D, int64_t F) {
+    if (B <= 0) return 0;
+    return bitlinear_glu_workspace_bytes(B * M, D, F);
+}
+
+int bitlinear_glu_forward_batched(const uint16_t* x, const float* rms_w_gu,
+                                  const uint8_t* packed_gu, const float* gamma_gu,
+                                  const float* rms_w_down, const uint8_t* packed_down,
+                                  const float* gamma_down, int64_t B, int64_t M, int64_t D,
+                                  int64_t F, float eps, float* y, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    return glu_impl(x, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down, B, M, D,
+                    F, eps, y, ws, ws_bytes, stream);
 }
 
 int bitlinear_quantize(const uint16_t* x, const float* rms_weight, int64_t M, int64_t K, float eps,

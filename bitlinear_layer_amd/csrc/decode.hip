@@ -247,14 +247,16 @@ struct Plan {
 
 // Lanes per row (LPR) and 16-byte steps per lane (S) for a row of `nchunks`
 // 64-weight chunks: fewest idle lanes with at most 4 / MAXM code chunks
-// held per lane (64 registers), preferring wider rows on ties.
+// held per lane (64 registers) -- 7 for one token, whose codes leave room --
+// preferring wider rows on ties.
+constexpr int kMaxStepsOneToken = 7;
 Plan plan_for(int nchunks, int maxm) {
     Plan best;
     double best_idle = 2.0;
     for (int l2 = 6; l2 >= 3; --l2) {
         const int lpr = 1 << l2;
         const int s = (nchunks + lpr - 1) / lpr;
-        if (s < 1 || s * maxm > 4) continue;
+        if (s < 1 || s * maxm > (maxm == 1 ? kMaxStepsOneToken : 4)) continue;
         const double idle = 1.0 - (double)nchunks / (double)(s * lpr);
         if (idle < best_idle - 1e-9) {
             best_idle = idle;
@@ -267,7 +269,7 @@ Plan plan_for(int nchunks, int maxm) {
 
 template <int MAXM, int S, int LPR, Epilogue EP>
 hipError_t launch_msl(const DecodeArgs& a, hipStream_t stream) {
-    constexpr int kBufRows = 8 / (EP == Epilogue::kGluBf16 ? 2 : 1) / (S >= 3 ? 4 : S);
+    constexpr int kBufRows = 8 / (EP == Epilogue::kGluBf16 ? 2 : 1) / (S >= 5 ? 8 : (S >= 3 ? 4 : S));
     constexpr int U = kBufRows < 1 ? 1 : (kBufRows > LPR ? LPR : kBufRows);
     constexpr int RW = kWave / LPR;
     const int64_t total_rows = (int64_t)a.N * a.batch;
@@ -293,12 +295,16 @@ hipError_t launch_ms(const DecodeArgs& a, const Plan& p, hipStream_t stream) {
 
 template <int MAXM, Epilogue EP>
 hipError_t launch_m(const DecodeArgs& a, const Plan& p, hipStream_t stream) {
-    // plan_for keeps S * MAXM <= 4, so only those instantiations exist.
+    // plan_for keeps S * MAXM <= 4 (S <= 7 for one token), so only those
+    // instantiations exist.
     switch (p.S) {
         case 1: return launch_ms<MAXM, 1, EP>(a, p, stream);
         case 2: if constexpr (MAXM <= 2) return launch_ms<MAXM, 2, EP>(a, p, stream); break;
         case 3: if constexpr (MAXM == 1) return launch_ms<MAXM, 3, EP>(a, p, stream); break;
         case 4: if constexpr (MAXM == 1) return launch_ms<MAXM, 4, EP>(a, p, stream); break;
+        case 5: if constexpr (MAXM == 1) return launch_ms<MAXM, 5, EP>(a, p, stream); break;
+        case 6: if constexpr (MAXM == 1) return launch_ms<MAXM, 6, EP>(a, p, stream); break;
+        case 7: if constexpr (MAXM == 1) return launch_ms<MAXM, 7, EP>(a, p, stream); break;
     }
     return hipErrorInvalidValue;
 }

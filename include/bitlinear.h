@@ -151,12 +151,14 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
  * ------------------------------------------------------------------------- */
 
 /* Workspace bytes for bitlinear_forward / bitlinear_forward_ex (int8 codes
- * [M][K rounded up to 64], per-token scale and code sum). */
+ * [M][K], per-token scale and code sum, each part 256-byte aligned). */
 size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* x: bf16 [M][K]; rms_weight: fp32 [K]; packed: [N][K/4] (from
  * bitlinear_pack_weights); gamma: device fp32 scalar; y: fp32 [M][N].
- * Dispatches on M between the GEMV and the MFMA kernels. */
+ * Dispatches on M: one fused kernel (quantisation and product) for M <= 4
+ * and K % 64 == 0; otherwise the quantisation pass, then the ternary product
+ * on the int8 matrix cores (or the GEMV for M <= 4). */
 int bitlinear_forward(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
                       const float* gamma, int64_t M, int64_t N, int64_t K, float eps,
                       float* y, void* ws, size_t ws_bytes, void* stream);
@@ -214,6 +216,20 @@ int bitlinear_glu_forward(const uint16_t* x, const float* rms_w_gu,
                           const float* rms_w_down, const uint8_t* packed_down,
                           const float* gamma_down, int64_t M, int64_t D, int64_t F,
                           float eps, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* B independent mixers of the same shape, e.g. one decode step through a
+ * stack of layers: x bf16 [B][M][D], rms_w_gu fp32 [B][D], packed_gu
+ * [B][2F][D/4], gamma_gu fp32 [B], rms_w_down fp32 [B][F], packed_down
+ * [B][D][F/4], gamma_down fp32 [B] (device), y fp32 [B][M][D].  Mixer b
+ * computes exactly what bitlinear_glu_forward computes on its slices.
+ * B*M <= BITLINEAR_MAX_DIM. */
+size_t bitlinear_glu_batched_workspace_bytes(int64_t B, int64_t M, int64_t D, int64_t F);
+int bitlinear_glu_forward_batched(const uint16_t* x, const float* rms_w_gu,
+                                  const uint8_t* packed_gu, const float* gamma_gu,
+                                  const float* rms_w_down, const uint8_t* packed_down,
+                                  const float* gamma_down, int64_t B, int64_t M, int64_t D,
+                                  int64_t F, float eps, float* y, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* First half of the mixer alone: h = bf16(SiLU(gate) * up), h bf16 [M][F].
  * Workspace: bitlinear_forward_workspace_bytes(M, 2F, D). */

@@ -45,6 +45,8 @@ def test_sizes():
     assert fw >= 8192 * 2048 + 2 * 8192 * 4 and fw % 256 == 0
     assert bl.bitlinear_forward_workspace_bytes(0, 16, 16) == 0
     assert bl.bitlinear_forward_batched_workspace_bytes(4, 1, 64, 64) == bl.bitlinear_forward_workspace_bytes(4, 64, 64)
+    assert bl.bitlinear_glu_batched_workspace_bytes(4, 1, 64, 96) == bl.bitlinear_glu_workspace_bytes(4, 64, 96)
+    assert bl.bitlinear_glu_batched_workspace_bytes(0, 1, 64, 96) == 0
     gw = bl.bitlinear_glu_workspace_bytes(4096, 2048, 5632)
     assert gw >= 4096 * 2048 + 4096 * 5632 * 2 + 4096 * 5632
     assert bl.bitlinear_pack_workspace_bytes(2048, 2048) % 256 == 0
@@ -91,6 +93,10 @@ def test_other_entry_points_reject():
     assert L.bitlinear_unpack_weights(None, 4, 64, FAKE, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_forward_batched(FAKE, FAKE, FAKE, FAKE, 0, 1, 64, 64, 1e-6, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_forward_batched(FAKE, FAKE, FAKE, FAKE, 70000, 1, 64, 64, 1e-6, FAKE, FAKE, 1 << 30, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_glu_forward_batched(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 64, 64, 1e-6, FAKE,
+                                           FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_glu_forward_batched(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 64, 72, 1e-6, FAKE,
+                                           FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_glu_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 40, 1e-6, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_glu_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 1e-6, FAKE, FAKE, 16, None) == bl.BITLINEAR_ERR_WORKSPACE
     assert L.bitlinear_glu_hidden(FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 1e-6, FAKE, FAKE, 16, None, 0) == bl.BITLINEAR_ERR_WORKSPACE

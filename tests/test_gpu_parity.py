@@ -191,6 +191,9 @@ FORWARD = [
     (4, 65, 4096, "student_t3", 0.0, 1.0),
     (1, 1000, 16384, "normal", 0.0, 1.0),    # decode, four steps per lane
     (3, 77, 192, "normal", 0.0, 1.0),
+    (1, 70, 2176, "normal", 0.0, 1.0),       # decode, 8 lanes a row, five steps per lane
+    (1, 33, 3008, "student_t3", 0.0, 1.0),   # decode, six steps per lane
+    (1, 65, 3520, "normal", 0.005, 50.0),    # decode, seven steps per lane
 ]
 
 
@@ -319,7 +322,7 @@ def assert_h_parity(h_gpu, h_ref):
     assert diff.max(initial=0) <= 1 and np.mean(diff != 0) <= 1e-3, (diff.max(), np.mean(diff != 0))
 
 
-@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (5, 256, 320), (130, 256, 320), (3, 2048, 5632),
+@pytest.mark.parametrize("M,D,F", [(1, 256, 320), (5, 256, 320), (130, 256, 320), (1, 3008, 64), (3, 2048, 5632),
                                    (2, 208, 96)])
 def test_glu_hidden(M, D, F):
     x, g_gu, W_gu, g_dn, W_dn = _glu_inputs(M, D, F, seed=M)
@@ -341,6 +344,28 @@ def test_glu_forward(M, D, F):
     y = bl.bitlinear_glu_forward(gu.to_dev_bf16(x), gu.to_dev(g_gu), pgu, ggu, gu.to_dev(g_dn), pdn,
                                  gdn).cpu().numpy()
     gu.assert_y_parity(y, ref["y"])
+
+
+# Batched mixers: one-token problems take the fused kernel for both
+# projections, five tokens the quantisation pass and few-token product, 130
+# the tiled MFMA product; each mixer has its own weights and RMSNorm gains.
+@pytest.mark.parametrize("M", [1, 5, 130])
+def test_glu_forward_batched(M):
+    B, D, F = 3, 256, 320
+    _say("glu forward batched", B, M, D, F)
+    cases = [_glu_inputs(M, D, F, seed=M + 200 + b) for b in range(B)]
+    packs = [(gu.pack_on_gpu(c[2]), gu.pack_on_gpu(c[4])) for c in cases]
+    x = torch.stack([gu.to_dev_bf16(c[0]) for c in cases])
+    g_gu = torch.stack([gu.to_dev(c[1]) for c in cases])
+    g_dn = torch.stack([gu.to_dev(c[3]) for c in cases])
+    pgu = torch.stack([p[0][0] for p in packs])
+    ggu = torch.cat([p[0][1] for p in packs])
+    pdn = torch.stack([p[1][0] for p in packs])
+    gdn = torch.cat([p[1][1] for p in packs])
+    y = bl.bitlinear_glu_forward_batched(x, g_gu, pgu, ggu, g_dn, pdn, gdn).cpu().numpy()
+    for b, c in enumerate(cases):
+        ref = gu.orc().glu(*c)
+        gu.assert_y_parity(y[b], ref["y"])
 
 
 # --------------------------------------------------------------------------
