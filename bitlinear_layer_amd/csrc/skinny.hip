@@ -26,6 +26,8 @@
 //     epilogue subtracts sum_k q (the weights are stored as w + 1) and
 //     rescales ([datacamp, "Các thành phần lõi: MLGRU và GLU"]: scaled
 //     ternary accumulation).
+#include <algorithm>
+
 #include "epilogue.h"
 
 namespace bl {
@@ -142,6 +144,129 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(ProductArgs a) {
     }
 }
 
+// Same product for K <= 2048 (K % 512 == 0) with the weights read in runs of
+// 128 contiguous bytes: a load instruction covers 8 rows x 128 bytes (lane l:
+// row l / 8, bytes 16 * (l % 8) of a 512-wide k pair), which streams like
+// the one-token kernel's long runs.  The wave writes each 16-row group into
+// its own LDS buffer (row pitch K/4 + 16, so that writes and the quarter
+// reads below are bank-conflict free) and reads it back in the MFMA layout;
+// the buffer is private to the wave, so no barrier is needed.  The codes of
+// the tokens for all of K stay in registers (NCH 256-wide chunks, at most
+// 128 VGPRs), read once per block.  Blocks take runs of rows as in the
+// kernel above, and each wave keeps the next group's loads in flight while
+// it multiplies the current one.
+template <int NCH, Epilogue EP>
+__global__ __launch_bounds__(kSkinnyThreads) void skinny_runs_kernel(ProductArgs a, int rows_per_block) {
+    extern __shared__ int8_t wbuf[];  // per wave: [16][K/4 + 16] packed bytes
+    constexpr int kRowBytes = NCH * 64;
+    constexpr int kPitch = kRowBytes + 16;
+    constexpr int kPairs = NCH / 2;       // 128-byte runs per row
+    constexpr int kLoads = 2 * kPairs;    // 16-byte loads per lane per group
+    const int M = a.M, N = a.N;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r = lane & 15, g = lane >> 4;
+    int8_t* buf = wbuf + wave * 16 * kPitch;
+    const int row0 = blockIdx.x * rows_per_block;
+    const int rows = min(rows_per_block, N - row0);
+    const int ngroups = (rows + 15) / 16;
+    const uint8_t* P = a.packed + (int64_t)b * N * kRowBytes;
+
+    // load k of a group: half h = k / kPairs (rows 8h..8h+7), pair p = k % kPairs
+    auto load_group = [&](int grp, uint4 (&dst)[kLoads]) {
+        const int rbase = row0 + 16 * (wave + kSkinnyWaves * grp);
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            const int h = k / kPairs, p = k % kPairs;
+            const int row = min(rbase + 8 * h + (lane >> 3), N - 1);
+            dst[k] = load_stream16(reinterpret_cast<const uint32_t*>(P + (int64_t)row * kRowBytes + 128 * p +
+                                                                     16 * (lane & 7)));
+        }
+    };
+    const int my_groups = ngroups > wave ? (ngroups - wave + kSkinnyWaves - 1) / kSkinnyWaves : 0;
+    uint4 wv[kLoads];
+    if (my_groups > 0) load_group(0, wv);
+
+    // Codes of token r for this lane's k-slices: chunk c, step t -> bytes
+    // 256c + 64g + 16t (zeros for rows past M).
+    i32x4 aq[NCH][4];
+    const int8_t* Q = a.q + ((int64_t)b * M + min(r, M - 1)) * (NCH * 256) + 64 * g;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            aq[c][t] = i32x4{0, 0, 0, 0};
+            if (r < M) aq[c][t] = *reinterpret_cast<const i32x4*>(Q + 256 * c + 16 * t);
+        }
+    const float gamma = EP == Epilogue::kI32 ? 0.0f : a.gamma[b];
+    int32_t sq[4];
+    float cs[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t tk = (int64_t)b * M + min(4 * g + v, M - 1);
+        sq[v] = a.sumq[tk];
+        cs[v] = EP == Epilogue::kI32 ? 0.0f : gamma / a.s[tk];
+    }
+
+    for (int grp = 0; grp < my_groups; ++grp) {
+        // stage this group in the wave's buffer, then request the next one
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            const int h = k / kPairs, p = k % kPairs;
+            *reinterpret_cast<uint4*>(buf + (8 * h + (lane >> 3)) * kPitch + 128 * p + 16 * (lane & 7)) = wv[k];
+        }
+        if (grp + 1 < my_groups) load_group(grp + 1, wv);
+        i32x4 acc = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const uint4 wq = *reinterpret_cast<const uint4*>(buf + r * kPitch + 64 * c + 16 * g);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t w = t == 0 ? wq.x : (t == 1 ? wq.y : (t == 2 ? wq.z : wq.w));
+                int32_t c0, c1, c2, c3;
+                decode_codes(w, c0, c1, c2, c3);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[c][t], i32x4{c0, c1, c2, c3}, acc, 0, 0, 0);
+            }
+        }
+        const int n = row0 + 16 * (wave + kSkinnyWaves * grp) + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * g + v;
+            if (m < M && n < N) {
+                const int64_t tk = (int64_t)b * M + m;
+                const int32_t val = acc[v] - sq[v];
+                if (EP == Epilogue::kI32)
+                    static_cast<int32_t*>(a.out)[tk * N + n] = val;
+                else
+                    static_cast<float*>(a.out)[tk * N + n] = rescale(val, cs[v]);
+            }
+        }
+    }
+}
+
+template <int NCH, Epilogue EP>
+hipError_t launch_runs(const ProductArgs& a, hipStream_t stream) {
+    const int64_t total = (int64_t)a.N * a.batch;
+    int64_t rpb = round_up((total + 2047) / 2048, (int64_t)64);  // about 2048 blocks
+    rpb = std::min<int64_t>(rpb, round_up((int64_t)a.N, (int64_t)64));
+    const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
+    const size_t lds = (size_t)kSkinnyWaves * 16 * (NCH * 64 + 16);
+    skinny_runs_kernel<NCH, EP><<<grid, kSkinnyThreads, lds, stream>>>(a, (int)rpb);
+    return hipGetLastError();
+}
+
+template <Epilogue EP>
+hipError_t launch_runs_ep(const ProductArgs& a, hipStream_t stream) {
+    switch (a.K / kChunkK) {
+        case 2: return launch_runs<2, EP>(a, stream);
+        case 4: return launch_runs<4, EP>(a, stream);
+        case 6: return launch_runs<6, EP>(a, stream);
+        case 8: return launch_runs<8, EP>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool skinny_supported(int M, int K, Epilogue ep) {
@@ -151,6 +276,9 @@ bool skinny_supported(int M, int K, Epilogue ep) {
 
 hipError_t launch_skinny(const ProductArgs& a, Epilogue ep, hipStream_t stream) {
     if (!skinny_supported(a.M, a.K, ep)) return hipErrorInvalidValue;
+    if (a.K % 512 == 0 && a.K <= 2048)
+        return ep == Epilogue::kI32 ? launch_runs_ep<Epilogue::kI32>(a, stream)
+                                    : launch_runs_ep<Epilogue::kF32>(a, stream);
     constexpr int kRowsPerBlock = kSkinnyWaves * 16 * kSkinnyU;
     const dim3 grid((unsigned)((a.N + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)a.batch);
     const size_t lds = (size_t)a.M * (a.K + 16);

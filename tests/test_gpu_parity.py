@@ -139,9 +139,11 @@ MATMUL = [(M, N, K) for M in (1, 3, 8, 130, 257) for (N, K) in ((7, 16), (129, 4
 # with ragged M and N, and even and odd numbers of LDS stages (one, three,
 # four, five, eight).
 MATMUL += [(300, 520, 1024), (129, 256, 128), (2900, 3000, 512), (300, 520, 384), (2900, 3000, 640)]
-# M <= 16 with K % 256 == 0 runs the few-token MFMA kernel (weights streamed
-# into registers): one to three load groups, ragged N, 1 to 16 tokens.
-MATMUL += [(1, 300, 512), (5, 130, 768), (8, 2100, 2048), (16, 77, 1280), (12, 64, 3328)]
+# M <= 16 with K % 256 == 0 runs the few-token MFMA kernels: K % 512 == 0 up
+# to 2048 the run-loading one (two to eight chunks), else the quarter-loading
+# one (one to three load groups); ragged N, 1 to 16 tokens.
+MATMUL += [(1, 300, 512), (5, 130, 768), (8, 2100, 2048), (16, 77, 1280), (12, 64, 3328),
+           (3, 90, 1024), (16, 200, 1536)]
 
 
 @pytest.mark.parametrize("M,N,K", MATMUL)
