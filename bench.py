@@ -238,6 +238,23 @@ def bench_glu_layers(torch, bl, wl, L, M, D, F, steps, warmup, stream):
                 gbps=nbytes / (wall * 1e-3) / 1e9, kernel_gbps=nbytes / (ev * 1e-3) / 1e9)
 
 
+def bench_hbm_copy(torch, nbytes, steps):
+    """Context: a plain device-to-device copy of buffers far larger than the
+    256 MB Infinity Cache (read + write bytes per second)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    del a, b
+    torch.cuda.empty_cache()
+    return dict(bytes_each_way=nbytes, gbps_read_plus_write=2.0 * nbytes * steps / el / 1e9)
+
+
 # --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
@@ -330,6 +347,7 @@ def main():
         secondary["glu_m1_layers"] = bench_glu_layers(torch, bl, wl, 128, 1, 2048, 5632, max(5, args.steps // 2),
                                                       args.warmup, stream)
         secondary["glu_m1"] = bench_glu(torch, bl, wl, 1, 2048, 5632, 100, args.warmup, stream)
+        secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
 
