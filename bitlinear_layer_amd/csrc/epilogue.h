@@ -16,9 +16,22 @@ namespace bl {
 
 __device__ __forceinline__ float rescale(int32_t acc, float c) { return (float)acc * c; }
 
+// SiLU(v) = v * sigmoid(v), with e = e^-|v| = 2^(-|v| log2 e) in (0, 1] from
+// v_exp_f32 and the reciprocal of 1 + e (in (1, 2]) from v_rcp_f32:
+// sigmoid(|v|) = 1 / (1 + e) and sigmoid(-|v|) = e / (1 + e). Nothing can
+// overflow; for large negative v the result tends to -0 as e underflows.
+// Each step is within about 1 fp32 ulp, apart from the rounding of
+// -|v| log2 e, whose effect on the result is near a * 2^-24 relative for
+// v = -a < 0 — far below the half-ulp of the bf16 the product is stored in.
+__device__ __forceinline__ float silu_f32(float v) {
+    constexpr float kNegLog2e = -1.44269502e+00f;   // -log2(e) rounded to fp32
+    const float e = __builtin_amdgcn_exp2f(fabsf(v) * kNegLog2e);
+    const float q = __builtin_amdgcn_rcpf(1.0f + e);
+    return v * (v < 0.0f ? e * q : q);
+}
+
 __device__ __forceinline__ uint16_t glu_bf16(float zg, float zu) {
-    const float silu = zg / (1.0f + expf(-zg));
-    return (uint16_t)f32_to_bf16_bits(silu * zu);
+    return (uint16_t)f32_to_bf16_bits(silu_f32(zg) * zu);
 }
 
 }  // namespace bl
