@@ -19,6 +19,8 @@
 //      rescales ([datacamp, "Các thành phần lõi: MLGRU và GLU"]: scaled
 //      ternary accumulation) or, for the GLU, forms bf16(SiLU(gate) * up).
 // B independent problems of the same shape run in one launch (grid.y).
+#include <atomic>
+
 #include "epilogue.h"
 
 namespace bl {
@@ -26,6 +28,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCus = 256;
 
 // Block-cooperative RMSNorm + absmax int8 of one token row into LDS; the
 // same arithmetic and reduction order as the block-per-row quant_kernel, so
@@ -267,15 +271,37 @@ Plan plan_for(int nchunks, int maxm) {
     return best;
 }
 
+// Rows per block (a multiple of `gran`) for `batch` problems of N rows.
+// Blocks stay inside one problem, so the rows of a problem are split into
+// equal blocks; the split minimises the rows of the busiest CU when the
+// blocks are dealt out evenly over `ncu` compute units (plus one granule of
+// set-up per block). Unequal blocks -- a full block beside a sliver, or one
+// block more on a few CUs -- otherwise cost up to a quarter of the rate.
+int64_t decode_rows_per_block(int64_t N, int64_t batch, int64_t gran, int ncu) {
+    int64_t rpb = round_up(N, gran);
+    double best = -1.0;
+    for (int64_t nb = 1; nb <= N; ++nb) {
+        const int64_t r = round_up((N + nb - 1) / nb, gran);
+        const int64_t blocks = (N + r - 1) / r * batch;
+        const double cost = (double)((blocks + ncu - 1) / ncu) * (double)(r + gran);
+        if (best < 0.0 || cost < best) {
+            best = cost;
+            rpb = r;
+        }
+        if (r == gran) break;
+    }
+    return rpb;
+}
+
 template <int MAXM, int S, int LPR, Epilogue EP>
 hipError_t launch_msl(const DecodeArgs& a, hipStream_t stream) {
-    constexpr int kBufRows = 8 / (EP == Epilogue::kGluBf16 ? 2 : 1) / (S >= 5 ? 8 : (S >= 3 ? 4 : S));
+    // Loads in flight per lane, double buffered: U row sets of S 16-byte
+    // chunks, U = 8 / S for S <= 2 and 2 beyond (half that for the GLU,
+    // which loads a gate and an up row per set).
+    constexpr int kBufRows = 8 / (EP == Epilogue::kGluBf16 ? 2 : 1) / (S >= 3 ? 4 : S);
     constexpr int U = kBufRows < 1 ? 1 : (kBufRows > LPR ? LPR : kBufRows);
     constexpr int RW = kWave / LPR;
-    const int64_t total_rows = (int64_t)a.N * a.batch;
-    int64_t rpb = (total_rows + 1023) / 1024;  // about 1024 blocks
-    rpb = round_up(rpb < 1 ? 1 : rpb, (int64_t)kWaves * RW);
-    if (rpb > a.N) rpb = round_up(a.N, (int64_t)kWaves * RW);
+    const int64_t rpb = decode_rows_per_block(a.N, a.batch, (int64_t)kWaves * RW, device_cu_count());
     const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
     const size_t lds = (size_t)a.M * a.K;
     decode_kernel<MAXM, S, U, LPR, EP><<<grid, kThreads, lds, stream>>>(a, (int)rpb);
@@ -319,6 +345,19 @@ hipError_t launch_ep(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int device_cu_count() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCus;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = kDefaultCus;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 bool decode_supported(int M, int K) {
     if (M < 1 || M > kDecodeMaxM || K % 64 != 0) return false;

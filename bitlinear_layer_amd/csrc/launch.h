@@ -9,6 +9,9 @@ namespace bl {
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// Compute units of the current device, queried once per device.
+int device_cu_count();
+
 // Per-token activation stage produced by the quantisation kernel:
 // q int8 [rows][K] (row stride K), s fp32 [rows], sumq int32 [rows] = sum_k q.
 struct ActStage {
