@@ -19,6 +19,7 @@
 //      rescales ([datacamp, "Các thành phần lõi: MLGRU và GLU"]: scaled
 //      ternary accumulation) or, for the GLU, forms bf16(SiLU(gate) * up).
 // B independent problems of the same shape run in one launch (grid.y).
+#include <algorithm>
 #include <atomic>
 
 #include "epilogue.h"
@@ -271,28 +272,6 @@ Plan plan_for(int nchunks, int maxm) {
     return best;
 }
 
-// Rows per block (a multiple of `gran`) for `batch` problems of N rows.
-// Blocks stay inside one problem, so the rows of a problem are split into
-// equal blocks; the split minimises the rows of the busiest CU when the
-// blocks are dealt out evenly over `ncu` compute units (plus one granule of
-// set-up per block). Unequal blocks -- a full block beside a sliver, or one
-// block more on a few CUs -- otherwise cost up to a quarter of the rate.
-int64_t decode_rows_per_block(int64_t N, int64_t batch, int64_t gran, int ncu) {
-    int64_t rpb = round_up(N, gran);
-    double best = -1.0;
-    for (int64_t nb = 1; nb <= N; ++nb) {
-        const int64_t r = round_up((N + nb - 1) / nb, gran);
-        const int64_t blocks = (N + r - 1) / r * batch;
-        const double cost = (double)((blocks + ncu - 1) / ncu) * (double)(r + gran);
-        if (best < 0.0 || cost < best) {
-            best = cost;
-            rpb = r;
-        }
-        if (r == gran) break;
-    }
-    return rpb;
-}
-
 template <int MAXM, int S, int LPR, Epilogue EP>
 hipError_t launch_msl(const DecodeArgs& a, hipStream_t stream) {
     // Loads in flight per lane, double buffered: U row sets of S 16-byte
@@ -301,7 +280,7 @@ hipError_t launch_msl(const DecodeArgs& a, hipStream_t stream) {
     constexpr int kBufRows = 8 / (EP == Epilogue::kGluBf16 ? 2 : 1) / (S >= 3 ? 4 : S);
     constexpr int U = kBufRows < 1 ? 1 : (kBufRows > LPR ? LPR : kBufRows);
     constexpr int RW = kWave / LPR;
-    const int64_t rpb = decode_rows_per_block(a.N, a.batch, (int64_t)kWaves * RW, device_cu_count());
+    const int64_t rpb = balanced_rows_per_block(a.N, a.batch, (int64_t)kWaves * RW);
     const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
     const size_t lds = (size_t)a.M * a.K;
     decode_kernel<MAXM, S, U, LPR, EP><<<grid, kThreads, lds, stream>>>(a, (int)rpb);
@@ -357,6 +336,37 @@ int device_cu_count() {
         cache[dev].store(n, std::memory_order_relaxed);
     }
     return n;
+}
+
+// Rows per block (a multiple of `gran`) for `batch` problems of N rows.
+// Blocks stay inside one problem, so the rows of a problem are split into nb
+// equal blocks. The split minimises the rows of the busiest CU when the
+// nb * batch blocks are dealt out evenly over the device's CUs, counting one
+// granule of set-up per block. Unequal blocks (a full block beside a sliver,
+// or one block more on a few CUs) otherwise cost up to a quarter of the rate.
+// Candidates are nb = 1..16 and the nb that make nb * batch a small multiple
+// of the CU count, so the search stays cheap beside a launch.
+int64_t balanced_rows_per_block(int64_t N, int64_t batch, int64_t gran) {
+    const int64_t ncu = device_cu_count();
+    const int64_t nb_max = (N + gran - 1) / gran;
+    int64_t best_r = round_up(N, gran);
+    double best = -1.0;
+    auto consider = [&](int64_t nb) {
+        nb = std::min(std::max<int64_t>(nb, 1), nb_max);
+        const int64_t r = round_up((N + nb - 1) / nb, gran);
+        const int64_t blocks = (N + r - 1) / r * batch;
+        const double cost = (double)((blocks + ncu - 1) / ncu) * (double)(r + gran);
+        if (best < 0.0 || cost < best || (cost == best && r > best_r)) {
+            best = cost;
+            best_r = r;
+        }
+    };
+    for (int64_t nb = 1; nb <= 16; ++nb) consider(nb);
+    for (int64_t k = 1; k <= 32; ++k) {
+        consider(k * ncu / batch);
+        consider((k * ncu + batch - 1) / batch);
+    }
+    return best_r;
 }
 
 bool decode_supported(int M, int K) {

@@ -11,6 +11,10 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // Compute units of the current device, queried once per device.
 int device_cu_count();
+// Rows per block, a multiple of `gran`, for `batch` problems of N rows each,
+// when a block stays inside one problem: equal blocks, split so that the
+// busiest compute unit has the fewest rows.
+int64_t balanced_rows_per_block(int64_t N, int64_t batch, int64_t gran);
 
 // Per-token activation stage produced by the quantisation kernel:
 // q int8 [rows][K] (row stride K), s fp32 [rows], sumq int32 [rows] = sum_k q.

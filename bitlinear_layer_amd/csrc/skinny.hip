@@ -40,6 +40,12 @@ constexpr int kSkinnyWaves = kSkinnyThreads / kWave;
 constexpr int kSkinnyU = 2;      // 16-row weight groups per wave
 constexpr int kChunkK = 256;     // k per chunk (64 packed bytes of a row)
 constexpr int kGroup = 4;        // chunks per load group (double-buffered)
+#ifndef SPLIT_D2
+#define SPLIT_D2 8
+#endif
+#ifndef SPLIT_D4
+#define SPLIT_D4 4
+#endif
 
 template <Epilogue EP>
 __global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(ProductArgs a) {
@@ -245,11 +251,157 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_runs_kernel(ProductArgs
     }
 }
 
+// Same product for K = 1024 * NCHW (K = 2048 or 4096): the four waves of a
+// block split K into quarters and walk the same 16-row groups together, so
+// a wave holds the codes of a quarter of K only (NCHW 256-wide chunks) and
+// keeps D groups of weights in flight instead of one. Each load instruction
+// still covers 8 rows x 128 contiguous bytes (lane l: row l / 8, bytes
+// 16 * (l % 8) of a 128-byte run of the wave's quarter); the group is
+// reshaped through the wave's own LDS buffer as above. Each wave leaves its
+// partial sums of a group in LDS; after every batch of four groups one
+// barrier, then wave w adds the four quarters of group w of the batch
+// (integer sums, exact in any order) and stores them. The output writes,
+// though only M * 4 bytes per 512-byte weight row, cost the stream more than
+// their size: reads mixed with writes on HBM run slower than reads alone,
+// whatever the store width or order. Partial sums are double-buffered by batch, so the barrier of batch
+// i + 1 also orders the reads of batch i before their overwrite.
+constexpr int kSplitBatch = 4;  // 16-row groups per reduction: one per wave
+
+template <int NCHW, int D, Epilogue EP>
+__global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArgs a, int rows_per_block) {
+    static_assert(kSkinnyWaves == 4 && kSplitBatch == kSkinnyWaves, "four K quarters, one group per wave to add");
+    static_assert((D > kSplitBatch ? D : kSplitBatch) % D == 0 && (D > kSplitBatch ? D : kSplitBatch) % kSplitBatch == 0,
+                  "whole rings and batches per loop trip");
+    constexpr int kSliceBytes = NCHW * 64;  // packed bytes of a row in one quarter of K
+    constexpr int kPitch = kSliceBytes + 16;
+    constexpr int kRuns = kSliceBytes / 128;
+    constexpr int kLoads = 2 * kRuns;       // 16-byte loads per lane per group
+    extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+    const int M = a.M, N = a.N;
+    const int64_t row_bytes = 4 * kSliceBytes;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r = lane & 15, g = lane >> 4;
+    int8_t* buf = smem + wave * 16 * kPitch;
+    // partial sums: [2 batches][kSplitBatch groups][4 quarters][64 lanes] x int4
+    i32x4* part = reinterpret_cast<i32x4*>(smem + kSkinnyWaves * 16 * kPitch);
+    const int row0 = blockIdx.x * rows_per_block;
+    const int rows = min(rows_per_block, N - row0);
+    const int last_row = row0 + rows - 1;
+    const int ngroups = (rows + 15) / 16;
+    constexpr int kRing = D > kSplitBatch ? D : kSplitBatch;  // groups per loop trip (static ring slots)
+    const int niters = (ngroups + kRing - 1) / kRing;
+    const uint8_t* P = a.packed + (int64_t)b * N * row_bytes + wave * kSliceBytes;
+
+    // Loads of group grp; rows past the block's last are clamped to it (read
+    // again from cache, never stored).
+    auto load_group = [&](int grp, uint4 (&dst)[kLoads]) {
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            const int h = k / kRuns, p = k % kRuns;
+            const int row = min(row0 + 16 * grp + 8 * h + (lane >> 3), last_row);
+            dst[k] = load_stream16(reinterpret_cast<const uint32_t*>(P + (int64_t)row * row_bytes + 128 * p +
+                                                                     16 * (lane & 7)));
+        }
+    };
+    uint4 wv[D][kLoads];
+#pragma unroll
+    for (int s = 0; s < D; ++s) load_group(s, wv[s]);
+
+    // Codes of token r for this lane's k-slices of the wave's quarter:
+    // chunk c, step t -> k = K/4 * wave + 256c + 64g + 16t (zeros past M).
+    i32x4 aq[NCHW][4];
+    const int8_t* Q = a.q + ((int64_t)b * M + min(r, M - 1)) * (4 * NCHW * 256) + wave * (NCHW * 256) + 64 * g;
+#pragma unroll
+    for (int c = 0; c < NCHW; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            aq[c][t] = i32x4{0, 0, 0, 0};
+            if (r < M) aq[c][t] = *reinterpret_cast<const i32x4*>(Q + 256 * c + 16 * t);
+        }
+    const float gamma = EP == Epilogue::kI32 ? 0.0f : a.gamma[b];
+    int32_t sq[4];
+    float cs[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t tk = (int64_t)b * M + min(4 * g + v, M - 1);
+        sq[v] = a.sumq[tk];
+        cs[v] = EP == Epilogue::kI32 ? 0.0f : gamma / a.s[tk];
+    }
+
+    for (int it = 0; it < niters; ++it) {
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+            const int s = j % D;
+            const int grp = it * kRing + j;
+            i32x4* pb = part + ((grp / kSplitBatch) & 1) * (kSplitBatch * kSkinnyWaves * kWave);
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k) {
+                const int h = k / kRuns, p = k % kRuns;
+                *reinterpret_cast<uint4*>(buf + (8 * h + (lane >> 3)) * kPitch + 128 * p + 16 * (lane & 7)) = wv[s][k];
+            }
+            load_group(grp + D, wv[s]);
+            i32x4 acc = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NCHW; ++c) {
+                const uint4 wq = *reinterpret_cast<const uint4*>(buf + r * kPitch + 64 * c + 16 * g);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t w = t == 0 ? wq.x : (t == 1 ? wq.y : (t == 2 ? wq.z : wq.w));
+                    int32_t c0, c1, c2, c3;
+                    decode_codes(w, c0, c1, c2, c3);
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[c][t], i32x4{c0, c1, c2, c3}, acc, 0, 0, 0);
+                }
+            }
+            pb[((j % kSplitBatch) * kSkinnyWaves + wave) * kWave + lane] = acc;
+            if ((j + 1) % kSplitBatch != 0) continue;
+            // the batch is complete: wave w adds the quarters of its group w
+            __syncthreads();
+            const int rgrp = grp + 1 - kSplitBatch + wave;
+            if (rgrp < ngroups) {
+                const i32x4* src = pb + wave * kSkinnyWaves * kWave + lane;
+                const i32x4 sum = src[0] + src[kWave] + src[2 * kWave] + src[3 * kWave];
+                const int n = row0 + 16 * rgrp + r;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 4 * g + v;
+                    if (m < M && n <= last_row) {
+                        const int64_t tk = (int64_t)b * M + m;
+                        const int32_t val = sum[v] - sq[v];
+                        if (EP == Epilogue::kI32)
+                            static_cast<int32_t*>(a.out)[tk * N + n] = val;
+                        else
+                            static_cast<float*>(a.out)[tk * N + n] = rescale(val, cs[v]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int NCHW, int D, Epilogue EP>
+hipError_t launch_split(const ProductArgs& a, hipStream_t stream) {
+    const int64_t rpb = balanced_rows_per_block(a.N, a.batch, (int64_t)16 * kSplitBatch);
+    const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
+    const size_t lds = (size_t)kSkinnyWaves * 16 * (NCHW * 64 + 16) +
+                       (size_t)2 * kSplitBatch * kSkinnyWaves * kWave * sizeof(i32x4);
+    skinny_split_kernel<NCHW, D, EP><<<grid, kSkinnyThreads, lds, stream>>>(a, (int)rpb);
+    return hipGetLastError();
+}
+
+template <Epilogue EP>
+hipError_t launch_split_ep(const ProductArgs& a, hipStream_t stream) {
+    switch (a.K) {
+        case 2048: return launch_split<2, SPLIT_D2, EP>(a, stream);
+        case 4096: return launch_split<4, SPLIT_D4, EP>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int NCH, Epilogue EP>
 hipError_t launch_runs(const ProductArgs& a, hipStream_t stream) {
-    const int64_t total = (int64_t)a.N * a.batch;
-    int64_t rpb = round_up((total + 2047) / 2048, (int64_t)64);  // about 2048 blocks
-    rpb = std::min<int64_t>(rpb, round_up((int64_t)a.N, (int64_t)64));
+    const int64_t rpb = balanced_rows_per_block(a.N, a.batch, (int64_t)kSkinnyWaves * 16);
     const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
     const size_t lds = (size_t)kSkinnyWaves * 16 * (NCH * 64 + 16);
     skinny_runs_kernel<NCH, EP><<<grid, kSkinnyThreads, lds, stream>>>(a, (int)rpb);
@@ -276,6 +428,11 @@ bool skinny_supported(int M, int K, Epilogue ep) {
 
 hipError_t launch_skinny(const ProductArgs& a, Epilogue ep, hipStream_t stream) {
     if (!skinny_supported(a.M, a.K, ep)) return hipErrorInvalidValue;
+#ifndef NO_SPLIT
+    if (a.K == 2048 || a.K == 4096)
+        return ep == Epilogue::kI32 ? launch_split_ep<Epilogue::kI32>(a, stream)
+                                    : launch_split_ep<Epilogue::kF32>(a, stream);
+#endif
     if (a.K % 512 == 0 && a.K <= 2048)
         return ep == Epilogue::kI32 ? launch_runs_ep<Epilogue::kI32>(a, stream)
                                     : launch_runs_ep<Epilogue::kF32>(a, stream);

@@ -144,6 +144,10 @@ MATMUL += [(300, 520, 1024), (129, 256, 128), (2900, 3000, 512), (300, 520, 384)
 # one (one to three load groups); ragged N, 1 to 16 tokens.
 MATMUL += [(1, 300, 512), (5, 130, 768), (8, 2100, 2048), (16, 77, 1280), (12, 64, 3328),
            (3, 90, 1024), (16, 200, 1536)]
+# K = 2048 and 4096 with 5..16 tokens run the K-split few-token kernel: one
+# batch of four groups, a ragged group past several batches, a problem
+# smaller than one group, all 16 token rows.
+MATMUL += [(5, 64, 2048), (16, 1000, 2048), (7, 17, 4096), (13, 333, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", MATMUL)
@@ -233,6 +237,27 @@ def test_forward_batched(K):
         xs = [wl.x_normal(M, K, seed=10 + b) for b in range(B)]
         Ws = [wl.w_normal(N, K, seed=20 + b) for b in range(B)]
         gs = [wl.rms_weight(K, "random", seed=30 + b) for b in range(B)]
+        packs = [gu.pack_on_gpu(W) for W in Ws]
+        x = torch.stack([gu.to_dev_bf16(a) for a in xs])
+        g = torch.stack([gu.to_dev(a) for a in gs])
+        packed = torch.stack([p for p, _ in packs])
+        gamma = torch.cat([gm for _, gm in packs])
+        y = bl.bitlinear_forward_batched(x, g, packed, gamma).cpu().numpy()
+        for b in range(B):
+            ref = gu.orc().bitlinear(xs[b], gs[b], Ws[b])
+            gu.assert_y_parity(y[b], ref["y"])
+
+
+# Batched few-token problems on the K-split kernel (K = 2048, 4096): each
+# slice has its own codes, scales and weights; N = 200 leaves a ragged group.
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_forward_batched_few_tokens(K):
+    B, N = 3, 200
+    for M in (5, 8, 16):
+        _say("batched few tokens", B, M, N, K)
+        xs = [wl.x_normal(M, K, seed=70 + b) for b in range(B)]
+        Ws = [wl.w_normal(N, K, seed=80 + b) for b in range(B)]
+        gs = [wl.rms_weight(K, "random", seed=90 + b) for b in range(B)]
         packs = [gu.pack_on_gpu(W) for W in Ws]
         x = torch.stack([gu.to_dev_bf16(a) for a in xs])
         g = torch.stack([gu.to_dev(a) for a in gs])
