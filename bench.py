@@ -72,20 +72,36 @@ class EventTimer:
         return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
 
 
-def timed_loop(torch, fn, steps, warmup, stream):
+def timed_loop(torch, fn, steps, warmup, stream, per_call_events=False):
     """Run fn warmup times, then exactly `steps` times between device
-    synchronisations.  Returns (wall ms per step, event ms per call)."""
+    synchronisations.  Returns (wall ms per step, event ms per call).
+
+    By default one HIP event pair on the library's stream brackets the timed
+    steps (nothing is inserted between calls, so the wall time is not
+    stretched); the event time per call is that span / steps.  With
+    per_call_events each call gets its own pair (for single-call latency)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    timer = EventTimer(torch, stream)
+    if per_call_events:
+        timer = EventTimer(torch, stream)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            with timer:
+                fn()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return wall, timer.mean_ms()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record(stream)
     for _ in range(steps):
-        with timer:
-            fn()
+        fn()
+    end.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return wall, timer.mean_ms()
+    return wall, start.elapsed_time(end) / steps
 
 
 # sources the headline kernel is compiled from (its counters go stale when any changes)
@@ -169,7 +185,7 @@ def bench_single_layer(torch, bl, wl, M, N, K, steps, stream):
     def step():
         bl.bitlinear_forward(x, g, packed[0], gamma[:1], y=y, ws=ws)
 
-    wall, ev = timed_loop(torch, step, steps, 20, stream)
+    wall, ev = timed_loop(torch, step, steps, 20, stream, per_call_events=True)
     nbytes = layer_bytes(M, N, K)
     return dict(M=M, N=N, K=K, us_per_call_wall=wall * 1e3, us_per_call_event=ev * 1e3,
                 implied_gbps=nbytes / (ev * 1e-3) / 1e9)
