@@ -254,6 +254,28 @@ def bench_glu_layers(torch, bl, wl, L, M, D, F, steps, warmup, stream):
                 gbps=nbytes / (wall * 1e-3) / 1e9, kernel_gbps=nbytes / (ev * 1e-3) / 1e9)
 
 
+def bench_repack(torch, bl, wl, L, N, K, steps, warmup, stream):
+    """Re-ternarisation of L fp32 master matrices [N, K] in one batched pack
+    call (a training step's re-pack of a layer stack).  The algorithmic bytes
+    are one read of W and the packed write; the two-pass kernels read W
+    twice (gamma, then the codes)."""
+    W = torch.empty((L, N, K), dtype=torch.float32, device=DEV)
+    for layer in range(L):
+        W[layer] = wl.w_normal_device(N, K, seed=0, layer=layer, device=DEV)
+    packed = torch.empty((L, N, K // 4), dtype=torch.uint8, device=DEV)
+    gamma = torch.empty(L, dtype=torch.float32, device=DEV)
+    ws = torch.empty(bl.bitlinear_pack_batched_workspace_bytes(L, N, K), dtype=torch.uint8, device=DEV)
+    wall, ev = timed_loop(torch, lambda: bl.bitlinear_pack_weights_batched(W, packed=packed, gamma=gamma, ws=ws),
+                          steps, warmup, stream)
+    alg = L * (4 * N * K + N * K // 4 + 4)
+    two_pass = L * (8 * N * K + N * K // 4 + 4)
+    del W, packed, gamma, ws
+    torch.cuda.empty_cache()
+    return dict(layers=L, N=N, K=K, wall_ms=wall, event_ms=ev, algorithmic_bytes=alg,
+                gbps_algorithmic=alg / (ev * 1e-3) / 1e9, gbps_two_pass=two_pass / (ev * 1e-3) / 1e9,
+                weights_per_s=L * N * K / (ev * 1e-3))
+
+
 def bench_hbm_copy(torch, nbytes, steps):
     """Context: a plain device-to-device copy of buffers far larger than the
     256 MB Infinity Cache (read + write bytes per second)."""
@@ -363,6 +385,8 @@ def main():
         secondary["glu_m1_layers"] = bench_glu_layers(torch, bl, wl, 128, 1, 2048, 5632, max(5, args.steps // 2),
                                                       args.warmup, stream)
         secondary["glu_m1"] = bench_glu(torch, bl, wl, 1, 2048, 5632, 100, args.warmup, stream)
+        log("[bench] re-ternarisation of 64 x 2048 x 2048 fp32 master weights")
+        secondary["repack_64x2048x2048"] = bench_repack(torch, bl, wl, 64, 2048, 2048, 10, 2, stream)
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)

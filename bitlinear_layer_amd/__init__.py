@@ -46,6 +46,8 @@ _SIGNATURES = {
     "bitlinear_packed_bytes": (_S, [_I, _I]),
     "bitlinear_pack_workspace_bytes": (_S, [_I, _I]),
     "bitlinear_pack_weights": (_INT, [_P, _I, _I, _P, _P, _P, _S, _P]),
+    "bitlinear_pack_batched_workspace_bytes": (_S, [_I, _I, _I]),
+    "bitlinear_pack_weights_batched": (_INT, [_P, _I, _I, _I, _P, _P, _P, _S, _P]),
     "bitlinear_unpack_weights": (_INT, [_P, _I, _I, _P, _P]),
     "bitlinear_forward_workspace_bytes": (_S, [_I, _I, _I]),
     "bitlinear_forward": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P]),
@@ -167,6 +169,25 @@ def bitlinear_pack_weights(W, packed=None, gamma=None, ws=None, stream=None):
     ws, nbytes = _workspace(bitlinear_pack_workspace_bytes(N, K), ws, W.device)
     _check(lib().bitlinear_pack_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(ws), nbytes,
                                         _stream(stream)))
+    return packed, gamma
+
+
+def bitlinear_pack_batched_workspace_bytes(B, N, K):
+    return lib().bitlinear_pack_batched_workspace_bytes(B, N, K)
+
+
+def bitlinear_pack_weights_batched(W, packed=None, gamma=None, ws=None, stream=None):
+    """fp32 W [B, N, K] -> (packed uint8 [B, N, K/4], gamma fp32 [B]), one
+    gamma per matrix."""
+    _dev(W, "W", (torch.float32,), 3)
+    B, N, K = W.shape
+    if packed is None:
+        packed = torch.empty((B, N, K // 4), dtype=torch.uint8, device=W.device)
+    if gamma is None:
+        gamma = torch.empty(B, dtype=torch.float32, device=W.device)
+    ws, nbytes = _workspace(bitlinear_pack_batched_workspace_bytes(B, N, K), ws, W.device)
+    _check(lib().bitlinear_pack_weights_batched(_ptr(W), B, N, K, _ptr(packed), _ptr(gamma), _ptr(ws), nbytes,
+                                                _stream(stream)))
     return packed, gamma
 
 

@@ -229,6 +229,25 @@ int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
                        BITLINEAR_KERNEL_AUTO, st);
 }
 
+// B matrices of one shape, back to back (B = 1 for bitlinear_pack_weights).
+int pack_impl(const float* W, int64_t B, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+              void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_k(K, "K"));
+    CHECK(N >= 1 && N <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "N must be in [1, MAX_DIM]");
+    CHECK(B >= 1 && B <= kMaxBatch, BITLINEAR_ERR_INVALID_ARG, "batch must be in [1, %lld]",
+          (long long)kMaxBatch);
+    CHECK(N * K <= kMaxElems && B * N * K / 16 <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    CHECK_PTR(W);
+    CHECK_PTR(packed);
+    CHECK_SCALAR(gamma);
+    TRY(check_ws(ws, ws_bytes, bitlinear_pack_batched_workspace_bytes(B, N, K)));
+    hipStream_t st = as_stream(stream);
+    const int64_t total = N * K;
+    TRY(hip_status(bl::launch_gamma(W, total, B, static_cast<double*>(ws), gamma, st), "gamma launch"));
+    return hip_status(bl::launch_ternarize_pack(W, total, B, gamma, reinterpret_cast<uint32_t*>(packed), st),
+                      "pack launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,24 +267,22 @@ size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
 }
 
 size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
-    if (N <= 0 || K <= 0) return 0;
-    return (size_t)bl::round_up((int64_t)bl::gamma_partials(N * K) * 8, 256);
+    return bitlinear_pack_batched_workspace_bytes(1, N, K);
+}
+
+size_t bitlinear_pack_batched_workspace_bytes(int64_t B, int64_t N, int64_t K) {
+    if (B <= 0 || N <= 0 || K <= 0 || B > kMaxBatch || N > kMaxElems / K) return 0;
+    return (size_t)bl::round_up(B * (int64_t)bl::gamma_partials(N * K) * 8, 256);
 }
 
 int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
                            void* ws, size_t ws_bytes, void* stream) {
-    TRY(check_k(K, "K"));
-    CHECK(N >= 1 && N <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "N must be in [1, MAX_DIM]");
-    CHECK(N * K <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    CHECK_PTR(W);
-    CHECK_PTR(packed);
-    CHECK_SCALAR(gamma);
-    TRY(check_ws(ws, ws_bytes, bitlinear_pack_workspace_bytes(N, K)));
-    hipStream_t st = as_stream(stream);
-    const int64_t total = N * K;
-    TRY(hip_status(bl::launch_gamma(W, total, static_cast<double*>(ws), gamma, st), "gamma launch"));
-    return hip_status(bl::launch_ternarize_pack(W, total, gamma, reinterpret_cast<uint32_t*>(packed), st),
-                      "pack launch");
+    return pack_impl(W, 1, N, K, packed, gamma, ws, ws_bytes, stream);
+}
+
+int bitlinear_pack_weights_batched(const float* W, int64_t B, int64_t N, int64_t K, uint8_t* packed,
+                                   float* gamma, void* ws, size_t ws_bytes, void* stream) {
+    return pack_impl(W, B, N, K, packed, gamma, ws, ws_bytes, stream);
 }
 
 int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, void* stream) {

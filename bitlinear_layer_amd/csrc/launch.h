@@ -31,9 +31,11 @@ ActStage act_stage_carve(void* base, int64_t rows, int64_t K);
 // --- weights ---------------------------------------------------------------
 // Number of fp64 partial sums the gamma reduction uses for `total` weights.
 int gamma_partials(int64_t total);
-hipError_t launch_gamma(const float* W, int64_t total, double* partial, float* gamma,
+// `batch` matrices of `total` elements each, back to back; partial holds
+// gamma_partials(total) sums per matrix and gamma one value per matrix.
+hipError_t launch_gamma(const float* W, int64_t total, int64_t batch, double* partial, float* gamma,
                         hipStream_t stream);
-hipError_t launch_ternarize_pack(const float* W, int64_t total, const float* gamma,
+hipError_t launch_ternarize_pack(const float* W, int64_t total, int64_t batch, const float* gamma,
                                  uint32_t* packed, hipStream_t stream);
 hipError_t launch_unpack(const uint32_t* packed, int64_t nwords, int8_t* w, hipStream_t stream);
 

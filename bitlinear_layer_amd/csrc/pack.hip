@@ -5,9 +5,10 @@
 // nearest of -1, 0, +1.  Readings: one gamma per matrix, sum of |W| in fp64,
 // w = clip(rint(W / (gamma + 1e-5)), -1, 1) with an IEEE fp32 division.
 //
-// Kernels (all HBM-bound; W is read twice, packed written once):
+// Kernels (all HBM-bound; W is read twice, packed written once), each over a
+// batch of matrices of one shape along grid y (one gamma per matrix):
 //   gamma_partial  -- fixed-range fp64 partial sums of |W| (one per block)
-//   gamma_final    -- one block sums the partials in a fixed order
+//   gamma_final    -- one block per matrix sums its partials in a fixed order
 //   ternarize_pack -- one thread per 16-weight group -> one packed word
 #include "device_common.h"
 #include "launch.h"
@@ -22,29 +23,46 @@ __global__ __launch_bounds__(kPackThreads) void gamma_partial_kernel(const float
                                                                      int64_t total, int64_t chunk,
                                                                      double* __restrict__ partial) {
     __shared__ double scratch[kPackThreads / kWave];
+    W += (int64_t)blockIdx.y * total;  // matrix blockIdx.y of the batch
     const int64_t begin = (int64_t)blockIdx.x * chunk;
     const int64_t end = begin + chunk < total ? begin + chunk : total;
+    constexpr int64_t kStep = 4 * kPackThreads;
     double acc = 0.0;
-    // chunk and total are multiples of 4, so float4 loads stay aligned.
-    for (int64_t i = begin + 4 * (int64_t)threadIdx.x; i < end; i += 4 * kPackThreads) {
-        const float4 v = *reinterpret_cast<const float4*>(W + i);
+    // chunk and total are multiples of 4, so float4 loads stay aligned.  Four
+    // loads are issued before their sums; the order of the sums is that of
+    // the one-load loop.
+    auto add = [&](const float4 v) {
         acc += (double)fabsf(v.x);
         acc += (double)fabsf(v.y);
         acc += (double)fabsf(v.z);
         acc += (double)fabsf(v.w);
+    };
+    int64_t i = begin + 4 * (int64_t)threadIdx.x;
+    for (; i + 3 * kStep < end; i += 4 * kStep) {
+        const float4 v0 = *reinterpret_cast<const float4*>(W + i);
+        const float4 v1 = *reinterpret_cast<const float4*>(W + i + kStep);
+        const float4 v2 = *reinterpret_cast<const float4*>(W + i + 2 * kStep);
+        const float4 v3 = *reinterpret_cast<const float4*>(W + i + 3 * kStep);
+        add(v0);
+        add(v1);
+        add(v2);
+        add(v3);
     }
+    for (; i < end; i += kStep) add(*reinterpret_cast<const float4*>(W + i));
     acc = block_sum(acc, scratch);
-    if (threadIdx.x == 0) partial[blockIdx.x] = acc;
+    if (threadIdx.x == 0) partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = acc;
 }
 
+// One block per matrix of the batch.
 __global__ __launch_bounds__(kPackThreads) void gamma_final_kernel(const double* __restrict__ partial,
                                                                    int nparts, int64_t total,
                                                                    float* __restrict__ gamma) {
     __shared__ double scratch[kPackThreads / kWave];
+    partial += (int64_t)blockIdx.x * nparts;
     double acc = 0.0;
     for (int i = threadIdx.x; i < nparts; i += kPackThreads) acc += partial[i];
     acc = block_sum(acc, scratch);
-    if (threadIdx.x == 0) *gamma = (float)(acc / (double)total);
+    if (threadIdx.x == 0) gamma[blockIdx.x] = (float)(acc / (double)total);
 }
 
 __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(const float* __restrict__ W,
@@ -53,8 +71,9 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(const floa
                                                                       uint32_t* __restrict__ packed) {
     const int64_t i = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
     if (i >= nwords) return;
-    const float d = *gamma + 1e-5f;
-    const float4* src = reinterpret_cast<const float4*>(W + 16 * i);
+    const int64_t b = blockIdx.y;  // matrix of the batch
+    const float d = gamma[b] + 1e-5f;
+    const float4* src = reinterpret_cast<const float4*>(W + 16 * (b * nwords + i));
     float v[16];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -72,7 +91,7 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(const floa
         const uint32_t code = (uint32_t)((int)t + 1);
         word |= code << (8 * (j & 3) + 2 * (j >> 2));
     }
-    packed[i] = word;
+    packed[b * nwords + i] = word;
 }
 
 __global__ __launch_bounds__(kPackThreads) void unpack_kernel(const uint32_t* __restrict__ packed,
@@ -100,20 +119,21 @@ int gamma_partials(int64_t total) {
     return n > kMaxPartials ? kMaxPartials : (int)n;
 }
 
-hipError_t launch_gamma(const float* W, int64_t total, double* partial, float* gamma,
+hipError_t launch_gamma(const float* W, int64_t total, int64_t batch, double* partial, float* gamma,
                         hipStream_t stream) {
     const int nparts = gamma_partials(total);
     const int64_t chunk = round_up((total + nparts - 1) / nparts, 4);
-    gamma_partial_kernel<<<nparts, kPackThreads, 0, stream>>>(W, total, chunk, partial);
-    gamma_final_kernel<<<1, kPackThreads, 0, stream>>>(partial, nparts, total, gamma);
+    gamma_partial_kernel<<<dim3((unsigned)nparts, (unsigned)batch), kPackThreads, 0, stream>>>(W, total, chunk,
+                                                                                              partial);
+    gamma_final_kernel<<<(unsigned)batch, kPackThreads, 0, stream>>>(partial, nparts, total, gamma);
     return hipGetLastError();
 }
 
-hipError_t launch_ternarize_pack(const float* W, int64_t total, const float* gamma,
+hipError_t launch_ternarize_pack(const float* W, int64_t total, int64_t batch, const float* gamma,
                                  uint32_t* packed, hipStream_t stream) {
     const int64_t nwords = total / 16;
-    ternarize_pack_kernel<<<grid_for(nwords, kPackThreads), kPackThreads, 0, stream>>>(W, nwords,
-                                                                                       gamma, packed);
+    ternarize_pack_kernel<<<dim3(grid_for(nwords, kPackThreads), (unsigned)batch), kPackThreads, 0, stream>>>(
+        W, nwords, gamma, packed);
     return hipGetLastError();
 }
 

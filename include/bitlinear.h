@@ -136,6 +136,21 @@ size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
 int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed,
                            float* gamma, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for bitlinear_pack_weights_batched (0 for an invalid
+ * shape). */
+size_t bitlinear_pack_batched_workspace_bytes(int64_t B, int64_t N, int64_t K);
+
+/* B matrices of one shape ternarised in one call -- the re-ternarisation of
+ * a stack of layers from their fp32 master weights, e.g. once per training
+ * step ([ld246, "训练与优化：新的策略"]: the ternary weights are recomputed
+ * from full-precision ones, gradients passing straight through).
+ * W: device fp32 [B][N][K]; packed: device [B][N][K/4]; gamma: device fp32
+ * [B], one mean |W| per matrix.  Each matrix gets exactly the bytes and gamma
+ * that bitlinear_pack_weights gives it.  1 <= B <= 65535. */
+int bitlinear_pack_weights_batched(const float* W, int64_t B, int64_t N, int64_t K,
+                                   uint8_t* packed, float* gamma, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* Test/inspection: decode packed [N][K/4] into int8 [N][K] as code - 1.
  * Valid codes give -1, 0, +1; the unused code 3 decodes to 2, outside the
  * ternary set, so that a corrupted matrix is visible to a check of w. */

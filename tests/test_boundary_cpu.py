@@ -50,6 +50,10 @@ def test_sizes():
     gw = bl.bitlinear_glu_workspace_bytes(4096, 2048, 5632)
     assert gw >= 4096 * 2048 + 4096 * 5632 * 2 + 4096 * 5632
     assert bl.bitlinear_pack_workspace_bytes(2048, 2048) % 256 == 0
+    assert bl.bitlinear_pack_batched_workspace_bytes(1, 2048, 2048) == bl.bitlinear_pack_workspace_bytes(2048, 2048)
+    assert bl.bitlinear_pack_batched_workspace_bytes(64, 2048, 2048) >= 64 * 8 * 2
+    assert bl.bitlinear_pack_batched_workspace_bytes(0, 2048, 2048) == 0
+    assert bl.bitlinear_pack_batched_workspace_bytes(70000, 64, 64) == 0
 
 
 def _fwd(x=FAKE, g=FAKE, p=FAKE, gamma=FAKE, M=4, N=64, K=64, eps=1e-6, y=FAKE, ws=FAKE,
@@ -91,6 +95,11 @@ def test_other_entry_points_reject():
     assert L.bitlinear_pack_weights(FAKE, 0, 16, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_pack_weights(FAKE, 64, 64, FAKE, FAKE, None, 0, None) == bl.BITLINEAR_ERR_WORKSPACE
     assert L.bitlinear_unpack_weights(None, 4, 64, FAKE, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_pack_weights_batched(FAKE, 0, 64, 64, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_pack_weights_batched(FAKE, 70000, 64, 64, FAKE, FAKE, FAKE, 1 << 30, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_pack_weights_batched(FAKE, 2, 64, 12, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_pack_weights_batched(FAKE, 2, 64, 64, FAKE, None, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_pack_weights_batched(FAKE, 2, 64, 64, FAKE, FAKE, FAKE, 8, None) == bl.BITLINEAR_ERR_WORKSPACE
     assert L.bitlinear_forward_batched(FAKE, FAKE, FAKE, FAKE, 0, 1, 64, 64, 1e-6, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_forward_batched(FAKE, FAKE, FAKE, FAKE, 70000, 1, 64, 64, 1e-6, FAKE, FAKE, 1 << 30, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_glu_forward_batched(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 64, 64, 1e-6, FAKE,

@@ -76,6 +76,23 @@ def test_pack_edge_cases():
     assert np.array_equal(bl.bitlinear_unpack_weights(packed, 64).cpu().numpy(), w_ref)
 
 
+@pytest.mark.parametrize("N,K", [(300, 2064), (2048, 2048)])
+def test_pack_batched(N, K):
+    """Three matrices in one call (normal, all zero, normal x 40): each gets
+    the oracle's bytes and gamma, the same as from a call of its own."""
+    _say("pack batched", N, K)
+    Ws = [wl.w_normal(N, K, seed=N + 1), np.zeros((N, K), np.float32),
+          (wl.w_normal(N, K, seed=N + 2) * np.float32(40.0)).astype(np.float32)]
+    packed, gamma = bl.bitlinear_pack_weights_batched(torch.stack([gu.to_dev(W) for W in Ws]))
+    packed, gamma = packed.cpu().numpy(), gamma.cpu().numpy()
+    for b, W in enumerate(Ws):
+        g_ref = gu.orc().gamma(W)
+        assert gamma[b] == g_ref, b
+        assert np.array_equal(packed[b], gu.orc().pack(gu.orc().ternarize(W, g_ref))), b
+        p1, g1 = gu.pack_on_gpu(W)
+        assert g1.item() == gamma[b] and np.array_equal(p1.cpu().numpy(), packed[b]), b
+
+
 def test_unpack_marks_unused_code():
     p = torch.full((2, 4), 0xFF, dtype=torch.uint8, device=gu.DEV)
     w = bl.bitlinear_unpack_weights(p, 16).cpu().numpy()
