@@ -40,12 +40,6 @@ constexpr int kSkinnyWaves = kSkinnyThreads / kWave;
 constexpr int kSkinnyU = 2;      // 16-row weight groups per wave
 constexpr int kChunkK = 256;     // k per chunk (64 packed bytes of a row)
 constexpr int kGroup = 4;        // chunks per load group (double-buffered)
-#ifndef SPLIT_D2
-#define SPLIT_D2 8
-#endif
-#ifndef SPLIT_D4
-#define SPLIT_D4 4
-#endif
 
 template <Epilogue EP>
 __global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(ProductArgs a) {
@@ -393,8 +387,10 @@ hipError_t launch_split(const ProductArgs& a, hipStream_t stream) {
 template <Epilogue EP>
 hipError_t launch_split_ep(const ProductArgs& a, hipStream_t stream) {
     switch (a.K) {
-        case 2048: return launch_split<2, SPLIT_D2, EP>(a, stream);
-        case 4096: return launch_split<4, SPLIT_D4, EP>(a, stream);
+        // weight groups in flight per wave: 8 at K = 2048 (3 waves per SIMD
+        // fit), 4 at K = 4096 (the codes of a quarter take twice the registers)
+        case 2048: return launch_split<2, 8, EP>(a, stream);
+        case 4096: return launch_split<4, 4, EP>(a, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -428,11 +424,9 @@ bool skinny_supported(int M, int K, Epilogue ep) {
 
 hipError_t launch_skinny(const ProductArgs& a, Epilogue ep, hipStream_t stream) {
     if (!skinny_supported(a.M, a.K, ep)) return hipErrorInvalidValue;
-#ifndef NO_SPLIT
     if (a.K == 2048 || a.K == 4096)
         return ep == Epilogue::kI32 ? launch_split_ep<Epilogue::kI32>(a, stream)
                                     : launch_split_ep<Epilogue::kF32>(a, stream);
-#endif
     if (a.K % 512 == 0 && a.K <= 2048)
         return ep == Epilogue::kI32 ? launch_runs_ep<Epilogue::kI32>(a, stream)
                                     : launch_runs_ep<Epilogue::kF32>(a, stream);
