@@ -94,19 +94,26 @@ bool use_gemv(int64_t M, int kernel) {
     return M <= 4;
 }
 
-// Whether a full forward runs as the single fused decode kernel.
-bool use_decode(int64_t M, int64_t K, int kernel) {
-    if (kernel == BITLINEAR_KERNEL_DECODE) return true;
-    return kernel == BITLINEAR_KERNEL_AUTO && bl::decode_supported((int)M, (int)K);
+// Whether a whole layer can run as one fused kernel (quantisation inside):
+// the one-token decode kernel for M <= 4 (either epilogue), the K-split
+// few-token kernel for 5..16 tokens (fp32 epilogue only).
+bool fused_supported(int64_t M, int64_t K, bool glu) {
+    return bl::decode_supported((int)M, (int)K) || (!glu && bl::decode_few_supported((int)M, (int)K));
 }
 
-int check_kernel(int kernel, int64_t M, int64_t K, bool fused_allowed) {
+// Whether a full forward runs as a single fused kernel.
+bool use_decode(int64_t M, int64_t K, int kernel, bool glu) {
+    if (kernel == BITLINEAR_KERNEL_DECODE) return true;
+    return kernel == BITLINEAR_KERNEL_AUTO && fused_supported(M, K, glu);
+}
+
+int check_kernel(int kernel, int64_t M, int64_t K, bool fused_allowed, bool glu = false) {
     CHECK(kernel == BITLINEAR_KERNEL_AUTO || kernel == BITLINEAR_KERNEL_GEMV ||
               kernel == BITLINEAR_KERNEL_MFMA || (fused_allowed && kernel == BITLINEAR_KERNEL_DECODE),
           BITLINEAR_ERR_INVALID_ARG, "kernel choice %d not available here", kernel);
     CHECK(kernel != BITLINEAR_KERNEL_GEMV || M <= bl::kGemvMaxM, BITLINEAR_ERR_INVALID_ARG,
           "the GEMV kernel takes M <= %d (got %lld)", bl::kGemvMaxM, (long long)M);
-    CHECK(kernel != BITLINEAR_KERNEL_DECODE || M == 0 || bl::decode_supported((int)M, (int)K),
+    CHECK(kernel != BITLINEAR_KERNEL_DECODE || M == 0 || fused_supported(M, K, glu),
           BITLINEAR_ERR_INVALID_ARG, "the fused decode kernel does not take M=%lld, K=%lld",
           (long long)M, (long long)K);
     return BITLINEAR_OK;
@@ -127,7 +134,9 @@ int run_decode(const uint16_t* x, const float* g, int64_t g_stride, const uint8_
     d.batch = (int)B;
     d.eps = eps;
     d.out = out;
-    return hip_status(bl::launch_decode(d, ep, stream), "fused decode launch");
+    // fused_supported() has admitted (M, K, ep) for one of the two kernels
+    if (bl::decode_supported(d.M, d.K)) return hip_status(bl::launch_decode(d, ep, stream), "fused decode launch");
+    return hip_status(bl::launch_decode_few(d, stream), "fused few-token launch");
 }
 
 // Ternary product + epilogue for `batch` problems whose activation stage is
@@ -163,7 +172,7 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
     CHECK(B * M <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "B*M exceeds BITLINEAR_MAX_DIM");
     CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems,
           BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    TRY(check_kernel(kernel, M, K, true));
+    TRY(check_kernel(kernel, M, K, true, false));
     if (M == 0 || N == 0) return BITLINEAR_OK;
     CHECK_PTR(x);
     CHECK_PTR(rms_weight);
@@ -173,7 +182,7 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
     const size_t need = bl::act_stage_bytes(B * M, K);
     TRY(check_ws(ws, ws_bytes, need));
     hipStream_t st = as_stream(stream);
-    if (use_decode(M, K, kernel))
+    if (use_decode(M, K, kernel, false))
         return run_decode(x, rms_weight, B > 1 ? K : 0, packed, gamma, B, M, N, K, eps, y,
                           bl::Epilogue::kF32, st);
     bl::ActStage act = bl::act_stage_carve(ws, B * M, K);
@@ -213,7 +222,7 @@ int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
     uint16_t* h = reinterpret_cast<uint16_t*>(base);
     base += bl::round_up(rows * F * 2, 256);
     bl::ActStage act_h = bl::act_stage_carve(base, rows, F);
-    if (use_decode(M, D, BITLINEAR_KERNEL_AUTO)) {
+    if (use_decode(M, D, BITLINEAR_KERNEL_AUTO, true)) {
         TRY(run_decode(x, rms_w_gu, B > 1 ? D : 0, packed_gu, gamma_gu, B, M, F, D, eps, h,
                        bl::Epilogue::kGluBf16, st));
     } else {
@@ -221,7 +230,7 @@ int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
         TRY(run_product(act_x, packed_gu, gamma_gu, M, F, D, B, h, bl::Epilogue::kGluBf16,
                         BITLINEAR_KERNEL_AUTO, st));
     }
-    if (use_decode(M, F, BITLINEAR_KERNEL_AUTO))
+    if (use_decode(M, F, BITLINEAR_KERNEL_AUTO, false))
         return run_decode(h, rms_w_down, B > 1 ? F : 0, packed_down, gamma_down, B, M, D, F, eps, y,
                           bl::Epilogue::kF32, st);
     TRY(hip_status(bl::launch_quant(h, rms_w_down, rows, M, (int)F, eps, act_h, st), "quantise launch"));
@@ -256,7 +265,7 @@ int bitlinear_abi_version(void) { return 1; }
 
 int bitlinear_decode_supported(int64_t M, int64_t K) {
     if (M < 1 || K < 1 || M > BITLINEAR_MAX_DIM || K > BITLINEAR_MAX_DIM) return 0;
-    return bl::decode_supported((int)M, (int)K) ? 1 : 0;
+    return fused_supported(M, K, false) ? 1 : 0;
 }
 
 const char* bitlinear_last_error(void) { return g_last_error.c_str(); }
@@ -380,7 +389,7 @@ int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu, const uint8_t
     TRY(check_eps(eps));
     CHECK(M * D <= kMaxElems && 2 * F * D <= kMaxElems && M * F <= kMaxElems,
           BITLINEAR_ERR_INVALID_ARG, "matrix too large");
-    TRY(check_kernel(kernel, M, D, true));
+    TRY(check_kernel(kernel, M, D, true, true));
     if (M == 0) return BITLINEAR_OK;
     CHECK_PTR(x);
     CHECK_PTR(rms_w_gu);
@@ -389,7 +398,7 @@ int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu, const uint8_t
     CHECK_PTR(h);
     TRY(check_ws(ws, ws_bytes, bl::act_stage_bytes(M, D)));
     hipStream_t st = as_stream(stream);
-    if (use_decode(M, D, kernel))
+    if (use_decode(M, D, kernel, true))
         return run_decode(x, rms_w_gu, 0, packed_gu, gamma_gu, 1, M, F, D, eps, h,
                           bl::Epilogue::kGluBf16, st);
     bl::ActStage act = bl::act_stage_carve(ws, M, D);

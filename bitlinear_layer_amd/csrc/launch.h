@@ -101,5 +101,9 @@ struct DecodeArgs {
 };
 bool decode_supported(int M, int K);
 hipError_t launch_decode(const DecodeArgs& a, Epilogue ep, hipStream_t stream);
+// The same for 5..16 tokens (fp32 epilogue): quantisation fused into the
+// K-split few-token product; K = 2048 or 4096 with M * K <= 32 KiB.
+bool decode_few_supported(int M, int K);
+hipError_t launch_decode_few(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace bl

@@ -29,6 +29,7 @@
 #include <algorithm>
 
 #include "epilogue.h"
+#include "quant_row.h"
 
 namespace bl {
 namespace {
@@ -260,9 +261,18 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_runs_kernel(ProductArgs
 // whatever the store width or order. Partial sums are double-buffered by batch, so the barrier of batch
 // i + 1 also orders the reads of batch i before their overwrite.
 constexpr int kSplitBatch = 4;  // 16-row groups per reduction: one per wave
+constexpr int kSplitPartBytes = 2 * kSplitBatch * kSkinnyWaves * kWave * 16;  // partial-sum region
 
-template <int NCHW, int D, Epilogue EP>
-__global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArgs a, int rows_per_block) {
+// FUSED: one launch for the whole layer, as the one-token decode kernel.
+// Each block first quantises its problem's M token rows itself (wave w
+// takes rows w, w + 4, ..., with the wave-per-row arithmetic of the
+// streaming quantiser), into the partial-sum region of LDS, free until the
+// first batch is added (M * K <= 32 KiB).  The weight loads of the first groups are issued before, so HBM
+// is busy from the start, and no codes are written to or read from HBM.
+// Otherwise the codes, scales and sums come from an activation stage.
+template <int NCHW, int D, Epilogue EP, bool FUSED>
+__global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArgs a, DecodeArgs d,
+                                                                      int rows_per_block) {
     static_assert(kSkinnyWaves == 4 && kSplitBatch == kSkinnyWaves, "four K quarters, one group per wave to add");
     static_assert((D > kSplitBatch ? D : kSplitBatch) % D == 0 && (D > kSplitBatch ? D : kSplitBatch) % kSplitBatch == 0,
                   "whole rings and batches per loop trip");
@@ -270,8 +280,12 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArg
     constexpr int kPitch = kSliceBytes + 16;
     constexpr int kRuns = kSliceBytes / 128;
     constexpr int kLoads = 2 * kRuns;       // 16-byte loads per lane per group
+    constexpr int K = 4 * NCHW * 256;
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-    const int M = a.M, N = a.N;
+    __shared__ float s_scale[kSkinnyMaxM];
+    __shared__ int32_t s_sumq[kSkinnyMaxM];
+    const int M = FUSED ? d.M : a.M, N = FUSED ? d.N : a.N;
+    const uint8_t* const packed = FUSED ? d.packed : a.packed;
     const int64_t row_bytes = 4 * kSliceBytes;
     const int b = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -286,7 +300,7 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArg
     const int ngroups = (rows + 15) / 16;
     constexpr int kRing = D > kSplitBatch ? D : kSplitBatch;  // groups per loop trip (static ring slots)
     const int niters = (ngroups + kRing - 1) / kRing;
-    const uint8_t* P = a.packed + (int64_t)b * N * row_bytes + wave * kSliceBytes;
+    const uint8_t* P = packed + (int64_t)b * N * row_bytes + wave * kSliceBytes;
 
     // Loads of group grp; rows past the block's last are clamped to it (read
     // again from cache, never stored).
@@ -303,10 +317,38 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArg
 #pragma unroll
     for (int s = 0; s < D; ++s) load_group(s, wv[s]);
 
+    // The problem's codes [M][K], scales and code sums.
+    const int8_t* qsrc;
+    const float* ssrc;
+    const int32_t* sqsrc;
+    if constexpr (FUSED) {
+        constexpr int CPL = K / 8 / kWave;  // 8-element chunks per lane
+        int8_t* qlds = reinterpret_cast<int8_t*>(part);
+        const uint16_t* X = d.x + (int64_t)b * M * K;
+        const float* G = d.g + (int64_t)b * d.g_stride;
+        auto g_chunk = [&](int c, float4& lo, float4& hi) {
+            const int idx = lane + c * kWave;
+            lo = *reinterpret_cast<const float4*>(G + 8 * idx);
+            hi = *reinterpret_cast<const float4*>(G + 8 * idx + 4);
+        };
+        for (int m = wave; m < M; m += kSkinnyWaves) {
+            uint4 xc[CPL];
+            load_x_row<CPL, true>(X + (int64_t)m * K, lane, K / 8, xc);
+            quant_row_regs<CPL, true>(xc, g_chunk, m, lane, K, d.eps, qlds, s_scale, s_sumq);
+        }
+        __syncthreads();
+        qsrc = qlds;
+        ssrc = s_scale;
+        sqsrc = s_sumq;
+    } else {
+        qsrc = a.q + (int64_t)b * M * K;
+        ssrc = a.s + (int64_t)b * M;
+        sqsrc = a.sumq + (int64_t)b * M;
+    }
     // Codes of token r for this lane's k-slices of the wave's quarter:
     // chunk c, step t -> k = K/4 * wave + 256c + 64g + 16t (zeros past M).
     i32x4 aq[NCHW][4];
-    const int8_t* Q = a.q + ((int64_t)b * M + min(r, M - 1)) * (4 * NCHW * 256) + wave * (NCHW * 256) + 64 * g;
+    const int8_t* Q = qsrc + (int64_t)min(r, M - 1) * K + wave * (NCHW * 256) + 64 * g;
 #pragma unroll
     for (int c = 0; c < NCHW; ++c)
 #pragma unroll
@@ -314,15 +356,17 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArg
             aq[c][t] = i32x4{0, 0, 0, 0};
             if (r < M) aq[c][t] = *reinterpret_cast<const i32x4*>(Q + 256 * c + 16 * t);
         }
-    const float gamma = EP == Epilogue::kI32 ? 0.0f : a.gamma[b];
+    const float gamma = EP == Epilogue::kI32 ? 0.0f : (FUSED ? d.gamma : a.gamma)[b];
     int32_t sq[4];
     float cs[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const int64_t tk = (int64_t)b * M + min(4 * g + v, M - 1);
-        sq[v] = a.sumq[tk];
-        cs[v] = EP == Epilogue::kI32 ? 0.0f : gamma / a.s[tk];
+        const int mm = min(4 * g + v, M - 1);
+        sq[v] = sqsrc[mm];
+        cs[v] = EP == Epilogue::kI32 ? 0.0f : gamma / ssrc[mm];
     }
+    // the codes in LDS are read before the partial sums overwrite them
+    if constexpr (FUSED) __syncthreads();
 
     for (int it = 0; it < niters; ++it) {
 #pragma unroll
@@ -363,10 +407,11 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArg
                     if (m < M && n <= last_row) {
                         const int64_t tk = (int64_t)b * M + m;
                         const int32_t val = sum[v] - sq[v];
+                        void* out = FUSED ? d.out : a.out;
                         if (EP == Epilogue::kI32)
-                            static_cast<int32_t*>(a.out)[tk * N + n] = val;
+                            static_cast<int32_t*>(out)[tk * N + n] = val;
                         else
-                            static_cast<float*>(a.out)[tk * N + n] = rescale(val, cs[v]);
+                            static_cast<float*>(out)[tk * N + n] = rescale(val, cs[v]);
                     }
                 }
             }
@@ -374,13 +419,13 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArg
     }
 }
 
-template <int NCHW, int D, Epilogue EP>
-hipError_t launch_split(const ProductArgs& a, hipStream_t stream) {
-    const int64_t rpb = balanced_rows_per_block(a.N, a.batch, (int64_t)16 * kSplitBatch);
-    const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
-    const size_t lds = (size_t)kSkinnyWaves * 16 * (NCHW * 64 + 16) +
-                       (size_t)2 * kSplitBatch * kSkinnyWaves * kWave * sizeof(i32x4);
-    skinny_split_kernel<NCHW, D, EP><<<grid, kSkinnyThreads, lds, stream>>>(a, (int)rpb);
+template <int NCHW, int D, Epilogue EP, bool FUSED>
+hipError_t launch_split(const ProductArgs& a, const DecodeArgs& d, hipStream_t stream) {
+    const int64_t N = FUSED ? d.N : a.N, batch = FUSED ? d.batch : a.batch;
+    const int64_t rpb = balanced_rows_per_block(N, batch, (int64_t)16 * kSplitBatch);
+    const dim3 grid((unsigned)((N + rpb - 1) / rpb), (unsigned)batch);
+    const size_t lds = (size_t)kSkinnyWaves * 16 * (NCHW * 64 + 16) + kSplitPartBytes;
+    skinny_split_kernel<NCHW, D, EP, FUSED><<<grid, kSkinnyThreads, lds, stream>>>(a, d, (int)rpb);
     return hipGetLastError();
 }
 
@@ -389,8 +434,8 @@ hipError_t launch_split_ep(const ProductArgs& a, hipStream_t stream) {
     switch (a.K) {
         // weight groups in flight per wave: 8 at K = 2048 (3 waves per SIMD
         // fit), 4 at K = 4096 (the codes of a quarter take twice the registers)
-        case 2048: return launch_split<2, 8, EP>(a, stream);
-        case 4096: return launch_split<4, 4, EP>(a, stream);
+        case 2048: return launch_split<2, 8, EP, false>(a, DecodeArgs{}, stream);
+        case 4096: return launch_split<4, 4, EP, false>(a, DecodeArgs{}, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -416,6 +461,16 @@ hipError_t launch_runs_ep(const ProductArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool decode_few_supported(int M, int K) {
+    return M >= 1 && M <= kSkinnyMaxM && (K == 2048 || K == 4096) && M * K <= kSplitPartBytes;
+}
+
+hipError_t launch_decode_few(const DecodeArgs& d, hipStream_t stream) {
+    if (!decode_few_supported(d.M, d.K)) return hipErrorInvalidValue;
+    return d.K == 2048 ? launch_split<2, 8, Epilogue::kF32, true>(ProductArgs{}, d, stream)
+                       : launch_split<4, 4, Epilogue::kF32, true>(ProductArgs{}, d, stream);
+}
 
 bool skinny_supported(int M, int K, Epilogue ep) {
     return M >= 1 && M <= kSkinnyMaxM && K % kChunkK == 0 && ep != Epilogue::kGluBf16 &&

@@ -103,12 +103,15 @@ typedef enum {
     BITLINEAR_KERNEL_AUTO = 0,   /* by token count M (what bitlinear_forward does)  */
     BITLINEAR_KERNEL_GEMV = 1,   /* quantise, then weight-streaming GEMV (M <= 8)   */
     BITLINEAR_KERNEL_MFMA = 2,   /* quantise, then int8 MFMA tiles                  */
-    BITLINEAR_KERNEL_DECODE = 3  /* one fused quantise+GEMV kernel; takes M <= 4
-                                    with K % 64 == 0 and K <= 16384 (M = 1),
-                                    8192 (M = 2) or 4096 (M = 3, 4)             */
+    BITLINEAR_KERNEL_DECODE = 3  /* one fused kernel, quantisation inside; takes
+                                    M <= 4 with K % 64 == 0 and K <= 16384
+                                    (M = 1), 8192 (M = 2) or 4096 (M = 3, 4);
+                                    and M <= 16 with K = 2048 or 4096 and
+                                    M * K <= 32768 (the fp32 forward only)   */
 } bitlinear_kernel;
 
-/* 1 when the fused decode kernel takes M tokens of length K, else 0. */
+/* 1 when a fused kernel (BITLINEAR_KERNEL_DECODE) takes M tokens of length K
+ * in bitlinear_forward, else 0. */
 int bitlinear_decode_supported(int64_t M, int64_t K);
 
 /* Version of this ABI (bumped on any incompatible change). */

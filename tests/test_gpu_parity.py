@@ -217,6 +217,9 @@ FORWARD = [
     (1, 70, 2176, "normal", 0.0, 1.0),       # decode, 8 lanes a row, five steps per lane
     (1, 33, 3008, "student_t3", 0.0, 1.0),   # decode, six steps per lane
     (1, 65, 3520, "normal", 0.005, 50.0),    # decode, seven steps per lane
+    (13, 333, 2048, "student_t3", 0.01, 20.0),  # fused few-token kernel, ragged groups
+    (6, 200, 4096, "normal", 0.0, 1.0),      # fused few-token kernel, K = 4096
+    (16, 130, 4096, "normal", 0.0, 1.0),     # 16 x 4096 codes exceed its LDS: two launches
 ]
 
 
