@@ -255,21 +255,23 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_runs_kernel(ProductArgs
 // reshaped through the wave's own LDS buffer as above. Each wave leaves its
 // partial sums of a group in LDS; after every batch of four groups one
 // barrier, then wave w adds the four quarters of group w of the batch
-// (integer sums, exact in any order) and stores them. The output writes,
-// though only M * 4 bytes per 512-byte weight row, cost the stream more than
-// their size: reads mixed with writes on HBM run slower than reads alone,
-// whatever the store width or order. Partial sums are double-buffered by batch, so the barrier of batch
-// i + 1 also orders the reads of batch i before their overwrite.
+// (integer sums, exact in any order) and stores them. Partial sums are
+// double-buffered by batch, so the barrier of batch i + 1 also orders the
+// reads of batch i before their overwrite. The output writes, though only
+// M * 4 bytes per 512-byte weight row, cost the stream more than their size:
+// reads mixed with writes run slower on HBM than reads alone, whatever the
+// store width or order.
 constexpr int kSplitBatch = 4;  // 16-row groups per reduction: one per wave
 constexpr int kSplitPartBytes = 2 * kSplitBatch * kSkinnyWaves * kWave * 16;  // partial-sum region
 
 // FUSED: one launch for the whole layer, as the one-token decode kernel.
-// Each block first quantises its problem's M token rows itself (wave w
-// takes rows w, w + 4, ..., with the wave-per-row arithmetic of the
-// streaming quantiser), into the partial-sum region of LDS, free until the
-// first batch is added (M * K <= 32 KiB).  The weight loads of the first groups are issued before, so HBM
-// is busy from the start, and no codes are written to or read from HBM.
-// Otherwise the codes, scales and sums come from an activation stage.
+// Each block first quantises its problem's M token rows itself (wave w takes
+// rows w, w + 4, ..., with the wave-per-row arithmetic of the streaming
+// quantiser) into the partial-sum region of LDS, which is free until the
+// first batch is added (M * K <= 32 KiB). The weight loads of the first
+// groups are issued before, so HBM is busy from the start, and no codes are
+// written to or read from HBM. Otherwise the codes, scales and sums come
+// from an activation stage.
 template <int NCHW, int D, Epilogue EP, bool FUSED>
 __global__ __launch_bounds__(kSkinnyThreads) void skinny_split_kernel(ProductArgs a, DecodeArgs d,
                                                                       int rows_per_block) {
