@@ -435,6 +435,35 @@ def test_full_decode_2048(M):
     gu.assert_y_parity(y, ref["y"], np.ones(M, bool))
 
 
+@pytest.mark.parametrize("M", [1, 8])
+def test_full_decode_1024_layers(M):
+    """The timed decode step exactly as launched: 1024 layers of 2048/2048 in
+    one batched call (one block of 2048 rows per layer).  Sampled layers
+    match the oracle, and match a single-layer call bit for bit (the same
+    arithmetic per row under a different blocking)."""
+    L, N, K = 1024, 2048, 2048
+    _say("full decode, 1024 layers", M)
+    x = wl.x_normal(L * M, K, seed=0).reshape(L, M, K)
+    g = np.ones(K, np.float32)
+    packed = torch.empty((L, N, K // 4), dtype=torch.uint8, device=gu.DEV)
+    gamma = torch.empty(L, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(bl.bitlinear_pack_workspace_bytes(N, K), dtype=torch.uint8, device=gu.DEV)
+    for layer in range(L):
+        W = wl.w_normal_device(N, K, seed=0, layer=layer, device=gu.DEV)
+        bl.bitlinear_pack_weights(W, packed=packed[layer], gamma=gamma[layer:layer + 1], ws=ws)
+    xd = gu.to_dev_bf16(x.reshape(L * M, K)).view(L, M, K)
+    gd = torch.ones((L, K), dtype=torch.float32, device=gu.DEV)
+    y = bl.bitlinear_forward_batched(xd, gd, packed, gamma).cpu().numpy()
+    for layer in (0, 1, 333, 1022, 1023):
+        W = wl.w_normal_device(N, K, seed=0, layer=layer, device=gu.DEV).cpu().numpy()
+        ref = gu.orc().bitlinear(x[layer], g, W)
+        gu.assert_y_parity(y[layer], ref["y"])
+        y1 = bl.bitlinear_forward(xd[layer], gd[layer], packed[layer], gamma[layer:layer + 1]).cpu().numpy()
+        assert np.array_equal(y1, y[layer]), layer
+    del packed
+    torch.cuda.empty_cache()
+
+
 def _full_sampled(M, N, K, recipe, of, os_, nrows, kernel=bl.BITLINEAR_KERNEL_AUTO):
     x, W, g = gu.oracle_inputs(M, N, K, seed=0, recipe=recipe, outlier_frac=of, outlier_scale=os_,
                                g_kind="ones")
