@@ -435,14 +435,14 @@ def test_full_decode_2048(M):
     gu.assert_y_parity(y, ref["y"], np.ones(M, bool))
 
 
-@pytest.mark.parametrize("M", [1, 8])
-def test_full_decode_1024_layers(M):
-    """The timed decode step exactly as launched: 1024 layers of 2048/2048 in
-    one batched call (one block of 2048 rows per layer).  Sampled layers
-    match the oracle, and match a single-layer call bit for bit (the same
-    arithmetic per row under a different blocking)."""
-    L, N, K = 1024, 2048, 2048
-    _say("full decode, 1024 layers", M)
+# The timed decode steps exactly as launched: L layers in one batched call,
+# with the layer counts that make about 1 GiB of weights.
+@pytest.mark.parametrize("L,M,N,K", [(1024, 1, 2048, 2048), (1024, 8, 2048, 2048), (645, 1, 2560, 2560),
+                                     (240, 1, 6912, 2560), (239, 1, 2560, 6912)])
+def test_full_decode_layers(L, M, N, K):
+    """Sampled layers match the oracle, and match a single-layer call bit for
+    bit (the same arithmetic per row under a different blocking)."""
+    _say("full decode, layers", L, M, N, K)
     x = wl.x_normal(L * M, K, seed=0).reshape(L, M, K)
     g = np.ones(K, np.float32)
     packed = torch.empty((L, N, K // 4), dtype=torch.uint8, device=gu.DEV)
@@ -454,13 +454,46 @@ def test_full_decode_1024_layers(M):
     xd = gu.to_dev_bf16(x.reshape(L * M, K)).view(L, M, K)
     gd = torch.ones((L, K), dtype=torch.float32, device=gu.DEV)
     y = bl.bitlinear_forward_batched(xd, gd, packed, gamma).cpu().numpy()
-    for layer in (0, 1, 333, 1022, 1023):
+    for layer in (0, 1, L // 3, L - 2, L - 1):
         W = wl.w_normal_device(N, K, seed=0, layer=layer, device=gu.DEV).cpu().numpy()
         ref = gu.orc().bitlinear(x[layer], g, W)
         gu.assert_y_parity(y[layer], ref["y"])
         y1 = bl.bitlinear_forward(xd[layer], gd[layer], packed[layer], gamma[layer:layer + 1]).cpu().numpy()
         assert np.array_equal(y1, y[layer]), layer
     del packed
+    torch.cuda.empty_cache()
+
+
+def test_full_glu_128_mixers():
+    """The timed one-token GLU step exactly as launched: 128 mixers of
+    2048/5632 in one batched call; sampled mixers against the oracle and
+    against single-mixer calls, bit for bit."""
+    L, D, F = 128, 2048, 5632
+    _say("full glu, 128 mixers")
+    x = wl.x_normal(L, D, seed=2).reshape(L, 1, D)
+    pgu = torch.empty((L, 2 * F, D // 4), dtype=torch.uint8, device=gu.DEV)
+    pdn = torch.empty((L, D, F // 4), dtype=torch.uint8, device=gu.DEV)
+    ggu = torch.empty(L, dtype=torch.float32, device=gu.DEV)
+    gdn = torch.empty(L, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(max(bl.bitlinear_pack_workspace_bytes(2 * F, D), bl.bitlinear_pack_workspace_bytes(D, F)),
+                     dtype=torch.uint8, device=gu.DEV)
+    w_gu = lambda layer: wl.w_normal_device(2 * F, D, seed=2, layer=2 * layer, device=gu.DEV)
+    w_dn = lambda layer: wl.w_normal_device(D, F, seed=2, layer=2 * layer + 1, device=gu.DEV)
+    for layer in range(L):
+        bl.bitlinear_pack_weights(w_gu(layer), packed=pgu[layer], gamma=ggu[layer:layer + 1], ws=ws)
+        bl.bitlinear_pack_weights(w_dn(layer), packed=pdn[layer], gamma=gdn[layer:layer + 1], ws=ws)
+    xd = gu.to_dev_bf16(x.reshape(L, D)).view(L, 1, D)
+    g_gu = torch.ones((L, D), dtype=torch.float32, device=gu.DEV)
+    g_dn = torch.ones((L, F), dtype=torch.float32, device=gu.DEV)
+    y = bl.bitlinear_glu_forward_batched(xd, g_gu, pgu, ggu, g_dn, pdn, gdn).cpu().numpy()
+    ones_d, ones_f = np.ones(D, np.float32), np.ones(F, np.float32)
+    for layer in (0, 1, 77, L - 1):
+        ref = gu.orc().glu(x[layer], ones_d, w_gu(layer).cpu().numpy(), ones_f, w_dn(layer).cpu().numpy())
+        gu.assert_y_parity(y[layer], ref["y"])
+        y1 = bl.bitlinear_glu_forward(xd[layer], g_gu[layer], pgu[layer], ggu[layer:layer + 1], g_dn[layer],
+                                      pdn[layer], gdn[layer:layer + 1]).cpu().numpy()
+        assert np.array_equal(y1, y[layer]), layer
+    del pgu, pdn
     torch.cuda.empty_cache()
 
 
