@@ -13,10 +13,13 @@ weight) + 4*M*N (y) + 4 (gamma).
 Also reported (`secondary`): the literal single-layer call at M=1, the M=8
 decode step, the one-token decode step of the 2560/6912 layer shapes (each
 over about 1 GiB of cold weights), the 8192-token prefill (int8 TOPS of the
-MFMA product kernel, timed apart from the quantisation kernel), and the GLU
-mixer at M=1 (one call, and one step through 128 mixers) and M=4096.  `roofline` is for the headline's dominant kernel, timed with HIP
-events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
-bounded sample of the headline workload on this host.
+MFMA product kernel, timed apart from the quantisation kernel), the GLU
+mixer at M=1 (one call, and one step through 128 mixers) and M=4096, the
+batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, and a
+plain 2 GiB device copy as context.  `roofline` is for the headline's
+dominant kernel, timed with one HIP event pair around the timed steps on the
+stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample of
+the headline workload on this host.
 
 One GPU only: `--gpus N` with N > 1 exits with a message.
 """
