@@ -243,6 +243,46 @@ def test_forward(M, N, K, recipe, of, os_):
         _forward_case(M, N, K, recipe, of, os_, kern)
 
 
+def _random_shapes(n, seed):
+    """Seeded (M, N, K) draws across the dispatch bands (1-4 tokens, 5-16,
+    17-128, 129-700) and row lengths that select different kernels (K % 64,
+    % 128, % 256, % 512 or 1024, 2048 and 4096 exactly, long rows), with N
+    ragged; sizes kept so the oracle stays fast."""
+    r = wl.rng(seed, 11)
+    ks = [16, 48, 64, 128, 256, 384, 512, 528, 1024, 1536, 2048, 2064, 2560, 3008, 4096, 5632, 6912, 8192]
+    bands = [(1, 5), (5, 17), (17, 129), (129, 701)]
+    out = []
+    for i in range(n):
+        lo, hi = bands[i % 4]
+        M, K, N = int(r.integers(lo, hi)), int(r.choice(ks)), int(r.integers(1, 3001))
+        while M * N * K > 4e7 and N > 1:
+            N = max(1, N // 2)
+        out.append((M, N, K))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(96, 2024)
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_SHAPES)))
+def test_forward_random_shapes(case):
+    """Every kernel that takes a seeded random shape against the oracle."""
+    M, N, K = RANDOM_SHAPES[case]
+    recipe, of, os_ = ("student_t3", 0.0, 1.0) if case % 3 == 0 else ("normal", 0.01 * (case % 2), 20.0)
+    x, W, g = gu.oracle_inputs(M, N, K, case, recipe, of, os_, "random")
+    ref = gu.orc().bitlinear(x, g, W)
+    packed, gamma = gu.pack_on_gpu(W)
+    xd, gd = gu.to_dev_bf16(x), gu.to_dev(g)
+    q, s = bl.bitlinear_quantize(xd, gd)
+    q = q.cpu().numpy()
+    gu.assert_q_parity(q, ref["q"], s.cpu().numpy(), ref["s"])
+    rows_eq = np.all(q == ref["q"], axis=1)
+    for kern in kernels_for(M, K):
+        _say("random shape", case, M, N, K, recipe, "kernel", kern)
+        y = bl.bitlinear_forward(xd, gd, packed, gamma, kernel=kern).cpu().numpy()
+        gu.assert_y_parity(y, ref["y"], rows_eq)
+
+
 def test_forward_parity_config_ones_gain():
     """The single-layer workload exactly as stated: gain 1, seed 0."""
     _say("forward parity config")
@@ -413,6 +453,24 @@ def test_glu_forward_batched(M):
     for b, c in enumerate(cases):
         ref = gu.orc().glu(*c)
         gu.assert_y_parity(y[b], ref["y"])
+
+
+@pytest.mark.parametrize("M,D,F", [(1, 64, 96), (2, 2048, 5632), (3, 512, 1040), (6, 256, 2048),
+                                   (11, 2048, 1024), (40, 128, 320), (300, 256, 96), (130, 1024, 2048)])
+def test_glu_forward_more_shapes(M, D, F):
+    """GLU mixers across the dispatch bands of both projections (fused
+    decode, few-token, small and large MFMA tiles), D and F ragged against
+    the tile widths."""
+    _say("glu shapes", M, D, F)
+    c = _glu_inputs(M, D, F, seed=M + D + F)
+    pgu, ggu = gu.pack_on_gpu(c[2])
+    pdn, gdn = gu.pack_on_gpu(c[4])
+    xd = gu.to_dev_bf16(c[0])
+    y = bl.bitlinear_glu_forward(xd, gu.to_dev(c[1]), pgu, ggu, gu.to_dev(c[3]), pdn, gdn).cpu().numpy()
+    h = gu.from_dev_bf16(bl.bitlinear_glu_hidden(xd, gu.to_dev(c[1]), pgu, ggu))
+    ref = gu.orc().glu(*c)
+    assert_h_parity(h, ref["h"])
+    gu.assert_y_parity(y, ref["y"])
 
 
 # --------------------------------------------------------------------------
