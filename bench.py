@@ -12,8 +12,10 @@ weight) + 4*M*N (y) + 4 (gamma).
 
 Also reported (`secondary`): the literal single-layer call at M=1, the M=8
 decode step, the one-token decode step of the 2560/6912 layer shapes (each
-over about 1 GiB of cold weights), the 8192-token prefill (int8 TOPS of the
-MFMA product kernel, timed apart from the quantisation kernel), the GLU
+over about 1 GiB of cold weights) and the same shapes at 64 and 512 tokens
+(over about 1 GiB, with HBM, int8 and combined-bound fractions) and at 4096
+and 16384 tokens, the 8192-token prefill (int8 TOPS of the MFMA product
+kernel, timed apart from the quantisation kernel), the GLU
 mixer at M=1 (one call, and one step through 128 mixers) and M=4096, the
 batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, and a
 plain 2 GiB device copy as context.  `roofline` is for the headline's
@@ -179,6 +181,21 @@ def bench_decode(torch, bl, wl, L, M, N, K, steps, warmup, stream):
     torch.cuda.empty_cache()
     return dict(layers=L, M=M, N=N, K=K, bytes_per_step=nbytes, wall_ms=wall, event_ms=ev,
                 gbps=nbytes / (wall * 1e-3) / 1e9, kernel_gbps=nbytes / (ev * 1e-3) / 1e9)
+
+
+def bench_sweep_layers(torch, bl, wl, M, N, K, steps, warmup, stream):
+    """A layer shape at M tokens over about 1 GiB of algorithmic bytes (L
+    independent layers in one batched call), with both roofline fractions:
+    HBM (bytes / 8 TB/s) and int8 MFMA (2 M N K / 5.0 POPS), and the fraction
+    of the combined bound max(bytes / BW, ops / peak)."""
+    L = max(1, (1 << 30) // layer_bytes(M, N, K))
+    r = bench_decode(torch, bl, wl, L, M, N, K, steps, warmup, stream)
+    t = r["event_ms"] * 1e-3
+    ops = 2.0 * L * M * N * K
+    t_min = max(r["bytes_per_step"] / HBM_PEAK, ops / I8_PEAK)
+    r.update(int8_ops_per_step=ops, tops=ops / t / 1e12, frac_hbm=r["bytes_per_step"] / t / HBM_PEAK,
+             frac_i8=ops / t / I8_PEAK, frac_combined_bound=t_min / t)
+    return r
 
 
 def bench_single_layer(torch, bl, wl, M, N, K, steps, stream):
@@ -384,6 +401,15 @@ def main():
             log(f"[bench] decode M=1 K={K2} N={N2} x {L2} layers")
             secondary[f"decode_m1_k{K2}_n{N2}_layers"] = bench_decode(
                 torch, bl, wl, L2, 1, N2, K2, max(5, args.steps // 2), args.warmup, stream)
+        for K2, N2 in ((2560, 2560), (2560, 6912), (6912, 2560)):
+            for M2 in (64, 512):
+                log(f"[bench] sweep M={M2} K={K2} N={N2} over ~1 GiB")
+                secondary[f"sweep_m{M2}_k{K2}_n{N2}_layers"] = bench_sweep_layers(
+                    torch, bl, wl, M2, N2, K2, max(5, args.steps // 5), args.warmup, stream)
+            for M2 in (4096, 16384):
+                log(f"[bench] sweep M={M2} K={K2} N={N2}")
+                secondary[f"sweep_m{M2}_k{K2}_n{N2}"] = bench_prefill(torch, bl, wl, M2, N2, K2, max(5, args.steps // 5),
+                                                                      args.warmup, stream)
         log("[bench] glu")
         secondary["glu_m1_layers"] = bench_glu_layers(torch, bl, wl, 128, 1, 2048, 5632, max(5, args.steps // 2),
                                                       args.warmup, stream)

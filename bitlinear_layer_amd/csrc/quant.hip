@@ -147,6 +147,14 @@ __global__ __launch_bounds__(kStreamThreads) void quant_stream_kernel(
     const int nchunks = K / 8;
 
     if constexpr (SHARED_G) {
+        // grid y: groups of `rows` rows with a weight each (a stack of
+        // layers); group blockIdx.y is a problem of its own from here on.
+        const int64_t group = blockIdx.y;
+        x += group * rows * K;
+        g += group * K;
+        q += group * rows * K;
+        s += group * rows;
+        if (sumq) sumq += group * rows;
         for (int i = threadIdx.x; i < kSpan; i += kStreamThreads) {
             float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
             if (FULL || i < nchunks) {
@@ -229,6 +237,16 @@ void launch_stream_g(dim3 grid, hipStream_t stream, const uint16_t* x, const flo
     if (rows_per_g >= rows) {
         quant_stream_kernel<CPL, FULL, true><<<grid, kStreamThreads, stream_lds_bytes<CPL>(), stream>>>(
             x, g, rows_per_g, rows, K, eps, out.q, out.s, out.sumq);
+    } else if (rows % rows_per_g == 0 && rows / rows_per_g <= 65535) {
+        // A weight per group of rows (a stack of layers): one launch with the
+        // groups along grid y, each block staging its group's weight in LDS
+        // once and walking that group's rows (up to 4 per wave, prefetched)
+        // -- rather than each wave re-reading a weight row per x row.
+        const int64_t groups = rows / rows_per_g;
+        const int64_t per_block = (int64_t)(kStreamThreads / kWave) * 4;
+        const dim3 ggrid((unsigned)((rows_per_g + per_block - 1) / per_block), (unsigned)groups);
+        quant_stream_kernel<CPL, FULL, true><<<ggrid, kStreamThreads, stream_lds_bytes<CPL>(), stream>>>(
+            x, g, rows_per_g, rows_per_g, K, eps, out.q, out.s, out.sumq);
     } else if constexpr (stream_per_row_g_ok(CPL, FULL)) {
         quant_stream_kernel<CPL, FULL, false><<<grid, kStreamThreads, 0, stream>>>(
             x, g, rows_per_g, rows, K, eps, out.q, out.s, out.sumq);
@@ -316,7 +334,8 @@ hipError_t launch_quant(const uint16_t* x, const float* g, int64_t rows, int64_t
     const int nchunks = K / 8;
     const int cpl = (nchunks + kWave - 1) / kWave;  // chunks per lane, one wave per row
     const bool full = K == cpl * kWave * 8;
-    if (rows >= 64 && cpl <= 16 && (rows_per_g >= rows || stream_per_row_g_ok(cpl, full))) {
+    const bool grouped_g = rows % rows_per_g == 0 && rows / rows_per_g <= 65535;
+    if (rows >= 64 && cpl <= 16 && (rows_per_g >= rows || grouped_g || stream_per_row_g_ok(cpl, full))) {
         const int64_t waves_per_block = kStreamThreads / kWave;
         const dim3 grid((unsigned)std::min<int64_t>((rows + waves_per_block - 1) / waves_per_block,
                                                     kStreamBlocks));
