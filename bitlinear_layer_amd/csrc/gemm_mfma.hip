@@ -59,14 +59,20 @@ __device__ __forceinline__ int64_t b_row(int tn, int r, int N) {
 }
 
 // Workgroups are dispatched to the 8 XCDs round robin (block i -> XCD i % 8),
-// and each XCD has its own L2.  Renumber tiles so that XCD x gets the
-// contiguous range [x * T/8, (x+1) * T/8): with N-tiles fastest, an XCD then
-// owns whole rows of token tiles -- each A tile is fetched into one L2 only,
-// and the packed weights (small) stay resident in every L2.
+// and each XCD has its own L2.  Renumber work items so that XCD x gets a
+// contiguous range of them: with N-tiles fastest, an XCD then owns whole rows
+// of token tiles -- each A tile is fetched into one L2 only -- and, for a
+// stack of problems in one launch (the batch flattened into the block index,
+// problem-major), whole problems: a layer's tiles share its codes and weights
+// in one L2 instead of fetching them into up to eight.  XCD x takes
+// items [start_x, start_x + count_x) with count_x = ceil((T - x) / 8), the
+// number of block indices i < T with i % 8 == x, so the map is one-to-one
+// for any T.
 __device__ __forceinline__ int xcd_tile(int bid, int tiles) {
     constexpr int kXcds = 8;
-    if (tiles % kXcds != 0) return bid;
-    return (bid % kXcds) * (tiles / kXcds) + bid / kXcds;
+    const int x = bid % kXcds, i = bid / kXcds;
+    const int q = tiles / kXcds, r = tiles % kXcds;
+    return x * q + min(x, r) + i;
 }
 
 template <int BM, int BN, int WM, int WN, Epilogue EP>
@@ -78,9 +84,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(ProductArgs a) {
 
     const int M = a.M, N = a.N, K = a.K;
     const int nwords = K / 16;
-    const int b = blockIdx.y;
     const int ntn = (N + T::kCols - 1) / T::kCols;
-    const int t = xcd_tile(blockIdx.x, gridDim.x);
+    const int per_problem = ntn * ((M + BM - 1) / BM);  // grid x = batch * per_problem
+    const int f = xcd_tile(blockIdx.x, gridDim.x);
+    const int b = f / per_problem;
+    const int t = f - b * per_problem;
     const int tn = t % ntn;
     const int tm = t / ntn;
     const int m0 = tm * BM;
@@ -273,9 +281,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
 
     const int M = a.M, N = a.N, K = a.K;
     const int nwords = K / 16;
-    const int b = blockIdx.y;
     const int ntn = (N + T::kCols - 1) / T::kCols;
-    const int t = xcd_tile(blockIdx.x, gridDim.x);
+    const int per_problem = ntn * ((M + BM - 1) / BM);  // grid x = batch * per_problem
+    const int f = xcd_tile(blockIdx.x, gridDim.x);
+    const int b = f / per_problem;
+    const int t = f - b * per_problem;
     const int tn = t % ntn;
     const int tm = t / ntn;
     const int m0 = tm * BM;
@@ -458,9 +468,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
 
     const int M = a.M, N = a.N, K = a.K;
     const int nwords = K / 16;
-    const int b = blockIdx.y;
     const int ntn = (N + kCols - 1) / kCols;
-    const int t = xcd_tile(blockIdx.x, gridDim.x);
+    const int per_problem = ntn * ((M + BM - 1) / BM);  // grid x = batch * per_problem
+    const int f = xcd_tile(blockIdx.x, gridDim.x);
+    const int b = f / per_problem;
+    const int t = f - b * per_problem;
     const int tn = t % ntn;
     const int tm = t / ntn;
     const int m0 = tm * BM;
@@ -791,7 +803,8 @@ template <int BM, int WM, int WN, Epilogue EP>
 hipError_t launch_x32(const ProductArgs& a, hipStream_t stream) {
     constexpr int kCols = EP == Epilogue::kGluBf16 ? 128 : 256;
     const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + BM - 1) / BM);
-    const dim3 grid((unsigned)tiles, (unsigned)a.batch);
+    if (tiles * a.batch > 0x7fffffff) return hipErrorInvalidValue;  // one grid dimension
+    const dim3 grid((unsigned)(tiles * a.batch));
     gemm_x32_kernel<BM, WM, WN, EP><<<grid, WM * WN * kWave, 0, stream>>>(a);
     return hipGetLastError();
 }
@@ -800,7 +813,8 @@ template <int BM, int BN, int WM, int WN, Epilogue EP>
 hipError_t launch_dma_tile(const ProductArgs& a, hipStream_t stream) {
     using T = Tile<BM, BN, WM, WN, EP>;
     const int64_t tiles = (int64_t)((a.N + T::kCols - 1) / T::kCols) * ((a.M + BM - 1) / BM);
-    const dim3 grid((unsigned)tiles, (unsigned)a.batch);
+    if (tiles * a.batch > 0x7fffffff) return hipErrorInvalidValue;  // one grid dimension
+    const dim3 grid((unsigned)(tiles * a.batch));
     gemm_dma_kernel<BM, BN, WM, WN, EP><<<grid, T::kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
@@ -809,7 +823,8 @@ template <int BM, int BN, int WM, int WN, Epilogue EP>
 hipError_t launch_tile(const ProductArgs& a, hipStream_t stream) {
     using T = Tile<BM, BN, WM, WN, EP>;
     const int64_t tiles = (int64_t)((a.N + T::kCols - 1) / T::kCols) * ((a.M + BM - 1) / BM);
-    const dim3 grid((unsigned)tiles, (unsigned)a.batch);
+    if (tiles * a.batch > 0x7fffffff) return hipErrorInvalidValue;  // one grid dimension
+    const dim3 grid((unsigned)(tiles * a.batch));
     gemm_kernel<BM, BN, WM, WN, EP><<<grid, T::kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
