@@ -145,8 +145,9 @@ size_t bitlinear_pack_batched_workspace_bytes(int64_t B, int64_t N, int64_t K);
 
 /* B matrices of one shape ternarised in one call -- the re-ternarisation of
  * a stack of layers from their fp32 master weights, e.g. once per training
- * step ([ld246, "训练与优化：新的策略"]: the ternary weights are recomputed
- * from full-precision ones, gradients passing straight through).
+ * step ([ld246, "训练与优化：新的策略"]: training passes gradients straight
+ * through the ternarisation, so the full-precision weights are kept, updated
+ * and ternarised again).
  * W: device fp32 [B][N][K]; packed: device [B][N][K/4]; gamma: device fp32
  * [B], one mean |W| per matrix.  Each matrix gets exactly the bytes and gamma
  * that bitlinear_pack_weights gives it.  1 <= B <= 65535. */
