@@ -261,23 +261,44 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-constexpr int kStages = 3;
 
 
 
-template <int BM, int BN, int WM, int WN, Epilogue EP>
+// Swizzle of the 16-byte pieces of a B stage row (BK / 64 pieces): rows
+// r and r + 8 (BK = 128) or r, r + 4, r + 8, r + 12 (BK = 256) share banks
+// and differ in the piece, so a 16-row fragment read is conflict free.
+template <int BK>
+__device__ __forceinline__ int b_swizzle(int r) {
+    return BK == 128 ? ((r >> 3) & 1) : ((r >> 2) & 3);
+}
+
+// BK: k per LDS stage (128 or 256).  A stage row is BK bytes of codes; a B
+// stage row is BK / 4 packed bytes.  With BK = 256 each DMA instruction reads
+// 64 contiguous bytes of each of 16 weight rows, where BK = 128 reads 32 of
+// each of 32 rows: 32-byte runs stream at about 3.8 TB/s, 64-byte runs at
+// 6.3-6.4 and 128-byte runs at 6.8 (copies of the pattern without arithmetic).
+template <int BM, int BN, int WM, int WN, Epilogue EP, int BK>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a) {
     using T = Tile<BM, BN, WM, WN, EP>;
     constexpr bool kGlu = T::kGlu;
     constexpr int kWavesPerBlock = WM * WN;
-    constexpr int kAStage = BM * kBK;         // bytes
-    constexpr int kBStage = BN * (kBK / 4);   // bytes
+    constexpr int kAStage = BM * BK;          // bytes
+    constexpr int kBStage = BN * (BK / 4);    // bytes
+    constexpr int kALanes = BK / 16;          // lanes per A row in a DMA instruction (8 or 16)
+    constexpr int kBLanes = BK / 64;          // lanes per B row (2 or 4)
+    static_assert(BK == 128 || BK == 256, "stage of 128 or 256 k");
+    // Stages in flight while one is multiplied: two of 16 KiB at BK = 128
+    // (three buffers, 48 KiB: three blocks per CU), one of 32 KiB at BK = 256
+    // (two buffers, 64 KiB: two blocks per CU; three buffers would leave one
+    // block per CU, which measured slower).
+    constexpr int kDist = BK == 256 ? 1 : 2;
+    constexpr int kBufs = kDist + 1;
     constexpr int kADma = kAStage / 1024 / kWavesPerBlock;  // 1 KiB DMA instructions per wave
     constexpr int kBDma = kBStage / 1024 / kWavesPerBlock;
     static_assert(kADma >= 1 && kBDma >= 1 && kADma * 1024 * kWavesPerBlock == kAStage &&
                       kBDma * 1024 * kWavesPerBlock == kBStage,
                   "stage must split into whole 1 KiB DMA instructions per wave");
-    __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * (kAStage + kBStage)];
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kBufs * (kAStage + kBStage)];
 
     const int M = a.M, N = a.N, K = a.K;
     const int nwords = K / 16;
@@ -301,29 +322,32 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
     // Per-lane global sources (stage 0) and LDS slots of this wave's DMAs.
     const int8_t* asrc[kADma];
     const uint32_t* bsrc[kBDma];
+    // The DMA writes lane i's 16 bytes to LDS slot i of its 1 KiB block, so
+    // the XOR swizzles of the LDS layout are applied to the global source:
+    // LDS slot (row r, chunk c) holds global chunk c ^ swizzle(r).
 #pragma unroll
     for (int i = 0; i < kADma; ++i) {
-        const int r = (wave * kADma + i) * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ (r & 7);
+        const int r = (wave * kADma + i) * (kWave / kALanes) + lane / kALanes;
+        const int chunk = (lane % kALanes) ^ (r % kALanes);
         asrc[i] = Q + (int64_t)min(m0 + r, M - 1) * K + 16 * chunk;
     }
 #pragma unroll
     for (int i = 0; i < kBDma; ++i) {
-        const int r = (wave * kBDma + i) * 32 + (lane >> 1);
-        const int half = (lane & 1) ^ ((r >> 3) & 1);
-        bsrc[i] = P + b_row<BN, kGlu>(tn, r, N) * nwords + 4 * half;
+        const int r = (wave * kBDma + i) * (kWave / kBLanes) + lane / kBLanes;
+        const int piece = (lane % kBLanes) ^ b_swizzle<BK>(r);
+        bsrc[i] = P + b_row<BN, kGlu>(tn, r, N) * nwords + 4 * piece;
     }
     auto issue_stage = [&](int st) {
-        const int buf = st % kStages;
+        const int buf = st % kBufs;
         int8_t* abase = lds + buf * kAStage;
-        int8_t* bbase = lds + kStages * kAStage + buf * kBStage;
+        int8_t* bbase = lds + kBufs * kAStage + buf * kBStage;
 #pragma unroll
         for (int i = 0; i < kADma; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[i] + st * kBK),
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[i] + st * BK),
                                              (lds_void_t*)(abase + (wave * kADma + i) * 1024), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < kBDma; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[i] + st * (kBK / 16)),
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[i] + st * (BK / 16)),
                                              (lds_void_t*)(bbase + (wave * kBDma + i) * 1024), 16, 0, 0);
     };
 
@@ -333,12 +357,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    const int nstages = K / kBK;
-    issue_stage(0);
-    if (nstages > 1) issue_stage(1);
+    const int nstages = K / BK;
+    for (int d = 0; d < kDist && d < nstages; ++d) issue_stage(d);
     for (int st = 0; st < nstages; ++st) {
-        // Stage st has landed once at most the next stage's DMAs are pending.
-        if (st + 1 < nstages)
+        // Stage st has landed once at most the stages after it are pending.
+        if (kDist == 2 && st + 1 < nstages)
             __builtin_amdgcn_s_waitcnt((kADma + kBDma) | (7 << 4) | (15 << 8));
         else
             __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
@@ -348,12 +371,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (st + 2 < nstages) issue_stage(st + 2);
-        const int buf = st % kStages;
+        if (st + kDist < nstages) issue_stage(st + kDist);
+        const int buf = st % kBufs;
         const int8_t* abase = lds + buf * kAStage;
-        const uint32_t* bbase = reinterpret_cast<const uint32_t*>(lds + kStages * kAStage + buf * kBStage);
+        const uint32_t* bbase = reinterpret_cast<const uint32_t*>(lds + kBufs * kAStage + buf * kBStage);
 #pragma unroll
-        for (int kk = 0; kk < kBK / 64; ++kk) {
+        for (int kk = 0; kk < BK / 64; ++kk) {
             i32x4 bfrag[T::FN];
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
@@ -362,8 +385,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
                     r = (j < T::FN / 2 ? 0 : BN / 2) + wn * (T::TN / 2) + (j % (T::FN / 2)) * 16 + (lane & 15);
                 else
                     r = wn * T::TN + j * 16 + (lane & 15);
-                const int half = kk ^ ((r >> 3) & 1);
-                const uint32_t pw = bbase[r * 8 + half * 4 + (lane >> 4)];
+                const int piece = kk ^ b_swizzle<BK>(r);
+                const uint32_t pw = bbase[r * (BK / 16) + piece * 4 + (lane >> 4)];
                 int32_t c0, c1, c2, c3;
                 decode_codes(pw, c0, c1, c2, c3);
                 bfrag[j] = i32x4{c0, c1, c2, c3};
@@ -371,8 +394,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
 #pragma unroll
             for (int i = 0; i < T::FM; ++i) {
                 const int r = wm * T::TM + i * 16 + (lane & 15);
-                const int chunk = (kk * 4 + (lane >> 4)) ^ (r & 7);
-                const i32x4 afrag = *reinterpret_cast<const i32x4*>(abase + r * kBK + 16 * chunk);
+                const int chunk = (kk * 4 + (lane >> 4)) ^ (r % kALanes);
+                const i32x4 afrag = *reinterpret_cast<const i32x4*>(abase + r * BK + 16 * chunk);
 #pragma unroll
                 for (int j = 0; j < T::FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, bfrag[j], acc[i][j], 0, 0, 0);
@@ -809,13 +832,13 @@ hipError_t launch_x32(const ProductArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, Epilogue EP>
+template <int BM, int BN, int WM, int WN, Epilogue EP, int BK>
 hipError_t launch_dma_tile(const ProductArgs& a, hipStream_t stream) {
     using T = Tile<BM, BN, WM, WN, EP>;
     const int64_t tiles = (int64_t)((a.N + T::kCols - 1) / T::kCols) * ((a.M + BM - 1) / BM);
     if (tiles * a.batch > 0x7fffffff) return hipErrorInvalidValue;  // one grid dimension
     const dim3 grid((unsigned)(tiles * a.batch));
-    gemm_dma_kernel<BM, BN, WM, WN, EP><<<grid, T::kThreads, 0, stream>>>(a);
+    gemm_dma_kernel<BM, BN, WM, WN, EP, BK><<<grid, T::kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -842,7 +865,8 @@ hipError_t launch_ep(const ProductArgs& a, hipStream_t stream) {
         const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + 255) / 256) * a.batch;
         return tiles > 128 ? launch_x32<256, 4, 2, EP>(a, stream) : launch_x32<128, 2, 4, EP>(a, stream);
     }
-    return whole_stages ? launch_dma_tile<64, 256, 1, 8, EP>(a, stream)
+    if (a.K % 256 == 0) return launch_dma_tile<64, 256, 1, 8, EP, 256>(a, stream);
+    return whole_stages ? launch_dma_tile<64, 256, 1, 8, EP, 128>(a, stream)
                         : launch_tile<64, 256, 1, 8, EP>(a, stream);
 }
 
