@@ -493,14 +493,11 @@ def test_full_decode_2048(M):
     gu.assert_y_parity(y, ref["y"], np.ones(M, bool))
 
 
-# The timed decode steps exactly as launched: L layers in one batched call,
-# with the layer counts that make about 1 GiB of weights.
-@pytest.mark.parametrize("L,M,N,K", [(1024, 1, 2048, 2048), (1024, 8, 2048, 2048), (645, 1, 2560, 2560),
-                                     (240, 1, 6912, 2560), (239, 1, 2560, 6912)])
-def test_full_decode_layers(L, M, N, K):
-    """Sampled layers match the oracle, and match a single-layer call bit for
-    bit (the same arithmetic per row under a different blocking)."""
-    _say("full decode, layers", L, M, N, K)
+def _check_layer_stack(L, M, N, K, nrows):
+    """L independent layers in one batched call: sampled rows of sampled
+    layers match the oracle, and each sampled layer matches a single-layer
+    call bit for bit (the same arithmetic per row under a different
+    blocking)."""
     x = wl.x_normal(L * M, K, seed=0).reshape(L, M, K)
     g = np.ones(K, np.float32)
     packed = torch.empty((L, N, K // 4), dtype=torch.uint8, device=gu.DEV)
@@ -514,12 +511,31 @@ def test_full_decode_layers(L, M, N, K):
     y = bl.bitlinear_forward_batched(xd, gd, packed, gamma).cpu().numpy()
     for layer in (0, 1, L // 3, L - 2, L - 1):
         W = wl.w_normal_device(N, K, seed=0, layer=layer, device=gu.DEV).cpu().numpy()
-        ref = gu.orc().bitlinear(x[layer], g, W)
-        gu.assert_y_parity(y[layer], ref["y"])
+        rows = _sample_rows(M, nrows, layer)
+        ref = gu.orc().bitlinear(x[layer][rows], g, W)
+        gu.assert_y_parity(y[layer][rows], ref["y"])
         y1 = bl.bitlinear_forward(xd[layer], gd[layer], packed[layer], gamma[layer:layer + 1]).cpu().numpy()
         assert np.array_equal(y1, y[layer]), layer
     del packed
     torch.cuda.empty_cache()
+
+
+# The timed decode steps exactly as launched: L layers in one batched call,
+# with the layer counts that make about 1 GiB of weights.
+@pytest.mark.parametrize("L,M,N,K", [(1024, 1, 2048, 2048), (1024, 8, 2048, 2048), (645, 1, 2560, 2560),
+                                     (240, 1, 6912, 2560), (239, 1, 2560, 6912)])
+def test_full_decode_layers(L, M, N, K):
+    _say("full decode, layers", L, M, N, K)
+    _check_layer_stack(L, M, N, K, M)
+
+
+# The timed 64- and 512-token steps of the 2560/6912 shapes exactly as
+# launched: about 1 GiB of layers in one batched call on the MFMA tiles.
+@pytest.mark.parametrize("L,M,N,K", [(408, 64, 2560, 2560), (164, 64, 6912, 2560), (179, 64, 2560, 6912),
+                                     (112, 512, 2560, 2560), (50, 512, 6912, 2560), (64, 512, 2560, 6912)])
+def test_full_sweep_layers(L, M, N, K):
+    _say("full sweep, layers", L, M, N, K)
+    _check_layer_stack(L, M, N, K, 8)
 
 
 def test_full_glu_128_mixers():
@@ -575,7 +591,7 @@ def test_full_prefill_8192():
     _full_sampled(8192, 2048, 2048, "student_t3", 0.0, 1.0, 48)
 
 
-@pytest.mark.parametrize("M", [1, 64, 512, 4096])
+@pytest.mark.parametrize("M", [1, 64, 512, 4096, 16384])
 @pytest.mark.parametrize("K,N", [(2560, 2560), (2560, 6912), (6912, 2560)])
 def test_full_sweep_2560(M, K, N):
     _say("sweep", M, K, N)
