@@ -19,9 +19,9 @@ kernel, timed apart from the quantisation kernel), the GLU
 mixer at M=1 (one call, and one step through 128 mixers) and M=4096, the
 batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, and a
 plain 2 GiB device copy as context.  `roofline` is for the headline's
-dominant kernel, timed with one HIP event pair around the timed steps on the
-stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample of
-the headline workload on this host.
+dominant kernel, timed with one HIP event pair on the stream it runs on,
+around a second pass of the timed steps; `cpu_baseline` times the CPU
+oracle on a bounded sample of the headline workload on this host.
 
 One GPU only: `--gpus N` with N > 1 exits with a message.
 """
@@ -81,10 +81,14 @@ def timed_loop(torch, fn, steps, warmup, stream, per_call_events=False):
     """Run fn warmup times, then exactly `steps` times between device
     synchronisations.  Returns (wall ms per step, event ms per call).
 
-    By default one HIP event pair on the library's stream brackets the timed
-    steps (nothing is inserted between calls, so the wall time is not
-    stretched); the event time per call is that span / steps.  With
-    per_call_events each call gets its own pair (for single-call latency)."""
+    By default the wall time covers exactly `steps` calls between two device
+    synchronisations, and a second pass of `steps` calls gives the event
+    time: one HIP event pair on the library's stream brackets them, recorded
+    behind one untimed call, so the device is already busy when the span
+    opens and the span holds the calls' own device time, not the host's
+    latency to issue the first of them.  Nothing is inserted between calls.
+    With per_call_events each call gets its own pair (for single-call
+    latency)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -97,15 +101,19 @@ def timed_loop(torch, fn, steps, warmup, stream, per_call_events=False):
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return wall, timer.mean_ms()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
+    fn()
     start.record(stream)
     for _ in range(steps):
         fn()
     end.record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
     return wall, start.elapsed_time(end) / steps
 
 
@@ -225,8 +233,8 @@ def bench_prefill(torch, bl, wl, M, N, K, steps, warmup, stream):
                               steps, warmup, stream)
     return dict(M=M, N=N, K=K, int8_ops=ops, quant_us=ev_q * 1e3, product_us=ev_p * 1e3,
                 product_tops=ops / (ev_p * 1e-3) / 1e12, product_frac_i8_peak=ops / (ev_p * 1e-3) / I8_PEAK,
-                forward_us=wall_f * 1e3, forward_tops=ops / (wall_f * 1e-3) / 1e12,
-                forward_bytes=layer_bytes(M, N, K))
+                forward_us=ev_f * 1e3, forward_tops=ops / (ev_f * 1e-3) / 1e12,
+                forward_us_wall=wall_f * 1e3, forward_bytes=layer_bytes(M, N, K))
 
 
 def bench_glu(torch, bl, wl, M, D, F, steps, warmup, stream):
@@ -241,8 +249,8 @@ def bench_glu(torch, bl, wl, M, D, F, steps, warmup, stream):
                           steps, warmup, stream)
     ops = 2.0 * M * D * F * 3
     nbytes = glu_bytes(M, D, F)
-    return dict(M=M, D=D, F=F, us=wall * 1e3, gbps=nbytes / (wall * 1e-3) / 1e9,
-                tops=ops / (wall * 1e-3) / 1e12, bytes=nbytes, int8_ops=ops)
+    return dict(M=M, D=D, F=F, us=ev * 1e3, us_wall=wall * 1e3, gbps=nbytes / (ev * 1e-3) / 1e9,
+                tops=ops / (ev * 1e-3) / 1e12, bytes=nbytes, int8_ops=ops)
 
 
 def bench_glu_layers(torch, bl, wl, L, M, D, F, steps, warmup, stream):
