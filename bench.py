@@ -10,7 +10,8 @@ value = algorithmic bytes moved per step / wall time per step, where the
 algorithmic bytes of one layer are N*K/4 (packed W) + 2*M*K (x) + 4*K (RMSNorm
 weight) + 4*M*N (y) + 4 (gamma).
 
-Also reported (`secondary`): the literal single-layer call at M=1, the M=8
+Also reported (`secondary`): the literal single-layer call at M=1, the same
+calls over the 1024 layers replayed from one HIP graph, the M=8
 decode step, the one-token decode step of the 2560/6912 layer shapes (each
 over about 1 GiB of cold weights) and the same shapes at 64 and 512 tokens
 (over about 1 GiB, with HBM, int8 and combined-bound fractions) and at 4096
@@ -219,6 +220,36 @@ def bench_single_layer(torch, bl, wl, M, N, K, steps, stream):
                 implied_gbps=nbytes / (ev * 1e-3) / 1e9)
 
 
+def bench_graph_calls(torch, bl, wl, L, M, N, K, steps, warmup, stream):
+    """L single-layer bitlinear_forward calls, one per layer of an L-layer
+    stack, captured once into a HIP graph and replayed: the time per call
+    that a caller issuing layer by layer sees without host launch overhead
+    (the batched call runs the same stack as one launch)."""
+    x, g, packed, gamma, y, _ = make_decode_layers(torch, bl, wl, L, M, N, K, seed=2)
+    ws = torch.empty(bl.bitlinear_forward_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+
+    def calls():
+        for layer in range(L):
+            bl.bitlinear_forward(x[layer], g[layer], packed[layer], gamma[layer:layer + 1], y=y[layer], ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    wall, ev = timed_loop(torch, graph.replay, steps, warmup, stream)
+    nbytes = L * layer_bytes(M, N, K)
+    del graph, x, g, packed, gamma, y, ws
+    torch.cuda.empty_cache()
+    return dict(calls=L, M=M, N=N, K=K, us_per_call_event=ev * 1e3 / L, us_per_call_wall=wall * 1e3 / L,
+                gbps=nbytes / (ev * 1e-3) / 1e9)
+
+
 def bench_prefill(torch, bl, wl, M, N, K, steps, warmup, stream):
     x = torch.from_numpy(wl.x_student_t(M, K, seed=0).view("int16")).to(DEV)
     g = torch.ones(K, dtype=torch.float32, device=DEV)
@@ -398,6 +429,9 @@ def main():
     if not args.no_secondary:
         log("[bench] single layer M=1")
         secondary["decode_m1_single_layer"] = bench_single_layer(torch, bl, wl, 1, N, K, 200, stream)
+        log("[bench] single-layer calls over 1024 layers, replayed from a HIP graph")
+        secondary["decode_m1_graph_1024_calls"] = bench_graph_calls(torch, bl, wl, args.layers, 1, N, K, 5, 2,
+                                                                    stream)
         log("[bench] decode M=8")
         secondary["decode_m8_layers"] = bench_decode(torch, bl, wl, args.layers, 8, N, K, max(5, args.steps // 2),
                                                      args.warmup, stream)

@@ -95,6 +95,86 @@ __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__
     sumq_out = qsum;
 }
 
+// The same for rows of at most CPT * kThreads chunks of 8 elements: each
+// thread loads its chunks of x and of the RMSNorm weight once, up front, and
+// keeps them in registers for all three passes, so the prologue waits on
+// memory once instead of once per pass.  Every sum runs in the order of
+// quantise_row_to_lds (chunk by chunk, element by element, then the block
+// reduction), so the codes are the same bit for bit.
+template <int CPT>
+__device__ __forceinline__ void quantise_row_regs(const uint16_t* __restrict__ xr,
+                                                  const float* __restrict__ gr, int K, float eps,
+                                                  int8_t* __restrict__ qrow, double* dscr, float* fscr,
+                                                  int32_t* iscr, float& scale_out, int32_t& sumq_out) {
+    const int nchunks = K / 8;
+    uint32_t p[CPT][4];
+    float gv[CPT][8];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int i = threadIdx.x + c * kThreads;
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        float4 g0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), g1 = g0;
+        if (i < nchunks) {
+            raw = *reinterpret_cast<const uint4*>(xr + 8 * i);
+            g0 = *reinterpret_cast<const float4*>(gr + 8 * i);
+            g1 = *reinterpret_cast<const float4*>(gr + 8 * i + 4);
+        }
+        p[c][0] = raw.x;
+        p[c][1] = raw.y;
+        p[c][2] = raw.z;
+        p[c][3] = raw.w;
+        gv[c][0] = g0.x;
+        gv[c][1] = g0.y;
+        gv[c][2] = g0.z;
+        gv[c][3] = g0.w;
+        gv[c][4] = g1.x;
+        gv[c][5] = g1.y;
+        gv[c][6] = g1.z;
+        gv[c][7] = g1.w;
+    }
+    auto xval = [&](int c, int j) { return (j & 1) ? bf16_hi(p[c][j >> 1]) : bf16_lo(p[c][j >> 1]); };
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        if (threadIdx.x + c * kThreads >= nchunks) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float v = xval(c, j);
+            ss += (double)v * (double)v;
+        }
+    }
+    ss = block_sum(ss, dscr);
+    const float ms = (float)(ss / (double)K);
+    const float r = 1.0f / sqrtf(ms + eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        if (threadIdx.x + c * kThreads >= nchunks) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((xval(c, j) * r) * gv[c][j]));
+    }
+    amax = block_max(amax, fscr);
+    const float scale = 127.0f / fmaxf(amax, 1e-5f);
+    int32_t qsum = 0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int i = threadIdx.x + c * kThreads;
+        if (i >= nchunks) continue;
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float t = fminf(fmaxf(rintf(((xval(c, j) * r) * gv[c][j]) * scale), -128.0f), 127.0f);
+            const int32_t qi = (int32_t)t;
+            qsum += qi;
+            packed[j >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (j & 3));
+        }
+        *reinterpret_cast<uint2*>(qrow + 8 * i) = make_uint2(packed[0], packed[1]);
+    }
+    qsum = block_sum(qsum, iscr);
+    scale_out = scale;
+    sumq_out = qsum;
+}
+
 template <int MAXM, int S, int U, int LPR, Epilogue EP>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows_per_block) {
     constexpr bool kGlu = EP == Epilogue::kGluBf16;
@@ -149,7 +229,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
     for (int m = 0; m < M; ++m) {
         float sc;
         int32_t sq;
-        quantise_row_to_lds(X + (int64_t)m * K, G, K, a.eps, qlds + (int64_t)m * K, dscr, fscr, iscr, sc, sq);
+        const uint16_t* xr = X + (int64_t)m * K;
+        int8_t* qr = qlds + (int64_t)m * K;
+        // Rows this instance takes are at most 64 * S * LPR wide (S chunks of
+        // 64 weights per lane, LPR lanes per row), so one form is compiled.
+        if constexpr (64 * S * LPR <= 8 * kThreads)
+            quantise_row_regs<1>(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
+        else if constexpr (64 * S * LPR <= 16 * kThreads)
+            quantise_row_regs<2>(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
+        else
+            quantise_row_to_lds(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
         if (threadIdx.x == 0) {
             s_scale[m] = sc;
             s_sumq[m] = sq;
