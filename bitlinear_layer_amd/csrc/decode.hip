@@ -31,6 +31,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultCus = 256;
+constexpr int kMaxRowChunks = 4;  // rows up to 4 * 8 * kThreads = 8192 wide stay in registers
 
 // Block-cooperative RMSNorm + absmax int8 of one token row into LDS; the
 // same arithmetic and reduction order as the block-per-row quant_kernel, so
@@ -233,10 +234,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
         int8_t* qr = qlds + (int64_t)m * K;
         // Rows this instance takes are at most 64 * S * LPR wide (S chunks of
         // 64 weights per lane, LPR lanes per row), so one form is compiled.
-        if constexpr (64 * S * LPR <= 8 * kThreads)
-            quantise_row_regs<1>(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
-        else if constexpr (64 * S * LPR <= 16 * kThreads)
-            quantise_row_regs<2>(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
+        constexpr int kRowChunks = (64 * S * LPR + 8 * kThreads - 1) / (8 * kThreads);
+        if constexpr (kRowChunks <= kMaxRowChunks)
+            quantise_row_regs<kRowChunks>(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
         else
             quantise_row_to_lds(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
         if (threadIdx.x == 0) {
