@@ -394,6 +394,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay line (its 1024-node graphs are slow under counter collection)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -429,9 +431,10 @@ def main():
     if not args.no_secondary:
         log("[bench] single layer M=1")
         secondary["decode_m1_single_layer"] = bench_single_layer(torch, bl, wl, 1, N, K, 200, stream)
-        log("[bench] single-layer calls over 1024 layers, replayed from a HIP graph")
-        secondary["decode_m1_graph_1024_calls"] = bench_graph_calls(torch, bl, wl, args.layers, 1, N, K, 5, 2,
-                                                                    stream)
+        if not args.no_graph:
+            log("[bench] single-layer calls over 1024 layers, replayed from a HIP graph")
+            secondary["decode_m1_graph_1024_calls"] = bench_graph_calls(torch, bl, wl, args.layers, 1, N, K, 5,
+                                                                        2, stream)
         log("[bench] decode M=8")
         secondary["decode_m8_layers"] = bench_decode(torch, bl, wl, args.layers, 8, N, K, max(5, args.steps // 2),
                                                      args.warmup, stream)
