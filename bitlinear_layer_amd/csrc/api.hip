@@ -54,7 +54,7 @@ int check_k(int64_t K, const char* name) {
     CHECK(K > 0, BITLINEAR_ERR_INVALID_ARG, "%s must be > 0 (got %lld)", name, (long long)K);
     CHECK(K % 16 == 0, BITLINEAR_ERR_INVALID_ARG, "%s must be a multiple of 16 (got %lld)", name,
           (long long)K);
-    CHECK(K <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "%s exceeds BITLINEAR_MAX_DIM", name);
+    CHECK(K <= BITLINEAR_MAX_K, BITLINEAR_ERR_INVALID_ARG, "%s exceeds BITLINEAR_MAX_K", name);
     return BITLINEAR_OK;
 }
 
@@ -264,7 +264,7 @@ extern "C" {
 int bitlinear_abi_version(void) { return 1; }
 
 int bitlinear_decode_supported(int64_t M, int64_t K) {
-    if (M < 1 || K < 1 || M > BITLINEAR_MAX_DIM || K > BITLINEAR_MAX_DIM) return 0;
+    if (M < 1 || K < 1 || M > BITLINEAR_MAX_DIM || K > BITLINEAR_MAX_K) return 0;
     return fused_supported(M, K, false) ? 1 : 0;
 }
 

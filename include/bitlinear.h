@@ -49,10 +49,10 @@
  *     unless the status is BITLINEAR_ERR_HIP, and bitlinear_last_error()
  *     returns a message (per calling thread).
  *   - Checked before launch: non-NULL pointers for non-empty tensors; sizes
- *     >= 0 with K > 0; K (and D, F for the GLU) multiples of 16; row counts
- *     and K at most BITLINEAR_MAX_DIM; 16-byte alignment of every pointer
- *     and 256-byte alignment of the workspace; workspace size; eps > 0 and
- *     finite.  M = 0 or N = 0 is a valid empty call that does nothing.
+ *     >= 0 with K > 0; K (and D, F for the GLU) multiples of 16 and at most
+ *     BITLINEAR_MAX_K; row counts at most BITLINEAR_MAX_DIM; 16-byte
+ *     alignment of every pointer and 256-byte alignment of the workspace;
+ *     workspace size; eps > 0 and finite.  M = 0 or N = 0 is a valid empty call that does nothing.
  *   - Inputs are read-only; outputs are fully overwritten; outputs, inputs
  *     and workspace must not overlap.  NaN/Inf inputs are outside the
  *     contract.
@@ -97,6 +97,11 @@ typedef enum {
 /* Largest M, N, K, B*M, D or F accepted (keeps every in-kernel row index and
  * every row length in 32 bits). */
 #define BITLINEAR_MAX_DIM ((int64_t)1 << 30)
+
+/* Largest reduction length accepted: K, and D and F for the GLU.  Codes lie
+ * in [-127, 127], so every accumulation and every code sum stays below
+ * 127 * 2^24 < 2^31 in magnitude and the int32 results are exact. */
+#define BITLINEAR_MAX_K ((int64_t)1 << 24)
 
 /* Kernel choice for bitlinear_forward_ex. */
 typedef enum {

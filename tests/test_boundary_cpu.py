@@ -71,6 +71,7 @@ def _fwd(x=FAKE, g=FAKE, p=FAKE, gamma=FAKE, M=4, N=64, K=64, eps=1e-6, y=FAKE, 
     (dict(M=-1), bl.BITLINEAR_ERR_INVALID_ARG),
     (dict(N=-5), bl.BITLINEAR_ERR_INVALID_ARG),
     (dict(M=1 << 31), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(K=(1 << 24) + 16, M=1, N=1), bl.BITLINEAR_ERR_INVALID_ARG),  # past BITLINEAR_MAX_K
     (dict(eps=0.0), bl.BITLINEAR_ERR_INVALID_ARG),
     (dict(eps=float("nan")), bl.BITLINEAR_ERR_INVALID_ARG),
     (dict(ws=None), bl.BITLINEAR_ERR_WORKSPACE),
@@ -113,6 +114,14 @@ def test_other_entry_points_reject():
     assert L.bitlinear_quantize(FAKE, FAKE, 4, 32, -1.0, FAKE, FAKE, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert L.bitlinear_ternary_matmul_i32(FAKE, FAKE, 4, 64, 64, FAKE, FAKE, 8, None, 0) == bl.BITLINEAR_ERR_WORKSPACE
     assert L.bitlinear_ternary_matmul_i32(FAKE, None, 4, 64, 64, FAKE, FAKE, 1 << 20, None, 0) == bl.BITLINEAR_ERR_INVALID_ARG
+    # reduction lengths past BITLINEAR_MAX_K (int32 sums could no longer be exact)
+    big = (1 << 24) + 16
+    assert L.bitlinear_ternary_matmul_i32(FAKE, FAKE, 1, 1, big, FAKE, FAKE, 1 << 30, None, 0) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_quantize(FAKE, FAKE, 1, big, 1e-6, FAKE, FAKE, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_glu_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, big, 1e-6, FAKE, FAKE, 1 << 30,
+                                   None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_decode_supported(1, big) == 0
+    assert L.bitlinear_ternary_matmul_i32(FAKE, FAKE, 1, 1, 1 << 24, FAKE, FAKE, 0, None, 0) == bl.BITLINEAR_ERR_WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
