@@ -43,6 +43,9 @@
  *     fp32.  gamma is a device fp32 scalar (no host round trip).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work and return; nothing synchronises the host.
+ *     No entry point allocates, copies or clears memory: each only launches
+ *     kernels on `stream`, so a sequence of calls can be captured into a HIP
+ *     graph and replayed (with the same pointers and sizes).
  *     Faults inside kernels surface at the caller's next synchronisation.
  *   - Return value: BITLINEAR_OK (0) or a bitlinear_status; on error nothing
  *     was launched (argument and workspace checks run before any launch)
