@@ -220,6 +220,10 @@ FORWARD = [
     (13, 333, 2048, "student_t3", 0.01, 20.0),  # fused few-token kernel, ragged groups
     (6, 200, 4096, "normal", 0.0, 1.0),      # fused few-token kernel, K = 4096
     (16, 130, 4096, "normal", 0.0, 1.0),     # 16 x 4096 codes exceed its LDS: two launches
+    (1, 65, 8192, "normal", 0.005, 50.0),    # widest decode row quantised from registers
+    (4, 33, 8192, "student_t3", 0.0, 1.0),   # the same, four tokens
+    (1, 40, 28672, "normal", 0.0, 1.0),      # widest row the fused decode kernel takes
+    (2, 24, 28736, "normal", 0.0, 1.0),      # one chunk past it: quantisation pass + product
 ]
 
 
