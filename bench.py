@@ -18,11 +18,12 @@ over about 1 GiB of cold weights) and the same shapes at 64 and 512 tokens
 and 16384 tokens, the 8192-token prefill (int8 TOPS of the MFMA product
 kernel, timed apart from the quantisation kernel), the GLU
 mixer at M=1 (one call, and one step through 128 mixers) and M=4096, the
-batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, and a
-plain 2 GiB device copy as context.  `roofline` is for the headline's
-dominant kernel, timed with one HIP event pair on the stream it runs on,
-around a second pass of the timed steps; `cpu_baseline` times the CPU
-oracle on a bounded sample of the headline workload on this host.
+batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, and, as
+context, a plain 2 GiB device copy and the vendor's dense int8 GEMM at the
+prefill shape.  `roofline` is for the headline's dominant kernel, timed with
+one HIP event pair on the stream it runs on, around a second pass of the
+timed steps; `cpu_baseline` times the CPU oracle on a bounded sample of the
+headline workload on this host.
 
 One GPU only: `--gpus N` with N > 1 exits with a message.
 """
@@ -352,6 +353,26 @@ def bench_hbm_copy(torch, nbytes, steps):
     return dict(bytes_each_way=nbytes, gbps_read_plus_write=2.0 * nbytes * steps / el / 1e9)
 
 
+def bench_vendor_int8_gemm(torch, M, N, K, steps, warmup, stream):
+    """Context, not this library's path: the vendor's dense int8 GEMM
+    (torch._int_mm, int8 [M, K] x int8 [K, N] -> int32 [M, N]) on the
+    prefill shape, with random int8 operands and B column-major (its faster
+    layout here).  It does no quantisation, no 2-bit unpacking and no
+    rescale."""
+    if not hasattr(torch, "_int_mm"):
+        return dict(error="torch._int_mm is not available")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(0)
+    a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=DEV, generator=gen)
+    b = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=DEV, generator=gen).t()
+    try:
+        wall, ev = timed_loop(torch, lambda: torch._int_mm(a, b), steps, warmup, stream)
+    except (RuntimeError, NotImplementedError) as ex:
+        return dict(error=repr(ex)[:200])
+    ops = 2.0 * M * N * K
+    return dict(M=M, N=N, K=K, us=ev * 1e3, tops=ops / (ev * 1e-3) / 1e12, frac_i8_peak=ops / (ev * 1e-3) / I8_PEAK)
+
+
 # --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
@@ -462,6 +483,9 @@ def main():
         log("[bench] re-ternarisation of 64 x 2048 x 2048 fp32 master weights")
         secondary["repack_64x2048x2048"] = bench_repack(torch, bl, wl, 64, 2048, 2048, 10, 2, stream)
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
+        log("[bench] context: vendor int8 GEMM at the prefill shape")
+        secondary["context_vendor_int8_gemm_8192x2048x2048"] = bench_vendor_int8_gemm(
+            torch, 8192, 2048, 2048, max(10, args.steps // 2), args.warmup, stream)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
 
