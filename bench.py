@@ -19,11 +19,11 @@ and 16384 tokens, the 8192-token prefill (int8 TOPS of the MFMA product
 kernel, timed apart from the quantisation kernel), the GLU
 mixer at M=1 (one call, and one step through 128 mixers) and M=4096, the
 batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, and, as
-context, a plain 2 GiB device copy and the vendor's dense int8 GEMM at the
-prefill shape.  `roofline` is for the headline's dominant kernel, timed with
-one HIP event pair on the stream it runs on, around a second pass of the
-timed steps; `cpu_baseline` times the CPU oracle on a bounded sample of the
-headline workload on this host.
+context, a plain 2 GiB device copy and, beside each product of 4096 tokens or
+more, the vendor's dense int8 GEMM on the same shape.  `roofline` is for the
+headline's dominant kernel, timed with one HIP event pair on the stream it
+runs on, around a second pass of the timed steps; `cpu_baseline` times the
+CPU oracle on a bounded sample of the headline workload on this host.
 
 One GPU only: `--gpus N` with N > 1 exits with a message.
 """
@@ -263,8 +263,10 @@ def bench_prefill(torch, bl, wl, M, N, K, steps, warmup, stream):
                               steps, warmup, stream)
     wall_f, ev_f = timed_loop(torch, lambda: bl.bitlinear_forward(x, g, packed, gamma, y=y, ws=ws),
                               steps, warmup, stream)
+    vendor_us = vendor_int8_gemm_us(torch, M, N, K, steps, warmup, stream)
     return dict(M=M, N=N, K=K, int8_ops=ops, quant_us=ev_q * 1e3, product_us=ev_p * 1e3,
                 product_tops=ops / (ev_p * 1e-3) / 1e12, product_frac_i8_peak=ops / (ev_p * 1e-3) / I8_PEAK,
+                context_vendor_int8_gemm_us=vendor_us,
                 forward_us=ev_f * 1e3, forward_tops=ops / (ev_f * 1e-3) / 1e12,
                 forward_us_wall=wall_f * 1e3, forward_bytes=layer_bytes(M, N, K))
 
@@ -353,24 +355,24 @@ def bench_hbm_copy(torch, nbytes, steps):
     return dict(bytes_each_way=nbytes, gbps_read_plus_write=2.0 * nbytes * steps / el / 1e9)
 
 
-def bench_vendor_int8_gemm(torch, M, N, K, steps, warmup, stream):
-    """Context, not this library's path: the vendor's dense int8 GEMM
-    (torch._int_mm, int8 [M, K] x int8 [K, N] -> int32 [M, N]) on the
-    prefill shape, with random int8 operands and B column-major (its faster
+def vendor_int8_gemm_us(torch, M, N, K, steps, warmup, stream):
+    """Context, not this library's path: device time of the vendor's dense
+    int8 GEMM (torch._int_mm, int8 [M, K] x int8 [K, N] -> int32 [M, N]) on
+    the same shape, with random int8 operands and B column-major (its faster
     layout here).  It does no quantisation, no 2-bit unpacking and no
-    rescale."""
+    rescale.  None where the call is not available."""
     if not hasattr(torch, "_int_mm"):
-        return dict(error="torch._int_mm is not available")
+        return None
     gen = torch.Generator(device=DEV)
     gen.manual_seed(0)
     a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=DEV, generator=gen)
     b = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=DEV, generator=gen).t()
     try:
-        wall, ev = timed_loop(torch, lambda: torch._int_mm(a, b), steps, warmup, stream)
-    except (RuntimeError, NotImplementedError) as ex:
-        return dict(error=repr(ex)[:200])
-    ops = 2.0 * M * N * K
-    return dict(M=M, N=N, K=K, us=ev * 1e3, tops=ops / (ev * 1e-3) / 1e12, frac_i8_peak=ops / (ev * 1e-3) / I8_PEAK)
+        _, ev = timed_loop(torch, lambda: torch._int_mm(a, b), steps, warmup, stream)
+    except (RuntimeError, NotImplementedError):
+        return None
+    del a, b
+    return ev * 1e3
 
 
 # --------------------------------------------------------------------------
@@ -483,9 +485,6 @@ def main():
         log("[bench] re-ternarisation of 64 x 2048 x 2048 fp32 master weights")
         secondary["repack_64x2048x2048"] = bench_repack(torch, bl, wl, 64, 2048, 2048, 10, 2, stream)
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
-        log("[bench] context: vendor int8 GEMM at the prefill shape")
-        secondary["context_vendor_int8_gemm_8192x2048x2048"] = bench_vendor_int8_gemm(
-            torch, 8192, 2048, 2048, max(10, args.steps // 2), args.warmup, stream)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
 
