@@ -33,14 +33,22 @@ constexpr int kMaxDevices = 64;
 constexpr int kDefaultCus = 256;
 constexpr int kMaxRowChunks = 4;  // rows up to 4 * 8 * kThreads = 8192 wide stay in registers
 
+// Sum q of the row is needed only in the epilogue: each wave leaves its
+// partial sum in qpart[wave] (made visible by the barrier that follows the
+// quantisation), instead of a block reduction with two more barriers here.
+// The integer sum does not depend on the order.
+__device__ __forceinline__ void put_wave_sum(int32_t v, int32_t* qpart) {
+    v = wave_sum(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) qpart[threadIdx.x / kWave] = v;
+}
+
 // Block-cooperative RMSNorm + absmax int8 of one token row into LDS; the
 // same arithmetic and reduction order as the block-per-row quant_kernel, so
 // the codes agree with it.
 __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__ xr,
                                                     const float* __restrict__ gr, int K, float eps,
                                                     int8_t* __restrict__ qrow, double* dscr,
-                                                    float* fscr, int32_t* iscr, float& scale_out,
-                                                    int32_t& sumq_out) {
+                                                    float* fscr, int32_t* qpart, float& scale_out) {
     const int nchunks = K / 8;
     double ss = 0.0;
     for (int i = threadIdx.x; i < nchunks; i += kThreads) {
@@ -91,9 +99,8 @@ __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__
         }
         *reinterpret_cast<uint2*>(qrow + 8 * i) = make_uint2(packed[0], packed[1]);
     }
-    qsum = block_sum(qsum, iscr);
+    put_wave_sum(qsum, qpart);
     scale_out = scale;
-    sumq_out = qsum;
 }
 
 // The same for rows of at most CPT * kThreads chunks of 8 elements: each
@@ -106,7 +113,7 @@ template <int CPT>
 __device__ __forceinline__ void quantise_row_regs(const uint16_t* __restrict__ xr,
                                                   const float* __restrict__ gr, int K, float eps,
                                                   int8_t* __restrict__ qrow, double* dscr, float* fscr,
-                                                  int32_t* iscr, float& scale_out, int32_t& sumq_out) {
+                                                  int32_t* qpart, float& scale_out) {
     const int nchunks = K / 8;
     uint32_t p[CPT][4];
     float gv[CPT][8];
@@ -171,9 +178,8 @@ __device__ __forceinline__ void quantise_row_regs(const uint16_t* __restrict__ x
         }
         *reinterpret_cast<uint2*>(qrow + 8 * i) = make_uint2(packed[0], packed[1]);
     }
-    qsum = block_sum(qsum, iscr);
+    put_wave_sum(qsum, qpart);
     scale_out = scale;
-    sumq_out = qsum;
 }
 
 template <int MAXM, int S, int U, int LPR, Epilogue EP>
@@ -184,9 +190,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
     extern __shared__ __attribute__((aligned(16))) int8_t qlds[];  // [M][K]
     __shared__ double dscr[kWaves];
     __shared__ float fscr[kWaves];
-    __shared__ int32_t iscr[kWaves];
+    __shared__ int32_t s_qpart[MAXM][kWaves];
     __shared__ float s_scale[MAXM];
-    __shared__ int32_t s_sumq[MAXM];
 
     const int b = blockIdx.y;
     const int M = a.M, N = a.N, K = a.K;
@@ -229,20 +234,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
     const float* G = a.g + (int64_t)b * a.g_stride;
     for (int m = 0; m < M; ++m) {
         float sc;
-        int32_t sq;
         const uint16_t* xr = X + (int64_t)m * K;
         int8_t* qr = qlds + (int64_t)m * K;
         // Rows this instance takes are at most 64 * S * LPR wide (S chunks of
         // 64 weights per lane, LPR lanes per row), so one form is compiled.
         constexpr int kRowChunks = (64 * S * LPR + 8 * kThreads - 1) / (8 * kThreads);
         if constexpr (kRowChunks <= kMaxRowChunks)
-            quantise_row_regs<kRowChunks>(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
+            quantise_row_regs<kRowChunks>(xr, G, K, a.eps, qr, dscr, fscr, s_qpart[m], sc);
         else
-            quantise_row_to_lds(xr, G, K, a.eps, qr, dscr, fscr, iscr, sc, sq);
-        if (threadIdx.x == 0) {
-            s_scale[m] = sc;
-            s_sumq[m] = sq;
-        }
+            quantise_row_to_lds(xr, G, K, a.eps, qr, dscr, fscr, s_qpart[m], sc);
+        if (threadIdx.x == 0) s_scale[m] = sc;
     }
     __syncthreads();
 
@@ -266,7 +267,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
         cs[m] = m < M ? gamma / s_scale[m] : 0.0f;
-        sumq[m] = m < M ? s_sumq[m] : 0;
+        sumq[m] = 0;
+        if (m < M) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) sumq[m] += s_qpart[m][w];
+        }
     }
 
     // 3. products of one buffered set of rows, 4. row sums and epilogue
