@@ -146,6 +146,56 @@ def test_quantize_edge_rows():
     assert np.array_equal(s.cpu().numpy(), s_ref)
 
 
+def _extreme_rows(M, K, seed):
+    """M token rows cycling through magnitudes at the edges of the format:
+    normal rows scaled to 1e15 and 1e18 (squares near the fp32 range), 1e30
+    (the fp32 mean square overflows, so the row quantises to zero on both
+    sides by the same reading), 1e-20 (eps dominates), bf16 subnormals, and
+    an ordinary row."""
+    base = wl.bf16_bits_to_f32(wl.x_normal(M, K, seed=seed)).astype(np.float64)
+    scales = (1e15, 1e18, 1e30, 1e-20, None, 1.0)
+    rng = wl.rng(seed, 7)
+    x = np.empty((M, K), np.uint16)
+    for m in range(M):
+        sc = scales[m % len(scales)]
+        if sc is None:  # subnormal bf16 patterns with random signs
+            mant = rng.integers(1, 128, size=K).astype(np.uint16)
+            x[m] = mant | (rng.integers(0, 2, size=K).astype(np.uint16) << 15)
+        else:
+            x[m] = wl.f32_to_bf16_bits((base[m] * sc).astype(np.float32))
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(6, 256), (72, 256), (4, 2048), (12, 1280)])
+def test_quantize_extreme_magnitudes(M, K):
+    """Every quantisation path (block per row, streaming, and through the
+    fused kernels below) on rows at the edges of bf16 and fp32."""
+    _say("quantize extreme magnitudes", M, K)
+    x = _extreme_rows(M, K, seed=M + K)
+    g = wl.rms_weight(K, "random", seed=2)
+    q_ref, s_ref = gu.orc().rmsnorm_quant(x, g, 1e-6)
+    q, s = bl.bitlinear_quantize(gu.to_dev_bf16(x), gu.to_dev(g), 1e-6)
+    gu.assert_q_parity(q.cpu().numpy(), q_ref, s.cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 64, 2048), (8, 64, 2048), (1, 40, 6912), (130, 64, 512)])
+def test_forward_extreme_magnitudes(M, N, K):
+    """The same rows through the fused decode kernel (1-4 tokens, register
+    and three-pass prologues), the fused few-token kernel (8 tokens) and the
+    quantisation pass + MFMA tiles (130 tokens), against the oracle."""
+    _say("forward extreme magnitudes", M, N, K)
+    x = _extreme_rows(M, K, seed=M + N + K)
+    if M == 1:
+        x[0] = _extreme_rows(2, K, seed=5)[1]  # the 1e18 row
+    W = wl.w_normal(N, K, seed=3)
+    g = wl.rms_weight(K, "random", seed=3)
+    ref = gu.orc().bitlinear(x, g, W)
+    packed, gamma = gu.pack_on_gpu(W)
+    y = bl.bitlinear_forward(gu.to_dev_bf16(x), gu.to_dev(g), packed, gamma).cpu().numpy()
+    q, _ = bl.bitlinear_quantize(gu.to_dev_bf16(x), gu.to_dev(g), 1e-6)
+    gu.assert_y_parity(y, ref["y"], np.all(q.cpu().numpy() == ref["q"], axis=1))
+
+
 # --------------------------------------------------------------------------
 # ternary accumulation (int32, bit-exact)
 # --------------------------------------------------------------------------
