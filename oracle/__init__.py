@@ -37,6 +37,7 @@ _SIGS = {
     "orc_bitlinear_ternary": (None, [_P, _P, _P, _F, _I, _I, _I, _F, _P, _P, _P, _P]),
     "orc_glu": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P]),
     "orc_glu_ternary": (None, [_P, _P, _P, _F, _P, _P, _F, _I, _I, _I, _F, _P, _P]),
+    "orc_bitlinear_backward": (None, [_P, _P, _P, _F, _P, _I, _I, _I, _F, _P, _P, _P]),
 }
 
 
@@ -194,3 +195,19 @@ class Oracle:
                                _ptr(_c(w_down, np.int8)), float(gamma_down), M, D, F,
                                float(eps), _ptr(y), _ptr(h))
         return dict(y=y, h=h)
+
+    def backward(self, x_bits, g, w, gamma, dy, eps=1e-6):
+        """Straight-through backward of the layer (w ternary [N, K], dy fp32
+        [M, N]) -> dict(dx [M, K], dg [K], dW [N, K]), fp64."""
+        x_bits = _c(x_bits, np.uint16)
+        w = _c(w, np.int8)
+        dy = _c(dy, np.float32)
+        M, K = x_bits.shape
+        N = w.shape[0]
+        assert w.shape == (N, K) and dy.shape == (M, N)
+        dx = np.empty((M, K), np.float64)
+        dg = np.empty(K, np.float64)
+        dW = np.empty((N, K), np.float64)
+        self.h.orc_bitlinear_backward(_ptr(x_bits), _ptr(_c(g, np.float32)), _ptr(w), float(gamma),
+                                      _ptr(dy), M, N, K, float(eps), _ptr(dx), _ptr(dg), _ptr(dW))
+        return dict(dx=dx, dg=dg, dW=dW)

@@ -274,3 +274,80 @@ void orc_glu(const uint16_t* x, const float* g_gu, const float* W_gu,
     free(w_gu);
     free(w_down);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass through BitLinear (straight-through estimator)              */
+/* ------------------------------------------------------------------------ */
+
+/* [ld246, "训练与优化：新的策略"]: the ternary weights and the activation
+ * quantisation are not differentiable, and training passes gradients
+ * through them with the straight-through estimator; [ld246, "融合 BitLinear
+ * 层的创新"]: the training-time layer fuses RMSNorm with the quantisation.
+ * Readings (pages silent on the details):
+ *   - both quantisers are the identity in the backward pass: the forward
+ *     value is y = xq W~^T with xq = q / s (the dequantised activations) and
+ *     W~ = gamma * w, and d xq / d xn = I, d W~ / d W = I (no clipping mask,
+ *     gamma and s held constant);
+ *   - hence, with dy the gradient of the loss with respect to y:
+ *       dxn = dy W~ = gamma * dy w            (ternary add/subtract per n),
+ *       dW  = dy^T xq,
+ *     and the RMSNorm xn = x * r * g, r = (mean(x^2) + eps)^(-1/2), gives
+ *       dg[k]   = sum_m dxn[m][k] * x[m][k] * r[m],
+ *       dx[m][k] = r g[k] dxn[m][k] - x[m][k] r^3 / K * sum_j dxn[m][j] g[j] x[m][j];
+ *   - q and s are the forward's own codes and scales (orc_rmsnorm_quant);
+ *     everything else is fp64. */
+void orc_bitlinear_backward(const uint16_t* x, const float* g, const int8_t* w,
+                            float gamma, const float* dy, int64_t M, int64_t N,
+                            int64_t K, float eps, double* dx, double* dg, double* dW) {
+    int8_t* q = (int8_t*)malloc((size_t)(M * K) + 1);
+    float* s = (float*)malloc((size_t)M * sizeof(float) + 1);
+    double* dxn = (double*)malloc((size_t)(M * K) * sizeof(double) + 1);
+    orc_rmsnorm_quant(x, g, M, K, eps, q, s);
+
+    /* dxn = gamma * dy w: weight +1 adds dy, -1 subtracts it, 0 skips. */
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            double a = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                if (w[n * K + k] == 1)
+                    a += (double)dy[m * N + n];
+                else if (w[n * K + k] == -1)
+                    a -= (double)dy[m * N + n];
+            }
+            dxn[m * K + k] = (double)gamma * a;
+        }
+    }
+
+    /* RMSNorm backward. */
+    for (int64_t k = 0; k < K; ++k) dg[k] = 0.0;
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)orc_bf16_to_float(row[k]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+        double S = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            S += dxn[m * K + k] * (double)g[k] * (double)orc_bf16_to_float(row[k]);
+        for (int64_t k = 0; k < K; ++k) {
+            double xv = (double)orc_bf16_to_float(row[k]);
+            dg[k] += dxn[m * K + k] * xv * r;
+            dx[m * K + k] = r * (double)g[k] * dxn[m * K + k] - xv * r * r * r * S / (double)K;
+        }
+    }
+
+    /* dW = dy^T xq, xq = q / s. */
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            double a = 0.0;
+            for (int64_t m = 0; m < M; ++m)
+                a += (double)dy[m * N + n] * ((double)q[m * K + k] / (double)s[m]);
+            dW[n * K + k] = a;
+        }
+    }
+    free(q);
+    free(s);
+    free(dxn);
+}

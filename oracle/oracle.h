@@ -91,4 +91,11 @@ void orc_glu_ternary(const uint16_t* x, const float* g_gu, const int8_t* w_gu,
                      float gamma_down, int64_t M, int64_t D, int64_t F, float eps,
                      double* y, uint16_t* h_out);
 
+/* Backward pass of BitLinear with the straight-through estimator, from a
+ * ternarised w and its gamma: given dy [M][N] (fp32), writes dx [M][K],
+ * dg [K] and dW [N][K] (fp64).  Readings in oracle.c. */
+void orc_bitlinear_backward(const uint16_t* x, const float* g, const int8_t* w,
+                            float gamma, const float* dy, int64_t M, int64_t N,
+                            int64_t K, float eps, double* dx, double* dg, double* dW);
+
 #endif

@@ -388,6 +388,94 @@ def pin_glu_silu_invariants(orc):
             assert np.all(np.abs(hp[neg]) <= 1e-11 * np.abs(up[neg]))
 
 
+# --------------------------------------------------------------------------
+# backward pass (straight-through estimator)
+# --------------------------------------------------------------------------
+
+def _backward_case(orc, M, N, K, seed, eps=1e-6):
+    x = wl.x_normal(M, K, seed=seed, outlier_frac=0.03, outlier_scale=20.0)
+    g = wl.rms_weight(K, "random", seed=seed)
+    W = wl.w_normal(N, K, seed=seed)
+    gamma = orc.gamma(W)
+    w = orc.ternarize(W, gamma)
+    dy = wl.dy_normal(M, N, seed=seed)
+    return x, g, W, gamma, w, dy, orc.backward(x, g, w, gamma, dy, eps)
+
+
+def pin_backward_vs_autograd(orc):
+    """The gradients equal torch.autograd (fp64, CPU) of the forward written
+    with both quantisers passed straight through:
+    xq = xn + (q/s - xn).detach(), W~ = W + (gamma w - W).detach(),
+    loss = sum((xq @ W~^T) * dy), xn = x r g, r = (mean(x^2) + eps)^-1/2."""
+    import torch
+
+    eps = 1e-6
+    for M, N, K, seed in ((6, 40, 48, 81), (3, 17, 5, 82), (9, 8, 33, 83)):
+        x, g, W, gamma, w, dy, got = _backward_case(orc, M, N, K, seed, eps)
+        q, s = orc.rmsnorm_quant(x, g, eps)
+        f64 = torch.float64
+        xt = torch.tensor(wl.bf16_bits_to_f32(x), dtype=f64, requires_grad=True)
+        gt = torch.tensor(g, dtype=f64, requires_grad=True)
+        Wt = torch.tensor(W, dtype=f64, requires_grad=True)
+        r = torch.rsqrt(xt.pow(2).mean(dim=1, keepdim=True) + float(np.float32(eps)))
+        xn = xt * r * gt
+        xdq = torch.tensor(q.astype(np.float64) / s.astype(np.float64)[:, None])
+        xq = xn + (xdq - xn).detach()
+        Wq = Wt + (float(gamma) * torch.tensor(w, dtype=f64) - Wt).detach()
+        loss = ((xq @ Wq.T) * torch.tensor(dy, dtype=f64)).sum()
+        loss.backward()
+        for name, ref in (("dx", xt.grad), ("dg", gt.grad), ("dW", Wt.grad)):
+            ref = ref.numpy()
+            tol = 1e-11 * max(np.abs(ref).max(), 1e-300)
+            assert np.abs(got[name] - ref).max() <= tol, (name, M, N, K)
+
+
+def pin_backward_scale_invariance(orc):
+    """RMSNorm is invariant to scaling its input (up to eps): doubling x
+    halves dx and leaves dg unchanged, and sum_k x_k dx_k ~ 0 for every row
+    (the gradient is orthogonal to the direction that does not change xn).
+    A one-hot dy[m][n] reaches dxn only through row n of gamma * w."""
+    M, N, K = 5, 24, 64
+    x, g, W, gamma, w, dy, out = _backward_case(orc, M, N, K, 91)
+    x2 = wl.f32_to_bf16_bits(2.0 * wl.bf16_bits_to_f32(x))  # exact
+    out2 = orc.backward(x2, g, w, gamma, dy)
+    assert np.allclose(out2["dx"], 0.5 * out["dx"], rtol=1e-5, atol=1e-5 * np.abs(out["dx"]).max())
+    assert np.allclose(out2["dg"], out["dg"], rtol=1e-5, atol=1e-5 * np.abs(out["dg"]).max())
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    proj = (xf * out["dx"]).sum(axis=1)
+    assert np.all(np.abs(proj) <= 1e-5 * (np.abs(xf * out["dx"]).sum(axis=1) + 1e-300))
+    # one-hot output gradient: with g = 1 and r the row's norm factor,
+    # r * dxn[m] minus its projection on x[m] is dx[m]; the projection
+    # vanishes against x, so dx[m] . v = r gamma w[n] . v for v orthogonal to x[m]
+    m, n = 2, 7
+    e = np.zeros((M, N), np.float32)
+    e[m, n] = 1.0
+    ones = np.ones(K, np.float32)
+    o = orc.backward(x, ones, w, gamma, e)
+    assert np.all(o["dx"][np.arange(M) != m] == 0.0)
+    assert np.all(o["dW"][np.arange(N) != n] == 0.0)
+    v = w[n].astype(np.float64)
+    v = v - (v @ xf[m]) / (xf[m] @ xf[m]) * xf[m]
+    r = 1.0 / math.sqrt((xf[m] ** 2).mean() + float(np.float32(1e-6)))
+    assert math.isclose(o["dx"][m] @ v, r * float(gamma) * (w[n].astype(np.float64) @ v), rel_tol=1e-9)
+
+
+def pin_backward_weight_gradient(orc):
+    """dW is the outer-product sum of dy and the dequantised activations:
+    for a single token it is dy[0][n] * q[0][k] / s[0] exactly (one term);
+    for two tokens it is the sum of the one-token results."""
+    N, K = 12, 32
+    x, g, W, gamma, w, dy, out = _backward_case(orc, 2, N, K, 95)
+    parts = []
+    for m in range(2):
+        o = orc.backward(x[m:m + 1], g, w, gamma, dy[m:m + 1])
+        q, s = orc.rmsnorm_quant(x[m:m + 1], g)
+        one = dy[m].astype(np.float64)[:, None] * (q[0].astype(np.float64) / float(s[0]))[None, :]
+        assert np.array_equal(o["dW"], one)
+        parts.append(one)
+    assert np.allclose(out["dW"], parts[0] + parts[1], rtol=0, atol=1e-15 * np.abs(out["dW"]).max())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -37,6 +37,15 @@ MUTANTS = [
      "double up = z[m * 2 * F + f];\n            double gate = z[m * 2 * F + F + f];"),
     ("glu_sigmoid_not_silu", "double silu = gate / (1.0 + exp(-gate));", "double silu = 1.0 / (1.0 + exp(-gate));"),
     ("bf16_truncates", "double n = rint(ldexp(a, -qe));", "double n = trunc(ldexp(a, -qe));"),
+    ("bwd_norm_term_sign", "dx[m * K + k] = r * (double)g[k] * dxn[m * K + k] - xv", "dx[m * K + k] = r * (double)g[k] * dxn[m * K + k] + xv"),
+    ("bwd_norm_drops_r_cubed", "xv * r * r * r * S / (double)K", "xv * r * S / (double)K"),
+    ("bwd_dg_drops_r", "dg[k] += dxn[m * K + k] * xv * r;", "dg[k] += dxn[m * K + k] * xv;"),
+    ("bwd_dw_ignores_scale", "((double)q[m * K + k] / (double)s[m])", "(double)q[m * K + k]"),
+    ("bwd_dxn_sign_swapped", "a -= (double)dy[m * N + n];", "a += (double)dy[m * N + n];"),
+    ("bwd_dxn_drops_gamma", "dxn[m * K + k] = (double)gamma * a;", "dxn[m * K + k] = a;"),
+    ("bwd_sum_drops_gain", "S += dxn[m * K + k] * (double)g[k] * (double)orc_bf16_to_float(row[k]);",
+     "S += dxn[m * K + k] * (double)orc_bf16_to_float(row[k]);"),
+    ("bwd_dw_transposed_token", "a += (double)dy[m * N + n] * ((double)q[m * K + k]", "a += (double)dy[((m + 1) % M) * N + n] * ((double)q[m * K + k]"),
 ]
 
 

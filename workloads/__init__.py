@@ -6,13 +6,13 @@ them to the storage types; it holds none of the method's arithmetic.
 
 Generator: NumPy's PCG64 seeded with SeedSequence([seed, stream]), one
 stream per tensor (x = 0, outlier positions = 1, W = 2, second W = 3, RMSNorm
-weights = 4), so every tensor is reproducible on its own.  The pages train on
+weights = 4, output gradient = 5), so every tensor is reproducible on its own.  The pages train on
 a text corpus that is not available; these draws stand in for the layer
 activations and master weights at the pages' model widths.
 """
 import numpy as np
 
-STREAM_X, STREAM_OUTLIER, STREAM_W, STREAM_W2, STREAM_G = 0, 1, 2, 3, 4
+STREAM_X, STREAM_OUTLIER, STREAM_W, STREAM_W2, STREAM_G, STREAM_DY = 0, 1, 2, 3, 4, 5
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -53,6 +53,12 @@ def x_student_t(M, K, df=3, seed=0):
 def w_normal(N, K, sigma=0.02, seed=0, stream=STREAM_W):
     """fp32 [N, K] master weights ~ N(0, sigma^2)."""
     return (rng(seed, stream).standard_normal((N, K)) * sigma).astype(np.float32)
+
+
+def dy_normal(M, N, seed=0, scale=1.0):
+    """fp32 [M, N] ~ N(0, scale^2): the gradient of a loss with respect to
+    the layer output, for the backward pass."""
+    return (rng(seed, STREAM_DY).standard_normal((M, N)) * scale).astype(np.float32)
 
 
 def rms_weight(K, kind="ones", seed=0):
