@@ -64,6 +64,8 @@ _SIGNATURES = {
     "bitlinear_glu_hidden": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P, _INT]),
     "bitlinear_quantize": (_INT, [_P, _P, _I, _I, _F, _P, _P, _P]),
     "bitlinear_ternary_matmul_i32": (_INT, [_P, _P, _I, _I, _I, _P, _P, _S, _P, _INT]),
+    "bitlinear_backward_workspace_bytes": (_S, [_I, _I, _I]),
+    "bitlinear_backward": (_INT, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _S, _P]),
 }
 
 _lib = None
@@ -342,6 +344,41 @@ def bitlinear_glu_forward_batched(x, rms_w_gu, packed_gu, gamma_gu, rms_w_down, 
                                                M, D, F, float(eps), _ptr(y), _ptr(ws), nbytes,
                                                _stream(stream)))
     return y
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def bitlinear_backward_workspace_bytes(M, N, K):
+    return lib().bitlinear_backward_workspace_bytes(M, N, K)
+
+
+def bitlinear_backward(x, rms_weight, packed, gamma, dy, eps=1e-6, dx=None, dg=None, dW=None, ws=None,
+                       stream=None):
+    """Straight-through backward: x bf16 [M, K], rms_weight [K], packed
+    [N, K/4], gamma [1], dy fp32 [M, N] -> (dx [M, K], dg [K], dW [N, K]),
+    all fp32."""
+    _dev(x, "x", _BF16, 2)
+    _dev(rms_weight, "rms_weight", (torch.float32,), 1)
+    _dev(packed, "packed", (torch.uint8,), 2)
+    _dev(gamma, "gamma", (torch.float32,), 1)
+    _dev(dy, "dy", (torch.float32,), 2)
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K or dy.shape != (M, N) or rms_weight.shape != (K,):
+        raise ValueError("backward shapes disagree with x")
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    if dg is None:
+        dg = torch.empty(K, dtype=torch.float32, device=x.device)
+    if dW is None:
+        dW = torch.empty((N, K), dtype=torch.float32, device=x.device)
+    ws, nbytes = _workspace(bitlinear_backward_workspace_bytes(M, N, K), ws, x.device)
+    _check(lib().bitlinear_backward(_ptr(x), _ptr(rms_weight), _ptr(packed), _ptr(gamma), _ptr(dy), M, N, K,
+                                    float(eps), _ptr(dx), _ptr(dg), _ptr(dW), _ptr(ws), nbytes,
+                                    _stream(stream)))
+    return dx, dg, dW
 
 
 def bitlinear_glu_hidden(x, rms_w_gu, packed_gu, gamma_gu, eps=1e-6, h=None, ws=None, stream=None,

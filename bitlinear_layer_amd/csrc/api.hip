@@ -471,4 +471,38 @@ int bitlinear_ternary_matmul_i32(const int8_t* q, const uint8_t* packed, int64_t
     return run_product(act, packed, nullptr, M, N, K, 1, acc, bl::Epilogue::kI32, kernel, st);
 }
 
+
+size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || K > BITLINEAR_MAX_K || M > BITLINEAR_MAX_DIM ||
+        N > BITLINEAR_MAX_DIM)
+        return 0;
+    return bl::backward_workspace_bytes(M, N, K);
+}
+
+int bitlinear_backward(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                       const float* gamma, const float* dy, int64_t M, int64_t N, int64_t K, float eps,
+                       float* dx, float* dg, float* dW, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_rows(M, "M"));
+    TRY(check_rows(N, "N"));
+    TRY(check_k(K, "K"));
+    TRY(check_eps(eps));
+    CHECK(M * K <= kMaxElems && N * K <= kMaxElems && M * N <= kMaxElems, BITLINEAR_ERR_INVALID_ARG,
+          "matrix too large");
+    CHECK_PTR(rms_weight);
+    CHECK_SCALAR(gamma);
+    CHECK_PTR(dg);
+    if (M > 0) {
+        CHECK_PTR(x);
+        CHECK_PTR(dx);
+    }
+    if (N > 0) {
+        CHECK_PTR(packed);
+        CHECK_PTR(dW);
+    }
+    if (M > 0 && N > 0) CHECK_PTR(dy);
+    TRY(check_ws(ws, ws_bytes, bl::backward_workspace_bytes(M, N, K)));
+    bl::BackwardArgs a{x, rms_weight, packed, gamma, dy, M, N, K, eps, dx, dg, dW, ws};
+    return hip_status(bl::launch_backward(a, as_stream(stream)), "backward launch");
+}
+
 }  // extern "C"

@@ -1,0 +1,402 @@
+// backward.hip -- gradients of the BitLinear layer (straight-through estimator).
+//
+// [ld246, "训练与优化：新的策略"]: training passes gradients straight through
+// the ternary weights and the activation quantiser; [ld246, "融合 BitLinear
+// 层的创新"]: the training-time layer fuses RMSNorm with the quantisation.
+// Reading: both quantisers are the identity in the backward pass, gamma and s
+// held constant.  For the forward value y = (q / s) (gamma w)^T and the
+// output gradient dy:
+//   dxn = gamma * dy w,        dW = dy^T (q / s),
+//   dg[k]    = sum_m dxn[m][k] x[m][k] r[m],
+//   dx[m][k] = r g[k] dxn[m][k] - x[m][k] r^3 / K * sum_j dxn[m][j] g[j] x[m][j],
+// with r = (mean(x^2) + eps)^-1/2.  Nothing is kept from the forward call: q
+// and s are recomputed by the forward's own quantisation kernel (the same
+// bits), r from x.
+//
+// Both products are dense floating-point contractions and run on the bf16
+// matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Their
+// operands are laid out with the reduction index contiguous and zero-padded
+// to a multiple of 64:
+//   dxn [M][K] = gamma * A1 [M][Np] . wT [K][Np]^T,   A1 = bf16(dy),  wT = w^T
+//   dW  [N][K] =         A2 [N][Mp] . qT [K][Mp]^T,   A2 = bf16(dy / s)^T, qT = q^T
+// w and q are exact in bf16, so the only roundings besides the fp32
+// accumulation are those of dy and dy / s to bf16.
+//
+// Kernels: dy_prep (A1 and A2 from one read of dy), q_transpose, w_transpose
+// (2-bit codes to bf16), the NT GEMM, norm_backward (dx in place over dxn,
+// per-block dg partials) and dg_reduce (fixed order, fp64).
+#include "device_common.h"
+#include "launch.h"
+
+namespace bl {
+namespace {
+
+constexpr int kT = 64;          // transpose tile edge
+constexpr int kPrepThreads = 256;
+constexpr uint32_t kBf16One = 0x3F80u;
+
+// ---------------------------------------------------------------------------
+// Operand preparation
+// ---------------------------------------------------------------------------
+
+// One 64 x 64 tile of dy: A1[m][n] = bf16(dy[m][n]) for m < M, n < Np (zero
+// past N); A2[n][m] = bf16(dy[m][n] / s[m]) for n < N, m < Mp (zero past M).
+__global__ __launch_bounds__(kPrepThreads) void dy_prep_kernel(const float* __restrict__ dy,
+                                                               const float* __restrict__ s, int M, int N,
+                                                               int Mp, int Np, uint32_t* __restrict__ A1,
+                                                               uint32_t* __restrict__ A2) {
+    __shared__ float tile[kT][kT + 1];
+    __shared__ float sinv[kT];
+    const int m0 = blockIdx.x * kT, n0 = blockIdx.y * kT;
+    const int t = threadIdx.x;
+    if (t < kT) sinv[t] = (m0 + t < M) ? s[m0 + t] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kT / 4; ++i) {
+        const int r = t / kT + 4 * i, c = t % kT;
+        const int m = m0 + r, n = n0 + c;
+        tile[r][c] = (m < M && n < N) ? dy[(int64_t)m * N + n] : 0.0f;
+    }
+    __syncthreads();
+    // A1 rows m, pairs of columns
+#pragma unroll
+    for (int i = 0; i < kT / 8; ++i) {
+        const int r = t / 32 + 8 * i, c = 2 * (t % 32);
+        const int m = m0 + r;
+        if (m < M) {
+            const uint32_t lo = f32_to_bf16_bits(tile[r][c]), hi = f32_to_bf16_bits(tile[r][c + 1]);
+            A1[((int64_t)m * Np + n0 + c) / 2] = lo | (hi << 16);
+        }
+    }
+    // A2 rows n, pairs of tokens; dy / s is an IEEE fp32 division
+#pragma unroll
+    for (int i = 0; i < kT / 8; ++i) {
+        const int c = t / 32 + 8 * i, r = 2 * (t % 32);
+        const int n = n0 + c;
+        if (n < N) {
+            const uint32_t lo = f32_to_bf16_bits(tile[r][c] / sinv[r]);
+            const uint32_t hi = f32_to_bf16_bits(tile[r + 1][c] / sinv[r + 1]);
+            A2[((int64_t)n * Mp + m0 + r) / 2] = lo | (hi << 16);
+        }
+    }
+}
+
+// qT[k][m] = bf16(q[m][k]) for k < K, m < Mp (zero past M).  K % 16 == 0.
+__global__ __launch_bounds__(kPrepThreads) void q_transpose_kernel(const int8_t* __restrict__ q, int M, int K,
+                                                                   int Mp, uint32_t* __restrict__ qT) {
+    __shared__ int8_t tile[kT][kT + 4];
+    const int m0 = blockIdx.x * kT, k0 = blockIdx.y * kT;
+    const int t = threadIdx.x;
+    {
+        const int r = t / 4, ch = t % 4;  // 64 rows x 4 chunks of 16 codes
+        const int m = m0 + r, k = k0 + 16 * ch;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M && k < K) v = *reinterpret_cast<const uint4*>(q + (int64_t)m * K + k);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[r][16 * ch]);
+        dst[0] = v.x;
+        dst[1] = v.y;
+        dst[2] = v.z;
+        dst[3] = v.w;
+    }
+    __syncthreads();
+    // int8 -> fp32 is exact and |q| <= 128 has at most 8 significant bits, so
+    // the top half of the fp32 pattern is the bf16 value.
+#pragma unroll
+    for (int i = 0; i < kT / 8; ++i) {
+        const int c = t / 32 + 8 * i, r = 2 * (t % 32);
+        const int k = k0 + c;
+        if (k < K) {
+            const uint32_t lo = __float_as_uint((float)tile[r][c]) >> 16;
+            const uint32_t hi = __float_as_uint((float)tile[r + 1][c]) >> 16;
+            qT[((int64_t)k * Mp + m0 + r) / 2] = lo | (hi << 16);
+        }
+    }
+}
+
+// wT[k][n] = w[n][k] in bf16 (-1, 0, +1) for k < K, n < Np (zero past N),
+// from the packed rows [N][K/4]: weight j of a 16-weight group sits in byte
+// j % 4 of the group's word, bits 2 (j / 4) + 1 .. 2 (j / 4), as code w + 1.
+__global__ __launch_bounds__(kPrepThreads) void w_transpose_kernel(const uint32_t* __restrict__ packed, int N,
+                                                                   int K, int Np, uint32_t* __restrict__ wT) {
+    __shared__ uint16_t tile[kT][kT + 2];
+    const int n0 = blockIdx.x * kT, k0 = blockIdx.y * kT;
+    const int t = threadIdx.x;
+    {
+        const int r = t / 4, wi = t % 4;  // 64 rows x 4 words of 16 weights
+        const int n = n0 + r, k = k0 + 16 * wi;
+        uint32_t word = 0x55555555u;      // code 1 everywhere: weight 0
+        if (n < N && k < K) word = packed[(int64_t)n * (K / 16) + k / 16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int code = (word >> (8 * (j & 3) + 2 * (j >> 2))) & 3;
+            tile[r][16 * wi + j] = code == 1 ? 0u : (code == 0 ? (uint16_t)(0x8000u | kBf16One) : (uint16_t)kBf16One);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kT / 8; ++i) {
+        const int c = t / 32 + 8 * i, r = 2 * (t % 32);
+        const int k = k0 + c;
+        if (k < K) wT[((int64_t)k * Np + n0 + r) / 2] = (uint32_t)tile[r][c] | ((uint32_t)tile[r + 1][c] << 16);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// C[rows][cols] = alpha * A[rows][R] . B[cols][R]^T on the bf16 matrix cores.
+// Block tile 128 x 128, four waves as 2 x 2, each a 64 x 64 tile of 32 x 32
+// fragments.  R advances in stages of 64, double-buffered in LDS through
+// registers: the next stage's global loads are in flight while the current
+// one is multiplied.  Operand pairing: lane l of A supplies row l % 32 and
+// lane l of B column l % 32, both with the same eight reduction indices
+// 8 (l / 32) + 0..7 of a 16-wide step; accumulator element v of lane l holds
+// C[(v % 4) + 8 (v / 4) + 4 (l / 32)][l % 32].  R % 64 == 0 (zero-padded
+// operands); rows and cols are arbitrary (loads clamped, stores masked).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGT = 128;          // block tile edge
+constexpr int kGK = 64;           // reduction per stage (bf16 elements)
+constexpr int kGPitch = kGK + 8;  // bf16 per LDS row: 144 bytes, 16-byte reads of 8 rows hit distinct banks
+constexpr int kGThreads = 256;
+
+struct GemmArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    float* C;
+    const float* alpha;  // device scalar, or nullptr for 1
+    int rows, cols, R;
+};
+
+__global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kGT * kGPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGT * kGPitch];
+    const int ntc = (g.cols + kGT - 1) / kGT;
+    const int tr = blockIdx.x / ntc, tc = blockIdx.x % ntc;
+    const int row0 = tr * kGT, col0 = tc * kGT;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    const int wm = wave / 2, wn = wave % 2;
+
+    // global -> register staging: 4 x 16 bytes of A and of B per thread
+    // (rows t / 8 + 32 i, 16-byte chunk t % 8 of the stage's 128 bytes)
+    const int srow = t / 8, sch = t % 8;
+    const uint16_t* abase = g.A + 8 * sch;
+    const uint16_t* bbase = g.B + 8 * sch;
+    int64_t aoff0 = (int64_t)min(row0 + srow, g.rows - 1) * g.R;
+    int64_t aoff1 = (int64_t)min(row0 + srow + 32, g.rows - 1) * g.R;
+    int64_t aoff2 = (int64_t)min(row0 + srow + 64, g.rows - 1) * g.R;
+    int64_t aoff3 = (int64_t)min(row0 + srow + 96, g.rows - 1) * g.R;
+    int64_t boff0 = (int64_t)min(col0 + srow, g.cols - 1) * g.R;
+    int64_t boff1 = (int64_t)min(col0 + srow + 32, g.cols - 1) * g.R;
+    int64_t boff2 = (int64_t)min(col0 + srow + 64, g.cols - 1) * g.R;
+    int64_t boff3 = (int64_t)min(col0 + srow + 96, g.cols - 1) * g.R;
+    const int lds0 = srow * kGPitch + 8 * sch;
+    constexpr int kLdsStep = 32 * kGPitch;
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define BWD_LOAD_STAGE(st)                                                                  \
+    do {                                                                                    \
+        const int64_t o_ = (int64_t)(st) * kGK;                                             \
+        ra0 = *reinterpret_cast<const uint4*>(abase + aoff0 + o_);                          \
+        ra1 = *reinterpret_cast<const uint4*>(abase + aoff1 + o_);                          \
+        ra2 = *reinterpret_cast<const uint4*>(abase + aoff2 + o_);                          \
+        ra3 = *reinterpret_cast<const uint4*>(abase + aoff3 + o_);                          \
+        rb0 = *reinterpret_cast<const uint4*>(bbase + boff0 + o_);                          \
+        rb1 = *reinterpret_cast<const uint4*>(bbase + boff1 + o_);                          \
+        rb2 = *reinterpret_cast<const uint4*>(bbase + boff2 + o_);                          \
+        rb3 = *reinterpret_cast<const uint4*>(bbase + boff3 + o_);                          \
+    } while (0)
+#define BWD_STORE_STAGE(buf)                                                                \
+    do {                                                                                    \
+        *reinterpret_cast<uint4*>(&As[buf][lds0]) = ra0;                                    \
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + kLdsStep]) = ra1;                         \
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + 2 * kLdsStep]) = ra2;                     \
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + 3 * kLdsStep]) = ra3;                     \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0]) = rb0;                                    \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + kLdsStep]) = rb1;                         \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 2 * kLdsStep]) = rb2;                     \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 3 * kLdsStep]) = rb3;                     \
+    } while (0)
+
+    f32x16 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};
+    const int nst = g.R / kGK;
+    const int afrag = (wm * 64 + (lane & 31)) * kGPitch + 8 * (lane >> 5);
+    const int bfrag = (wn * 64 + (lane & 31)) * kGPitch + 8 * (lane >> 5);
+    if (nst > 0) {
+        BWD_LOAD_STAGE(0);
+        BWD_STORE_STAGE(0);
+        __syncthreads();
+    }
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nst) BWD_LOAD_STAGE(st + 1);
+#pragma unroll
+        for (int ks = 0; ks < kGK / 16; ++ks) {
+            const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + 16 * ks]));
+            const bf16x8 a1 = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + 32 * kGPitch + 16 * ks]));
+            const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[buf][bfrag + 16 * ks]));
+            const bf16x8 b1 = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4*>(&Bs[buf][bfrag + 32 * kGPitch + 16 * ks]));
+            acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
+            acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
+            acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
+            acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
+        }
+        if (st + 1 < nst) BWD_STORE_STAGE(buf ^ 1);
+        __syncthreads();
+    }
+#undef BWD_LOAD_STAGE
+#undef BWD_STORE_STAGE
+
+    const float alpha = g.alpha ? *g.alpha : 1.0f;
+    auto store_frag = [&](const f32x16& acc, int i, int j) {
+        const int col = col0 + wn * 64 + j * 32 + (lane & 31);
+        if (col >= g.cols) return;
+        const int rbase = row0 + wm * 64 + i * 32 + 4 * (lane >> 5);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = rbase + (v % 4) + 8 * (v / 4);
+            if (row < g.rows) g.C[(int64_t)row * g.cols + col] = alpha * acc[v];
+        }
+    };
+    store_frag(acc00, 0, 0);
+    store_frag(acc01, 0, 1);
+    store_frag(acc10, 1, 0);
+    store_frag(acc11, 1, 1);
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm backward.  A block owns kNormRows rows.  Phase 1 (a wave per row):
+// ss = sum x^2 and S = sum dxn g x in fp64, r = (ss / K + eps)^-1/2 and
+// c = r^3 S / K.  Phase 2 (threads over columns, four each): dx = r g dxn -
+// x c written over dxn, and the block's partial dg[k] = sum_m dxn x r.
+// ---------------------------------------------------------------------------
+constexpr int kNormRows = 32;
+constexpr int kNormThreads = 256;
+
+__global__ __launch_bounds__(kNormThreads) void norm_backward_kernel(const uint16_t* __restrict__ x,
+                                                                     const float* __restrict__ gw, int M, int K,
+                                                                     float eps, float* __restrict__ dxio,
+                                                                     float* __restrict__ partial) {
+    __shared__ float s_r[kNormRows], s_c[kNormRows];
+    const int m0 = blockIdx.x * kNormRows;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    constexpr int kWaves = kNormThreads / kWave;
+    for (int rr = wave; rr < kNormRows; rr += kWaves) {
+        const int m = m0 + rr;
+        if (m >= M) break;
+        const uint16_t* xr = x + (int64_t)m * K;
+        const float* dr = dxio + (int64_t)m * K;
+        double ss = 0.0, S = 0.0;
+        for (int k = 4 * lane; k < K; k += 4 * kWave) {
+            const uint2 xv = *reinterpret_cast<const uint2*>(xr + k);
+            const float4 d = *reinterpret_cast<const float4*>(dr + k);
+            const float4 gv = *reinterpret_cast<const float4*>(gw + k);
+            const float xs[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+            const float ds[4] = {d.x, d.y, d.z, d.w};
+            const float gs[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ss += (double)xs[j] * (double)xs[j];
+                S += (double)ds[j] * (double)gs[j] * (double)xs[j];
+            }
+        }
+        ss = wave_sum(ss);
+        S = wave_sum(S);
+        if (lane == 0) {
+            const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+            s_r[rr] = (float)r;
+            s_c[rr] = (float)(r * r * r * S / (double)K);
+        }
+    }
+    __syncthreads();
+    const int mend = min(M - m0, kNormRows);
+    for (int k = 4 * t; k < K; k += 4 * kNormThreads) {
+        const float4 gv = *reinterpret_cast<const float4*>(gw + k);
+        float dg0 = 0.f, dg1 = 0.f, dg2 = 0.f, dg3 = 0.f;
+        for (int rr = 0; rr < mend; ++rr) {
+            const int64_t off = (int64_t)(m0 + rr) * K + k;
+            const uint2 xv = *reinterpret_cast<const uint2*>(x + off);
+            const float4 d = *reinterpret_cast<const float4*>(dxio + off);
+            const float r = s_r[rr], c = s_c[rr];
+            const float x0 = bf16_lo(xv.x), x1 = bf16_hi(xv.x), x2 = bf16_lo(xv.y), x3 = bf16_hi(xv.y);
+            float4 o;
+            o.x = r * gv.x * d.x - x0 * c;
+            o.y = r * gv.y * d.y - x1 * c;
+            o.z = r * gv.z * d.z - x2 * c;
+            o.w = r * gv.w * d.w - x3 * c;
+            *reinterpret_cast<float4*>(dxio + off) = o;
+            dg0 += d.x * x0 * r;
+            dg1 += d.y * x1 * r;
+            dg2 += d.z * x2 * r;
+            dg3 += d.w * x3 * r;
+        }
+        *reinterpret_cast<float4*>(partial + (int64_t)blockIdx.x * K + k) = make_float4(dg0, dg1, dg2, dg3);
+    }
+}
+
+// dg[k] = sum over blocks of the partials, in block order, fp64.
+__global__ __launch_bounds__(256) void dg_reduce_kernel(const float* __restrict__ partial, int nparts, int K,
+                                                        float* __restrict__ dg) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= K) return;
+    double a = 0.0;
+    for (int b = 0; b < nparts; ++b) a += (double)partial[(int64_t)b * K + k];
+    dg[k] = (float)a;
+}
+
+inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int64_t Mp = round_up(M, kT), Np = round_up(N, kT);
+    const int64_t nparts = (M + kNormRows - 1) / kNormRows;
+    return act_stage_bytes(M, K) + (size_t)round_up(M * Np * 2, 256) + (size_t)round_up(N * Mp * 2, 256) +
+           (size_t)round_up(K * Mp * 2, 256) + (size_t)round_up(K * Np * 2, 256) +
+           (size_t)round_up(nparts * K * 4, 256);
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t Mp = round_up(M, kT), Np = round_up(N, kT);
+    const int64_t nparts = (M + kNormRows - 1) / kNormRows;
+    char* base = static_cast<char*>(a.ws);
+    ActStage act = act_stage_carve(base, M, K);
+    base += act_stage_bytes(M, K);
+    uint16_t* A1 = reinterpret_cast<uint16_t*>(base);
+    base += round_up(M * Np * 2, 256);
+    uint16_t* A2 = reinterpret_cast<uint16_t*>(base);
+    base += round_up(N * Mp * 2, 256);
+    uint16_t* qT = reinterpret_cast<uint16_t*>(base);
+    base += round_up(K * Mp * 2, 256);
+    uint16_t* wT = reinterpret_cast<uint16_t*>(base);
+    base += round_up(K * Np * 2, 256);
+    float* partial = reinterpret_cast<float*>(base);
+
+    hipError_t e;
+    if (M > 0) {
+        e = launch_quant(a.x, a.g, M, M, (int)K, a.eps, act, stream);
+        if (e != hipSuccess) return e;
+        if (Np > 0) {
+            dy_prep_kernel<<<dim3(cdiv(Mp, kT), cdiv(Np, kT)), kPrepThreads, 0, stream>>>(
+                a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint32_t*>(A1),
+                reinterpret_cast<uint32_t*>(A2));
+            w_transpose_kernel<<<dim3(cdiv(Np, kT), cdiv(K, kT)), kPrepThreads, 0, stream>>>(
+                reinterpret_cast<const uint32_t*>(a.packed), (int)N, (int)K, (int)Np, reinterpret_cast<uint32_t*>(wT));
+        }
+        q_transpose_kernel<<<dim3(cdiv(Mp, kT), cdiv(K, kT)), kPrepThreads, 0, stream>>>(
+            act.q, (int)M, (int)K, (int)Mp, reinterpret_cast<uint32_t*>(qT));
+        GemmArgs g1{A1, wT, a.dx, a.gamma, (int)M, (int)K, (int)Np};
+        bwd_gemm_kernel<<<cdiv(M, kGT) * cdiv(K, kGT), kGThreads, 0, stream>>>(g1);
+        norm_backward_kernel<<<(unsigned)nparts, kNormThreads, 0, stream>>>(a.x, a.g, (int)M, (int)K, a.eps,
+                                                                          a.dx, partial);
+    }
+    if (N > 0) {
+        GemmArgs g2{A2, qT, a.dW, nullptr, (int)N, (int)K, (int)Mp};
+        bwd_gemm_kernel<<<cdiv(N, kGT) * cdiv(K, kGT), kGThreads, 0, stream>>>(g2);
+    }
+    dg_reduce_kernel<<<cdiv(K, 256), 256, 0, stream>>>(partial, (int)nparts, (int)K, a.dg);
+    return hipGetLastError();
+}
+
+}  // namespace bl

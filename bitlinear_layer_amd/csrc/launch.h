@@ -106,4 +106,24 @@ hipError_t launch_decode(const DecodeArgs& a, Epilogue ep, hipStream_t stream);
 bool decode_few_supported(int M, int K);
 hipError_t launch_decode_few(const DecodeArgs& a, hipStream_t stream);
 
+// --- backward (straight-through estimator) -------------------------------------
+// x bf16 [M][K], g fp32 [K], packed [N][K/4], gamma (device scalar), dy fp32
+// [M][N] -> dx fp32 [M][K], dg fp32 [K], dW fp32 [N][K]; ws of
+// backward_workspace_bytes(M, N, K) bytes, 256-byte aligned.
+struct BackwardArgs {
+    const uint16_t* x;
+    const float* g;
+    const uint8_t* packed;
+    const float* gamma;
+    const float* dy;
+    int64_t M, N, K;
+    float eps;
+    float* dx;
+    float* dg;
+    float* dW;
+    void* ws;
+};
+size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+
 }  // namespace bl

@@ -281,6 +281,35 @@ int bitlinear_ternary_matmul_i32(const int8_t* q, const uint8_t* packed, int64_t
                                  int64_t N, int64_t K, int32_t* acc, void* ws,
                                  size_t ws_bytes, void* stream, int kernel);
 
+/* ---------------------------------------------------------------------------
+ * Backward pass (training)
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes for bitlinear_backward (0 for an invalid shape). */
+size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Gradients of the layer with the straight-through estimator ([ld246,
+ * "训练与优化：新的策略"]: gradients pass straight through the ternary weights
+ * and the activation quantiser; [ld246, "融合 BitLinear 层的创新"]: RMSNorm and
+ * quantisation fused, activations read once).  Reading: both quantisers are
+ * the identity in the backward, gamma and s held constant, so for
+ * y = (q / s) (gamma w)^T:
+ *   dxn = gamma dy w,  dW = dy^T (q / s),
+ *   dg[k] = sum_m dxn[m][k] x[m][k] r[m],
+ *   dx[m][k] = r g[k] dxn[m][k] - x[m][k] r^3 / K sum_j dxn[m][j] g[j] x[m][j],
+ *   r = (mean_k x[m][k]^2 + eps)^-1/2.
+ * Inputs (device): x bf16 [M][K], rms_weight fp32 [K], packed [N][K/4] and
+ * gamma (fp32 scalar) of the forward, dy fp32 [M][N].  Outputs (device):
+ * dx fp32 [M][K], dg fp32 [K], dW fp32 [N][K] (the gradient with respect to
+ * the fp32 master weights).  q and s are recomputed from x with the
+ * forward's own kernel, so they are the forward's bits.  The two products
+ * run in bf16 with fp32 accumulation: dy and dy / s are rounded to bf16
+ * (nearest even); w and q are exact.  M = 0 gives dg = 0 and dW = 0; N = 0
+ * gives dx = 0 and dg = 0.  Deterministic (fixed reduction orders). */
+int bitlinear_backward(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                       const float* gamma, const float* dy, int64_t M, int64_t N, int64_t K, float eps,
+                       float* dx, float* dg, float* dW, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
