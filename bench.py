@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK = 8.0e12        # B/s, MI355X HBM3E
 I8_PEAK = 5.0e15         # dense int8 MFMA ops/s, MI355X
+BF16_PEAK = 2.5e15       # dense bf16 MFMA flops/s, MI355X
 DEV = "cuda:0"
 
 
@@ -271,6 +272,31 @@ def bench_prefill(torch, bl, wl, M, N, K, steps, warmup, stream):
                 forward_us_wall=wall_f * 1e3, forward_bytes=layer_bytes(M, N, K))
 
 
+def bench_backward(torch, bl, wl, M, N, K, steps, warmup, stream):
+    """Straight-through backward of one layer (dx, dg, dW from x, the packed
+    weights and dy).  Its two gradient products are bf16 contractions of
+    2*M*N*K flops each; the algorithmic bytes are x, dy, g, the packed
+    weights and gamma read once and dx, dg, dW written once."""
+    x = torch.from_numpy(wl.x_student_t(M, K, seed=0).view("int16")).to(DEV)
+    g = torch.ones(K, dtype=torch.float32, device=DEV)
+    packed, gamma = bl.bitlinear_pack_weights(torch.from_numpy(wl.w_normal(N, K, seed=0)).to(DEV))
+    dy = torch.from_numpy(wl.dy_normal(M, N, seed=0)).to(DEV)
+    dx = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    dg = torch.empty(K, dtype=torch.float32, device=DEV)
+    dW = torch.empty((N, K), dtype=torch.float32, device=DEV)
+    ws = torch.empty(bl.bitlinear_backward_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    wall, ev = timed_loop(torch, lambda: bl.bitlinear_backward(x, g, packed, gamma, dy, dx=dx, dg=dg, dW=dW, ws=ws),
+                          steps, warmup, stream)
+    flops = 4.0 * M * N * K
+    nbytes = 2 * M * K + 4 * M * N + 4 * K + N * K // 4 + 4 + 4 * M * K + 4 * K + 4 * N * K
+    del x, g, packed, gamma, dy, dx, dg, dW, ws
+    torch.cuda.empty_cache()
+    return dict(M=M, N=N, K=K, flops=flops, algorithmic_bytes=nbytes, backward_us=ev * 1e3,
+                backward_us_wall=wall * 1e3, tflops=flops / (ev * 1e-3) / 1e12,
+                frac_bf16_peak=flops / (ev * 1e-3) / BF16_PEAK,
+                roofline_us=max(flops / BF16_PEAK, nbytes / HBM_PEAK) * 1e6)
+
+
 def bench_glu(torch, bl, wl, M, D, F, steps, warmup, stream):
     x = torch.from_numpy(wl.x_normal(M, D, seed=0).view("int16")).to(DEV)
     g_gu = torch.ones(D, dtype=torch.float32, device=DEV)
@@ -487,6 +513,9 @@ def main():
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
+        log("[bench] backward (straight-through) 8192 x 2048 x 2048")
+        secondary["backward_8192x2048x2048"] = bench_backward(torch, bl, wl, 8192, 2048, 2048,
+                                                              max(10, args.steps // 2), args.warmup, stream)
 
     cpu = None
     if not args.no_cpu:

@@ -142,135 +142,194 @@ __global__ __launch_bounds__(kPrepThreads) void w_transpose_kernel(const uint32_
 
 // ---------------------------------------------------------------------------
 // C[rows][cols] = alpha * A[rows][R] . B[cols][R]^T on the bf16 matrix cores.
-// Block tile 128 x 128, four waves as 2 x 2, each a 64 x 64 tile of 32 x 32
-// fragments.  R advances in stages of 64, double-buffered in LDS through
-// registers: the next stage's global loads are in flight while the current
-// one is multiplied.  Operand pairing: lane l of A supplies row l % 32 and
-// lane l of B column l % 32, both with the same eight reduction indices
-// 8 (l / 32) + 0..7 of a 16-wide step; accumulator element v of lane l holds
-// C[(v % 4) + 8 (v / 4) + 4 (l / 32)][l % 32].  R % 64 == 0 (zero-padded
-// operands); rows and cols are arbitrary (loads clamped, stores masked).
+// Block tile 256 x 256, eight waves as 2 x 4, each a 128 x 64 tile of 32 x 32
+// fragments (4 x 2): per 16-wide reduction step a wave reads six fragments
+// from LDS for eight MFMAs, 0.75 KiB of LDS per MFMA (a 64 x 64 wave tile
+// needs 1 KiB, which four busy SIMDs cannot get from LDS).  R advances in
+// stages of 64, double-buffered in LDS through registers: the next stage's
+// global loads are in flight while the current one is multiplied.  Operand
+// pairing: lane l of A supplies row l % 32 and lane l of B column l % 32,
+// both with the same eight reduction indices 8 (l / 32) + 0..7 of a 16-wide
+// step; accumulator element v of lane l holds C[(v % 4) + 8 (v / 4) +
+// 4 (l / 32)][l % 32].  R % 64 == 0 (zero-padded operands); rows and cols
+// are arbitrary (loads clamped, stores masked).
+//
+// When the output has fewer tiles than the chip has compute units, the
+// reduction is split over `splits` blocks per tile (whole stages each); split
+// s writes its fp32 partial to P + s * rows * cols and split_reduce adds the
+// partials in split order and scales by alpha.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGT = 128;          // block tile edge
+constexpr int kGT = 256;          // block tile edge
 constexpr int kGK = 64;           // reduction per stage (bf16 elements)
 constexpr int kGPitch = kGK + 8;  // bf16 per LDS row: 144 bytes, 16-byte reads of 8 rows hit distinct banks
-constexpr int kGThreads = 256;
+constexpr int kGWM = 2, kGWN = 4; // wave grid
+constexpr int kGThreads = kGWM * kGWN * kWave;
+constexpr int kGFM = kGT / kGWM / 32, kGFN = kGT / kGWN / 32;  // fragments per wave: 4 x 2
+constexpr int kGLoads = kGT * kGK * 2 / 16 / kGThreads;          // 16-byte loads per thread per operand: 4
+constexpr int kMaxSplits = 8;
 
 struct GemmArgs {
     const uint16_t* A;
     const uint16_t* B;
-    float* C;
+    float* C;            // final output (splits == 1)
+    float* P;            // split partials (splits > 1)
     const float* alpha;  // device scalar, or nullptr for 1
-    int rows, cols, R;
+    int rows, cols, R, splits;
 };
 
 __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kGT * kGPitch];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGT * kGPitch];
     const int ntc = (g.cols + kGT - 1) / kGT;
-    const int tr = blockIdx.x / ntc, tc = blockIdx.x % ntc;
+    const int tile = blockIdx.x / g.splits, split = blockIdx.x % g.splits;
+    const int tr = tile / ntc, tc = tile % ntc;
     const int row0 = tr * kGT, col0 = tc * kGT;
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / kGWN, wn = wave % kGWN;
 
-    // global -> register staging: 4 x 16 bytes of A and of B per thread
-    // (rows t / 8 + 32 i, 16-byte chunk t % 8 of the stage's 128 bytes)
-    const int srow = t / 8, sch = t % 8;
-    const uint16_t* abase = g.A + 8 * sch;
-    const uint16_t* bbase = g.B + 8 * sch;
-    int64_t aoff0 = (int64_t)min(row0 + srow, g.rows - 1) * g.R;
-    int64_t aoff1 = (int64_t)min(row0 + srow + 32, g.rows - 1) * g.R;
-    int64_t aoff2 = (int64_t)min(row0 + srow + 64, g.rows - 1) * g.R;
-    int64_t aoff3 = (int64_t)min(row0 + srow + 96, g.rows - 1) * g.R;
-    int64_t boff0 = (int64_t)min(col0 + srow, g.cols - 1) * g.R;
-    int64_t boff1 = (int64_t)min(col0 + srow + 32, g.cols - 1) * g.R;
-    int64_t boff2 = (int64_t)min(col0 + srow + 64, g.cols - 1) * g.R;
-    int64_t boff3 = (int64_t)min(col0 + srow + 96, g.cols - 1) * g.R;
-    const int lds0 = srow * kGPitch + 8 * sch;
-    constexpr int kLdsStep = 32 * kGPitch;
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define BWD_LOAD_STAGE(st)                                                                  \
-    do {                                                                                    \
-        const int64_t o_ = (int64_t)(st) * kGK;                                             \
-        ra0 = *reinterpret_cast<const uint4*>(abase + aoff0 + o_);                          \
-        ra1 = *reinterpret_cast<const uint4*>(abase + aoff1 + o_);                          \
-        ra2 = *reinterpret_cast<const uint4*>(abase + aoff2 + o_);                          \
-        ra3 = *reinterpret_cast<const uint4*>(abase + aoff3 + o_);                          \
-        rb0 = *reinterpret_cast<const uint4*>(bbase + boff0 + o_);                          \
-        rb1 = *reinterpret_cast<const uint4*>(bbase + boff1 + o_);                          \
-        rb2 = *reinterpret_cast<const uint4*>(bbase + boff2 + o_);                          \
-        rb3 = *reinterpret_cast<const uint4*>(bbase + boff3 + o_);                          \
-    } while (0)
-#define BWD_STORE_STAGE(buf)                                                                \
-    do {                                                                                    \
-        *reinterpret_cast<uint4*>(&As[buf][lds0]) = ra0;                                    \
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + kLdsStep]) = ra1;                         \
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + 2 * kLdsStep]) = ra2;                     \
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + 3 * kLdsStep]) = ra3;                     \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0]) = rb0;                                    \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + kLdsStep]) = rb1;                         \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 2 * kLdsStep]) = rb2;                     \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 3 * kLdsStep]) = rb3;                     \
-    } while (0)
-
-    f32x16 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};
+    // stages [st0, st1) of this split
     const int nst = g.R / kGK;
-    const int afrag = (wm * 64 + (lane & 31)) * kGPitch + 8 * (lane >> 5);
-    const int bfrag = (wn * 64 + (lane & 31)) * kGPitch + 8 * (lane >> 5);
-    if (nst > 0) {
-        BWD_LOAD_STAGE(0);
+    const int per = (nst + g.splits - 1) / g.splits;
+    const int st0 = min(split * per, nst), st1 = min(st0 + per, nst);
+
+    // global -> register staging: rows t / 8 + 64 i, 16-byte chunk t % 8
+    const int srow = t / 8, sch = t % 8;
+    constexpr int kRowStep = kGThreads / 8;  // 64
+    static_assert(kGLoads == 4, "four staged loads per operand");
+    const int64_t aoff0 = (int64_t)min(row0 + srow, g.rows - 1) * g.R + 8 * sch;
+    const int64_t aoff1 = (int64_t)min(row0 + srow + kRowStep, g.rows - 1) * g.R + 8 * sch;
+    const int64_t aoff2 = (int64_t)min(row0 + srow + 2 * kRowStep, g.rows - 1) * g.R + 8 * sch;
+    const int64_t aoff3 = (int64_t)min(row0 + srow + 3 * kRowStep, g.rows - 1) * g.R + 8 * sch;
+    const int64_t boff0 = (int64_t)min(col0 + srow, g.cols - 1) * g.R + 8 * sch;
+    const int64_t boff1 = (int64_t)min(col0 + srow + kRowStep, g.cols - 1) * g.R + 8 * sch;
+    const int64_t boff2 = (int64_t)min(col0 + srow + 2 * kRowStep, g.cols - 1) * g.R + 8 * sch;
+    const int64_t boff3 = (int64_t)min(col0 + srow + 3 * kRowStep, g.cols - 1) * g.R + 8 * sch;
+    const int lds0 = srow * kGPitch + 8 * sch;
+    constexpr int kLdsStep = kRowStep * kGPitch;
+    // Named registers (not arrays): the staged values stay in VGPRs.
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define BWD_LOAD_STAGE(st)                                                      \
+    do {                                                                        \
+        const int64_t o_ = (int64_t)(st) * kGK;                                 \
+        ra0 = *reinterpret_cast<const uint4*>(g.A + aoff0 + o_);                \
+        ra1 = *reinterpret_cast<const uint4*>(g.A + aoff1 + o_);                \
+        ra2 = *reinterpret_cast<const uint4*>(g.A + aoff2 + o_);                \
+        ra3 = *reinterpret_cast<const uint4*>(g.A + aoff3 + o_);                \
+        rb0 = *reinterpret_cast<const uint4*>(g.B + boff0 + o_);                \
+        rb1 = *reinterpret_cast<const uint4*>(g.B + boff1 + o_);                \
+        rb2 = *reinterpret_cast<const uint4*>(g.B + boff2 + o_);                \
+        rb3 = *reinterpret_cast<const uint4*>(g.B + boff3 + o_);                \
+    } while (0)
+#define BWD_STORE_STAGE(buf)                                                    \
+    do {                                                                        \
+        *reinterpret_cast<uint4*>(&As[buf][lds0]) = ra0;                        \
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + kLdsStep]) = ra1;             \
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + 2 * kLdsStep]) = ra2;         \
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + 3 * kLdsStep]) = ra3;         \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0]) = rb0;                        \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + kLdsStep]) = rb1;             \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 2 * kLdsStep]) = rb2;         \
+        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 3 * kLdsStep]) = rb3;         \
+    } while (0)
+
+    f32x16 acc[kGFM][kGFN];
+#pragma unroll
+    for (int i = 0; i < kGFM; ++i)
+#pragma unroll
+        for (int j = 0; j < kGFN; ++j) acc[i][j] = f32x16{};
+
+    const int afrag = (wm * (kGT / kGWM) + (lane & 31)) * kGPitch + 8 * (lane >> 5);
+    const int bfrag = (wn * (kGT / kGWN) + (lane & 31)) * kGPitch + 8 * (lane >> 5);
+    if (st0 < st1) {
+        BWD_LOAD_STAGE(st0);
         BWD_STORE_STAGE(0);
         __syncthreads();
     }
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nst) BWD_LOAD_STAGE(st + 1);
+    for (int st = st0; st < st1; ++st) {
+        const int buf = (st - st0) & 1;
+        const bool more = st + 1 < st1;
+        if (more) BWD_LOAD_STAGE(st + 1);
 #pragma unroll
         for (int ks = 0; ks < kGK / 16; ++ks) {
-            const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + 16 * ks]));
-            const bf16x8 a1 = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + 32 * kGPitch + 16 * ks]));
-            const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[buf][bfrag + 16 * ks]));
-            const bf16x8 b1 = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const uint4*>(&Bs[buf][bfrag + 32 * kGPitch + 16 * ks]));
-            acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
-            acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
-            acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
-            acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
+            bf16x8 av[kGFM], bv[kGFN];
+#pragma unroll
+            for (int i = 0; i < kGFM; ++i)
+                av[i] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + i * 32 * kGPitch + 16 * ks]));
+#pragma unroll
+            for (int j = 0; j < kGFN; ++j)
+                bv[j] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4*>(&Bs[buf][bfrag + j * 32 * kGPitch + 16 * ks]));
+#pragma unroll
+            for (int i = 0; i < kGFM; ++i)
+#pragma unroll
+                for (int j = 0; j < kGFN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        if (st + 1 < nst) BWD_STORE_STAGE(buf ^ 1);
+        if (more) BWD_STORE_STAGE(buf ^ 1);
         __syncthreads();
     }
 #undef BWD_LOAD_STAGE
 #undef BWD_STORE_STAGE
 
-    const float alpha = g.alpha ? *g.alpha : 1.0f;
-    auto store_frag = [&](const f32x16& acc, int i, int j) {
-        const int col = col0 + wn * 64 + j * 32 + (lane & 31);
-        if (col >= g.cols) return;
-        const int rbase = row0 + wm * 64 + i * 32 + 4 * (lane >> 5);
+    const bool direct = g.splits == 1;
+    const float alpha = direct ? (g.alpha ? *g.alpha : 1.0f) : 1.0f;
+    float* out = direct ? g.C : g.P + (int64_t)split * g.rows * g.cols;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = rbase + (v % 4) + 8 * (v / 4);
-            if (row < g.rows) g.C[(int64_t)row * g.cols + col] = alpha * acc[v];
+    for (int i = 0; i < kGFM; ++i)
+#pragma unroll
+        for (int j = 0; j < kGFN; ++j) {
+            const int col = col0 + wn * (kGT / kGWN) + j * 32 + (lane & 31);
+            const int rbase = row0 + wm * (kGT / kGWM) + i * 32 + 4 * (lane >> 5);
+            if (col < g.cols) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = rbase + (v % 4) + 8 * (v / 4);
+                    if (row < g.rows) out[(int64_t)row * g.cols + col] = alpha * acc[i][j][v];
+                }
+            }
         }
-    };
-    store_frag(acc00, 0, 0);
-    store_frag(acc01, 0, 1);
-    store_frag(acc10, 1, 0);
-    store_frag(acc11, 1, 1);
+}
+
+// C[i] = alpha * sum_s P[s][i], s in order.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ P, int splits, int64_t n,
+                                                           const float* __restrict__ alpha_p, float* __restrict__ C) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    const float alpha = alpha_p ? *alpha_p : 1.0f;
+    float4 a = *reinterpret_cast<const float4*>(P + i);
+    for (int sp = 1; sp < splits; ++sp) {
+        const float4 b = *reinterpret_cast<const float4*>(P + (int64_t)sp * n + i);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    *reinterpret_cast<float4*>(C + i) = make_float4(alpha * a.x, alpha * a.y, alpha * a.z, alpha * a.w);
+}
+
+// Splits of the reduction for a rows x cols output over R: enough blocks to
+// give every compute unit a tile, at most kMaxSplits, at least one stage each.
+int gemm_splits(int64_t rows, int64_t cols, int64_t R, int cus) {
+    const int64_t tiles = ((rows + kGT - 1) / kGT) * ((cols + kGT - 1) / kGT);
+    const int64_t nst = R / kGK;
+    int64_t sp = (cus + tiles - 1) / tiles;
+    if (sp > kMaxSplits) sp = kMaxSplits;
+    if (sp > nst) sp = nst;
+    return sp < 1 ? 1 : (int)sp;
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm backward.  A block owns kNormRows rows.  Phase 1 (a wave per row):
+// RMSNorm backward.  A block owns kNormRows rows (small, so that the grid
+// holds several blocks per compute unit).  Phase 1 (a wave per row):
 // ss = sum x^2 and S = sum dxn g x in fp64, r = (ss / K + eps)^-1/2 and
 // c = r^3 S / K.  Phase 2 (threads over columns, four each): dx = r g dxn -
 // x c written over dxn, and the block's partial dg[k] = sum_m dxn x r.
 // ---------------------------------------------------------------------------
-constexpr int kNormRows = 32;
+constexpr int kNormRows = 8;
 constexpr int kNormThreads = 256;
 
 __global__ __launch_bounds__(kNormThreads) void norm_backward_kernel(const uint16_t* __restrict__ x,
@@ -334,17 +393,43 @@ __global__ __launch_bounds__(kNormThreads) void norm_backward_kernel(const uint1
     }
 }
 
-// dg[k] = sum over blocks of the partials, in block order, fp64.
-__global__ __launch_bounds__(256) void dg_reduce_kernel(const float* __restrict__ partial, int nparts, int K,
-                                                        float* __restrict__ dg) {
-    const int k = blockIdx.x * 256 + threadIdx.x;
-    if (k >= K) return;
+// dg[k] = sum over blocks of the partials in fp64.  A block takes 16
+// columns; its 64 thread groups each sum every 64th partial (in order), and
+// the 64 group sums are added in group order, so the result is
+// deterministic.  Short chains over many blocks keep the loads in flight.
+constexpr int kDgCols = 16, kDgSplit = 64;
+
+__global__ __launch_bounds__(kDgCols * kDgSplit) void dg_reduce_kernel(const float* __restrict__ partial,
+                                                                       int nparts, int K, float* __restrict__ dg) {
+    __shared__ double part[kDgSplit][kDgCols];
+    const int c = threadIdx.x % kDgCols, p = threadIdx.x / kDgCols;
+    const int k = blockIdx.x * kDgCols + c;
     double a = 0.0;
-    for (int b = 0; b < nparts; ++b) a += (double)partial[(int64_t)b * K + k];
-    dg[k] = (float)a;
+    if (k < K)
+        for (int b = p; b < nparts; b += kDgSplit) a += (double)partial[(int64_t)b * K + k];
+    part[p][c] = a;
+    __syncthreads();
+    if (p == 0 && k < K) {
+        double sum = 0.0;
+#pragma unroll
+        for (int i = 0; i < kDgSplit; ++i) sum += part[i][c];
+        dg[k] = (float)sum;
+    }
 }
 
 inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+// The reduction split is sized for the 256 compute units of the target chip
+// (a fixed count, so that the workspace size does not depend on the device).
+constexpr int kTargetCUs = 256;
+
+size_t split_bytes(int64_t M, int64_t N, int64_t K) {
+    const int64_t Mp = round_up(M, kT), Np = round_up(N, kT);
+    const int s1 = M > 0 ? gemm_splits(M, K, Np, kTargetCUs) : 1;
+    const int s2 = N > 0 ? gemm_splits(N, K, Mp, kTargetCUs) : 1;
+    const int64_t b1 = s1 > 1 ? s1 * M * K * 4 : 0, b2 = s2 > 1 ? s2 * N * K * 4 : 0;
+    return (size_t)round_up(b1 > b2 ? b1 : b2, 256);
+}
 
 }  // namespace
 
@@ -353,8 +438,22 @@ size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t nparts = (M + kNormRows - 1) / kNormRows;
     return act_stage_bytes(M, K) + (size_t)round_up(M * Np * 2, 256) + (size_t)round_up(N * Mp * 2, 256) +
            (size_t)round_up(K * Mp * 2, 256) + (size_t)round_up(K * Np * 2, 256) +
-           (size_t)round_up(nparts * K * 4, 256);
+           (size_t)round_up(nparts * K * 4, 256) + split_bytes(M, N, K);
 }
+
+namespace {
+hipError_t run_gemm(const uint16_t* A, const uint16_t* B, float* C, float* P, const float* alpha, int64_t rows,
+                    int64_t cols, int64_t R, hipStream_t stream) {
+    const int sp = gemm_splits(rows, cols, R, kTargetCUs);
+    GemmArgs g{A, B, C, P, alpha, (int)rows, (int)cols, (int)R, sp};
+    bwd_gemm_kernel<<<cdiv(rows, kGT) * cdiv(cols, kGT) * sp, kGThreads, 0, stream>>>(g);
+    if (sp > 1) {
+        const int64_t n = rows * cols;
+        split_reduce_kernel<<<cdiv(n / 4, 256), 256, 0, stream>>>(P, sp, n, alpha, C);
+    }
+    return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     const int64_t M = a.M, N = a.N, K = a.K;
@@ -372,6 +471,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     uint16_t* wT = reinterpret_cast<uint16_t*>(base);
     base += round_up(K * Np * 2, 256);
     float* partial = reinterpret_cast<float*>(base);
+    base += round_up(nparts * K * 4, 256);
+    float* splitbuf = reinterpret_cast<float*>(base);
 
     hipError_t e;
     if (M > 0) {
@@ -386,16 +487,16 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
         }
         q_transpose_kernel<<<dim3(cdiv(Mp, kT), cdiv(K, kT)), kPrepThreads, 0, stream>>>(
             act.q, (int)M, (int)K, (int)Mp, reinterpret_cast<uint32_t*>(qT));
-        GemmArgs g1{A1, wT, a.dx, a.gamma, (int)M, (int)K, (int)Np};
-        bwd_gemm_kernel<<<cdiv(M, kGT) * cdiv(K, kGT), kGThreads, 0, stream>>>(g1);
+        e = run_gemm(A1, wT, a.dx, splitbuf, a.gamma, M, K, Np, stream);
+        if (e != hipSuccess) return e;
         norm_backward_kernel<<<(unsigned)nparts, kNormThreads, 0, stream>>>(a.x, a.g, (int)M, (int)K, a.eps,
                                                                           a.dx, partial);
     }
     if (N > 0) {
-        GemmArgs g2{A2, qT, a.dW, nullptr, (int)N, (int)K, (int)Mp};
-        bwd_gemm_kernel<<<cdiv(N, kGT) * cdiv(K, kGT), kGThreads, 0, stream>>>(g2);
+        e = run_gemm(A2, qT, a.dW, splitbuf, nullptr, N, K, Mp, stream);
+        if (e != hipSuccess) return e;
     }
-    dg_reduce_kernel<<<cdiv(K, 256), 256, 0, stream>>>(partial, (int)nparts, (int)K, a.dg);
+    dg_reduce_kernel<<<cdiv(K, kDgCols), kDgCols * kDgSplit, 0, stream>>>(partial, (int)nparts, (int)K, a.dg);
     return hipGetLastError();
 }
 
