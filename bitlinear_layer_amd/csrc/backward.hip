@@ -41,42 +41,60 @@ constexpr uint32_t kBf16One = 0x3F80u;
 
 // One 64 x 64 tile of dy: A1[m][n] = bf16(dy[m][n]) for m < M, n < Np (zero
 // past N); A2[n][m] = bf16(dy[m][n] / s[m]) for n < N, m < Mp (zero past M).
+// Rows of dy are read 16 bytes at a time when N % 4 == 0 (VEC), and both
+// outputs are written four bf16 (8 bytes) at a time.
+template <bool VEC>
 __global__ __launch_bounds__(kPrepThreads) void dy_prep_kernel(const float* __restrict__ dy,
                                                                const float* __restrict__ s, int M, int N,
-                                                               int Mp, int Np, uint32_t* __restrict__ A1,
-                                                               uint32_t* __restrict__ A2) {
+                                                               int Mp, int Np, uint2* __restrict__ A1,
+                                                               uint2* __restrict__ A2) {
     __shared__ float tile[kT][kT + 1];
-    __shared__ float sinv[kT];
+    __shared__ float sv[kT];
     const int m0 = blockIdx.x * kT, n0 = blockIdx.y * kT;
     const int t = threadIdx.x;
-    if (t < kT) sinv[t] = (m0 + t < M) ? s[m0 + t] : 1.0f;
+    if (t < kT) sv[t] = (m0 + t < M) ? s[m0 + t] : 1.0f;
+    // 64 rows x 16 groups of four columns
 #pragma unroll
-    for (int i = 0; i < kT / 4; ++i) {
-        const int r = t / kT + 4 * i, c = t % kT;
+    for (int i = 0; i < kT / 16; ++i) {
+        const int r = t / 16 + 16 * i, c = 4 * (t % 16);
         const int m = m0 + r, n = n0 + c;
-        tile[r][c] = (m < M && n < N) ? dy[(int64_t)m * N + n] : 0.0f;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m < M) {
+            const float* src = dy + (int64_t)m * N + n;
+            if (VEC) {
+                if (n < N) v = *reinterpret_cast<const float4*>(src);
+            } else {
+                v.x = n < N ? src[0] : 0.f;
+                v.y = n + 1 < N ? src[1] : 0.f;
+                v.z = n + 2 < N ? src[2] : 0.f;
+                v.w = n + 3 < N ? src[3] : 0.f;
+            }
+        }
+        tile[r][c] = v.x;
+        tile[r][c + 1] = v.y;
+        tile[r][c + 2] = v.z;
+        tile[r][c + 3] = v.w;
     }
     __syncthreads();
-    // A1 rows m, pairs of columns
+    auto pack4 = [](float a, float b, float c, float d) {
+        return make_uint2(f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
+                          f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16));
+    };
+    // A1 rows m, four columns per thread
 #pragma unroll
-    for (int i = 0; i < kT / 8; ++i) {
-        const int r = t / 32 + 8 * i, c = 2 * (t % 32);
+    for (int i = 0; i < kT / 16; ++i) {
+        const int r = t / 16 + 16 * i, c = 4 * (t % 16);
         const int m = m0 + r;
-        if (m < M) {
-            const uint32_t lo = f32_to_bf16_bits(tile[r][c]), hi = f32_to_bf16_bits(tile[r][c + 1]);
-            A1[((int64_t)m * Np + n0 + c) / 2] = lo | (hi << 16);
-        }
+        if (m < M) A1[((int64_t)m * Np + n0 + c) / 4] = pack4(tile[r][c], tile[r][c + 1], tile[r][c + 2], tile[r][c + 3]);
     }
-    // A2 rows n, pairs of tokens; dy / s is an IEEE fp32 division
+    // A2 rows n, four tokens per thread; dy / s is an IEEE fp32 division
 #pragma unroll
-    for (int i = 0; i < kT / 8; ++i) {
-        const int c = t / 32 + 8 * i, r = 2 * (t % 32);
+    for (int i = 0; i < kT / 16; ++i) {
+        const int c = t / 16 + 16 * i, r = 4 * (t % 16);
         const int n = n0 + c;
-        if (n < N) {
-            const uint32_t lo = f32_to_bf16_bits(tile[r][c] / sinv[r]);
-            const uint32_t hi = f32_to_bf16_bits(tile[r + 1][c] / sinv[r + 1]);
-            A2[((int64_t)n * Mp + m0 + r) / 2] = lo | (hi << 16);
-        }
+        if (n < N)
+            A2[((int64_t)n * Mp + m0 + r) / 4] = pack4(tile[r][c] / sv[r], tile[r + 1][c] / sv[r + 1],
+                                                       tile[r + 2][c] / sv[r + 2], tile[r + 3][c] / sv[r + 3]);
     }
 }
 
@@ -479,9 +497,13 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
         e = launch_quant(a.x, a.g, M, M, (int)K, a.eps, act, stream);
         if (e != hipSuccess) return e;
         if (Np > 0) {
-            dy_prep_kernel<<<dim3(cdiv(Mp, kT), cdiv(Np, kT)), kPrepThreads, 0, stream>>>(
-                a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint32_t*>(A1),
-                reinterpret_cast<uint32_t*>(A2));
+            const dim3 grid(cdiv(Mp, kT), cdiv(Np, kT));
+            if (N % 4 == 0)
+                dy_prep_kernel<true><<<grid, kPrepThreads, 0, stream>>>(
+                    a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint2*>(A1), reinterpret_cast<uint2*>(A2));
+            else
+                dy_prep_kernel<false><<<grid, kPrepThreads, 0, stream>>>(
+                    a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint2*>(A1), reinterpret_cast<uint2*>(A2));
             w_transpose_kernel<<<dim3(cdiv(Np, kT), cdiv(K, kT)), kPrepThreads, 0, stream>>>(
                 reinterpret_cast<const uint32_t*>(a.packed), (int)N, (int)K, (int)Np, reinterpret_cast<uint32_t*>(wT));
         }
