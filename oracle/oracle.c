@@ -1,5 +1,6 @@
 /*
- * oracle.c -- plain, slow CPU definition of the BitLinear forward pass.
+ * oracle.c -- plain, slow CPU definition of the BitLinear forward pass (and
+ * of its straight-through backward, at the end of the file).
  *
  * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark, never by the library.  It is written
@@ -309,9 +310,10 @@ void orc_bitlinear_backward(const uint16_t* x, const float* g, const int8_t* w,
         for (int64_t k = 0; k < K; ++k) {
             double a = 0.0;
             for (int64_t n = 0; n < N; ++n) {
-                if (w[n * K + k] == 1)
+                const int wnk = w[n * K + k];
+                if (wnk == 1)
                     a += (double)dy[m * N + n];
-                else if (w[n * K + k] == -1)
+                else if (wnk == -1)
                     a -= (double)dy[m * N + n];
             }
             dxn[m * K + k] = (double)gamma * a;

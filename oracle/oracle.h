@@ -10,7 +10,8 @@
  *   [ld246]      ld246.com article 1724132886152, sections "三值权重的应用"
  *                (ternary weights: +1 adds, -1 subtracts, 0 skips) and
  *                "融合 BitLinear 层的创新" (RMSNorm and quantisation fused in
- *                front of the ternary product).
+ *                front of the ternary product) and "训练与优化：新的策略"
+ *                (straight-through gradients in training).
  *   [jiqizhixin] jiqizhixin.com 2024-06-11-4, section "具有三值权重的
  *                MatMul-free 密集层" (ternary dense layer, Algorithm 1:
  *                quantisation fused with RMSNorm and BitLinear) and section
