@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kPrepThreads) void dy_prep_kernel(const float* __re
                                                                uint2* __restrict__ A2) {
     __shared__ float tile[kT][kT + 1];
     __shared__ float sv[kT];
-    const int m0 = blockIdx.x * kT, n0 = blockIdx.y * kT;
+    const int64_t mt = Mp / kT;  // tiles along m; the grid is flat (m fastest)
+    const int m0 = (int)(blockIdx.x % mt) * kT, n0 = (int)(blockIdx.x / mt) * kT;
     const int t = threadIdx.x;
     if (t < kT) sv[t] = (m0 + t < M) ? s[m0 + t] : 1.0f;
     // 64 rows x 16 groups of four columns
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(kPrepThreads) void dy_prep_kernel(const float* __re
 __global__ __launch_bounds__(kPrepThreads) void q_transpose_kernel(const int8_t* __restrict__ q, int M, int K,
                                                                    int Mp, uint32_t* __restrict__ qT) {
     __shared__ int8_t tile[kT][kT + 4];
-    const int m0 = blockIdx.x * kT, k0 = blockIdx.y * kT;
+    const int64_t mt = Mp / kT;  // flat grid, m fastest
+    const int m0 = (int)(blockIdx.x % mt) * kT, k0 = (int)(blockIdx.x / mt) * kT;
     const int t = threadIdx.x;
     {
         const int r = t / 4, ch = t % 4;  // 64 rows x 4 chunks of 16 codes
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(kPrepThreads) void q_transpose_kernel(const int8_t*
 __global__ __launch_bounds__(kPrepThreads) void w_transpose_kernel(const uint32_t* __restrict__ packed, int N,
                                                                    int K, int Np, uint32_t* __restrict__ wT) {
     __shared__ uint16_t tile[kT][kT + 2];
-    const int n0 = blockIdx.x * kT, k0 = blockIdx.y * kT;
+    const int64_t nt = Np / kT;  // flat grid, n fastest
+    const int n0 = (int)(blockIdx.x % nt) * kT, k0 = (int)(blockIdx.x / nt) * kT;
     const int t = threadIdx.x;
     {
         const int r = t / 4, wi = t % 4;  // 64 rows x 4 words of 16 weights
@@ -497,17 +500,18 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
         e = launch_quant(a.x, a.g, M, M, (int)K, a.eps, act, stream);
         if (e != hipSuccess) return e;
         if (Np > 0) {
-            const dim3 grid(cdiv(Mp, kT), cdiv(Np, kT));
+            // flat grids: one dimension of grid y would cap N (or K) at 65535 tiles
+            const unsigned grid = cdiv(Mp, kT) * cdiv(Np, kT);
             if (N % 4 == 0)
                 dy_prep_kernel<true><<<grid, kPrepThreads, 0, stream>>>(
                     a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint2*>(A1), reinterpret_cast<uint2*>(A2));
             else
                 dy_prep_kernel<false><<<grid, kPrepThreads, 0, stream>>>(
                     a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint2*>(A1), reinterpret_cast<uint2*>(A2));
-            w_transpose_kernel<<<dim3(cdiv(Np, kT), cdiv(K, kT)), kPrepThreads, 0, stream>>>(
+            w_transpose_kernel<<<cdiv(Np, kT) * cdiv(K, kT), kPrepThreads, 0, stream>>>(
                 reinterpret_cast<const uint32_t*>(a.packed), (int)N, (int)K, (int)Np, reinterpret_cast<uint32_t*>(wT));
         }
-        q_transpose_kernel<<<dim3(cdiv(Mp, kT), cdiv(K, kT)), kPrepThreads, 0, stream>>>(
+        q_transpose_kernel<<<cdiv(Mp, kT) * cdiv(K, kT), kPrepThreads, 0, stream>>>(
             act.q, (int)M, (int)K, (int)Mp, reinterpret_cast<uint32_t*>(qT));
         e = run_gemm(A1, wT, a.dx, splitbuf, a.gamma, M, K, Np, stream);
         if (e != hipSuccess) return e;

@@ -177,3 +177,10 @@ def test_backward_full_size_sampled():
     b_dW = U * (dq.T @ np.abs(q).astype(np.float64))
     _check(dW[ns], ref["dW"], b_dW, "dW rows")
     assert np.all(np.isfinite(dg))
+
+
+def test_backward_rows_longer_than_65535_tiles():
+    """K = 4194368: 65537 tiles of 64 along K, one past what a second grid
+    dimension could hold; two tokens, three outputs."""
+    M, N, K = 2, 3, 4194368
+    _parity(M, N, K, seed=13, outliers=False)
