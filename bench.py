@@ -443,6 +443,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="run only these secondary workloads after the headline (comma-separated; "
+                         "available: backward)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay line (its 1024-node graphs are slow under counter collection)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -477,7 +480,8 @@ def main():
     log(f"[bench] decode: {head['gbps']:.1f} GB/s wall, {head['kernel_gbps']:.1f} GB/s by events")
 
     secondary = {}
-    if not args.no_secondary:
+    only = [w for w in args.only.split(",") if w]
+    if not args.no_secondary and not only:
         log("[bench] single layer M=1")
         secondary["decode_m1_single_layer"] = bench_single_layer(torch, bl, wl, 1, N, K, 200, stream)
         if not args.no_graph:
@@ -513,6 +517,8 @@ def main():
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
+
+    if (not args.no_secondary and not only) or "backward" in only:
         log("[bench] backward (straight-through) 8192 x 2048 x 2048")
         secondary["backward_8192x2048x2048"] = bench_backward(torch, bl, wl, 8192, 2048, 2048,
                                                               max(10, args.steps // 2), args.warmup, stream)
