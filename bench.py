@@ -18,9 +18,11 @@ over about 1 GiB of cold weights) and the same shapes at 64 and 512 tokens
 and 16384 tokens, the 8192-token prefill (int8 TOPS of the MFMA product
 kernel, timed apart from the quantisation kernel), the GLU
 mixer at M=1 (one call, and one step through 128 mixers) and M=4096, the
-batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, and, as
-context, a plain 2 GiB device copy and, beside each product of 4096 tokens or
-more, the vendor's dense int8 GEMM on the same shape.  `roofline` is for the
+batched re-ternarisation of 64 fp32 master matrices of 2048 x 2048, the
+straight-through backward of one layer at 8192 x 2048 x 2048 (TFLOP/s of its
+two bf16 products; `--only backward` runs the headline and this leg alone),
+and, as context, a plain 2 GiB device copy and, beside each product of 4096
+tokens or more, the vendor's dense int8 GEMM on the same shape.  `roofline` is for the
 headline's dominant kernel, timed with one HIP event pair on the stream it
 runs on, around a second pass of the timed steps; `cpu_baseline` times the
 CPU oracle on a bounded sample of the headline workload on this host.
