@@ -88,3 +88,51 @@ def test_graph_replay_matches_eager():
         if prev is not None:
             assert not np.array_equal(got[0], prev)
         prev = got[0]
+
+
+def test_graph_replay_backward_matches_eager():
+    """The backward pass captured into a graph (eight launches, split
+    reduction included) and replayed on new x and dy equals eager calls."""
+    dev = gu.DEV
+    M, N, K = 300, 2048, 512  # dW has 16 tiles, so its reduction is split
+    packed, gamma = gu.pack_on_gpu(wl.w_normal(N, K, seed=21))
+    g = gu.to_dev(wl.rms_weight(K, kind="uniform", seed=21))
+
+    def inputs(rep):
+        return (gu.to_dev_bf16(wl.x_normal(M, K, seed=300 + rep)), gu.to_dev(wl.dy_normal(M, N, seed=300 + rep)))
+
+    def outs():
+        return (torch.empty((M, K), dtype=torch.float32, device=dev), torch.empty(K, dtype=torch.float32, device=dev),
+                torch.empty((N, K), dtype=torch.float32, device=dev))
+
+    ws = torch.empty(bl.bitlinear_backward_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+    cx, cdy = inputs(0)
+    co = outs()
+
+    def run(x, dy, o, w):
+        bl.bitlinear_backward(x, g, packed, gamma, dy, dx=o[0], dg=o[1], dW=o[2], ws=w)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(cx, cdy, co, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(cx, cdy, co, ws)
+    torch.cuda.synchronize()
+    ews = torch.empty_like(ws)
+    for rep in range(1, 4):
+        x, dy = inputs(rep)
+        cx.copy_(x)
+        cdy.copy_(dy)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.cpu().numpy() for t in co]
+        eo = outs()
+        run(x, dy, eo, ews)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, [t.cpu().numpy() for t in eo])):
+            assert np.array_equal(a, b), f"replay {rep}, output {i}"
