@@ -414,6 +414,95 @@ __global__ __launch_bounds__(kNormThreads) void norm_backward_kernel(const uint1
     }
 }
 
+// The same RMSNorm backward for rows of at most CPL * 256 elements, held in
+// registers: a wave owns one row at a time (lane l: columns 4 (l + 64 c),
+// c < CPL), so x and dxn are read once and dx written once, with no second
+// pass.  A block owns kNormRowsRegs rows (each wave every fourth); its dg
+// partial is the four waves' sums added in wave order through LDS.
+constexpr int kNormRowsRegs = 16;
+
+template <int CPL>
+__global__ __launch_bounds__(kNormThreads) void norm_backward_regs_kernel(const uint16_t* __restrict__ x,
+                                                                          const float* __restrict__ gw, int M,
+                                                                          int K, float eps,
+                                                                          float* __restrict__ dxio,
+                                                                          float* __restrict__ partial) {
+    __shared__ float4 red[CPL * kWave];
+    const int m0 = blockIdx.x * kNormRowsRegs;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    constexpr int kWaves = kNormThreads / kWave;
+    float4 gv[CPL], acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int k = 4 * (lane + kWave * c);
+        gv[c] = k < K ? *reinterpret_cast<const float4*>(gw + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int rr = wave; rr < kNormRowsRegs; rr += kWaves) {
+        const int m = m0 + rr;
+        if (m >= M) break;
+        const uint16_t* xr = x + (int64_t)m * K;
+        float* dr = dxio + (int64_t)m * K;
+        float4 d[CPL], xv[CPL];
+        double ss = 0.0, S = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int k = 4 * (lane + kWave * c);
+            uint2 xb = make_uint2(0u, 0u);
+            d[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k < K) {
+                xb = *reinterpret_cast<const uint2*>(xr + k);
+                d[c] = *reinterpret_cast<const float4*>(dr + k);
+            }
+            xv[c] = make_float4(bf16_lo(xb.x), bf16_hi(xb.x), bf16_lo(xb.y), bf16_hi(xb.y));
+            ss += (double)xv[c].x * (double)xv[c].x + (double)xv[c].y * (double)xv[c].y +
+                  (double)xv[c].z * (double)xv[c].z + (double)xv[c].w * (double)xv[c].w;
+            S += (double)d[c].x * (double)gv[c].x * (double)xv[c].x + (double)d[c].y * (double)gv[c].y * (double)xv[c].y +
+                 (double)d[c].z * (double)gv[c].z * (double)xv[c].z + (double)d[c].w * (double)gv[c].w * (double)xv[c].w;
+        }
+        ss = wave_sum(ss);
+        S = wave_sum(S);
+        const double rd = 1.0 / sqrt(ss / (double)K + (double)eps);
+        const float r = (float)rd, cc = (float)(rd * rd * rd * S / (double)K);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int k = 4 * (lane + kWave * c);
+            if (k < K) {
+                float4 o;
+                o.x = r * gv[c].x * d[c].x - xv[c].x * cc;
+                o.y = r * gv[c].y * d[c].y - xv[c].y * cc;
+                o.z = r * gv[c].z * d[c].z - xv[c].z * cc;
+                o.w = r * gv[c].w * d[c].w - xv[c].w * cc;
+                *reinterpret_cast<float4*>(dr + k) = o;
+            }
+            acc[c].x += d[c].x * xv[c].x * r;
+            acc[c].y += d[c].y * xv[c].y * r;
+            acc[c].z += d[c].z * xv[c].z * r;
+            acc[c].w += d[c].w * xv[c].w * r;
+        }
+    }
+    // dg partial of the block: waves 0, 1, 2, 3 added in that order
+    for (int w = 0; w < kWaves; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                float4 v = acc[c];
+                if (w > 0) {
+                    const float4 p = red[c * kWave + lane];
+                    v = make_float4(p.x + v.x, p.y + v.y, p.z + v.z, p.w + v.w);
+                }
+                red[c * kWave + lane] = v;
+            }
+        }
+        __syncthreads();
+    }
+    for (int i = t; i < CPL * kWave; i += kNormThreads) {
+        const int c = i / kWave, l = i % kWave;
+        const int k = 4 * (l + kWave * c);
+        if (k < K) *reinterpret_cast<float4*>(partial + (int64_t)blockIdx.x * K + k) = red[i];
+    }
+}
+
 // dg[k] = sum over blocks of the partials in fp64.  A block takes 16
 // columns; its 64 thread groups each sum every 64th partial (in order), and
 // the 64 group sums are added in group order, so the result is
@@ -463,6 +552,30 @@ size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 namespace {
+// Blocks of the RMSNorm backward (= dg partials): the register form for rows
+// of at most 4096, the two-pass form above that.
+int64_t norm_blocks(int64_t M, int64_t K) {
+    return K <= 16 * 256 ? (M + kNormRowsRegs - 1) / kNormRowsRegs : (M + kNormRows - 1) / kNormRows;
+}
+
+hipError_t launch_norm_backward(const BackwardArgs& a, float* partial, int64_t nblocks, hipStream_t stream) {
+    const int M = (int)a.M, K = (int)a.K;
+    const unsigned grid = (unsigned)nblocks;
+    if (K <= 256)
+        norm_backward_regs_kernel<1><<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx, partial);
+    else if (K <= 512)
+        norm_backward_regs_kernel<2><<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx, partial);
+    else if (K <= 1024)
+        norm_backward_regs_kernel<4><<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx, partial);
+    else if (K <= 2048)
+        norm_backward_regs_kernel<8><<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx, partial);
+    else if (K <= 4096)
+        norm_backward_regs_kernel<16><<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx, partial);
+    else
+        norm_backward_kernel<<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx, partial);
+    return hipGetLastError();
+}
+
 hipError_t run_gemm(const uint16_t* A, const uint16_t* B, float* C, float* P, const float* alpha, int64_t rows,
                     int64_t cols, int64_t R, hipStream_t stream) {
     const int sp = gemm_splits(rows, cols, R, kTargetCUs);
@@ -494,6 +607,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     float* partial = reinterpret_cast<float*>(base);
     base += round_up(nparts * K * 4, 256);
     float* splitbuf = reinterpret_cast<float*>(base);
+    const int64_t nparts_used = M > 0 ? norm_blocks(M, K) : 0;  // <= nparts, the size reserved
 
     hipError_t e;
     if (M > 0) {
@@ -515,14 +629,14 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
             act.q, (int)M, (int)K, (int)Mp, reinterpret_cast<uint32_t*>(qT));
         e = run_gemm(A1, wT, a.dx, splitbuf, a.gamma, M, K, Np, stream);
         if (e != hipSuccess) return e;
-        norm_backward_kernel<<<(unsigned)nparts, kNormThreads, 0, stream>>>(a.x, a.g, (int)M, (int)K, a.eps,
-                                                                          a.dx, partial);
+        e = launch_norm_backward(a, partial, nparts_used, stream);
+        if (e != hipSuccess) return e;
     }
     if (N > 0) {
         e = run_gemm(A2, qT, a.dW, splitbuf, nullptr, N, K, Mp, stream);
         if (e != hipSuccess) return e;
     }
-    dg_reduce_kernel<<<cdiv(K, kDgCols), kDgCols * kDgSplit, 0, stream>>>(partial, (int)nparts, (int)K, a.dg);
+    dg_reduce_kernel<<<cdiv(K, kDgCols), kDgCols * kDgSplit, 0, stream>>>(partial, (int)nparts_used, (int)K, a.dg);
     return hipGetLastError();
 }
 

@@ -90,6 +90,9 @@ def _parity(M, N, K, seed, outliers=True):
 SHAPES = [
     (1, 16, 16), (5, 40, 48), (64, 64, 64), (130, 200, 272), (257, 129, 320),
     (600, 300, 1024), (33, 1000, 96), (1000, 24, 160),
+    # RMSNorm backward: rows held in registers up to K = 4096 (full and
+    # ragged last chunk), the two-pass form above
+    (37, 64, 4096), (21, 40, 3856), (40, 50, 4160),
 ]
 
 
