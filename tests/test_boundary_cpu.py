@@ -129,3 +129,37 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(bl, "_lib", None)
     with pytest.raises(RuntimeError):
         bl.lib()
+
+
+def _bwd(x=FAKE, g=FAKE, p=FAKE, gamma=FAKE, dy=FAKE, M=4, N=64, K=64, eps=1e-6, dx=FAKE, dg=FAKE, dW=FAKE,
+         ws=FAKE, ws_bytes=1 << 30):
+    return bl.lib().bitlinear_backward(x, g, p, gamma, dy, M, N, K, eps, dx, dg, dW, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(dy=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(dx=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(dg=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(dW=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(p=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(gamma=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(dy=MISALIGNED), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(K=24), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(K=(1 << 24) + 16, M=1, N=1), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(M=-1), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(ws=None), bl.BITLINEAR_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), bl.BITLINEAR_ERR_WORKSPACE),
+])
+def test_backward_rejects(kwargs, status):
+    assert _bwd(**kwargs) == status
+
+
+def test_backward_workspace_query():
+    L = bl.lib()
+    assert L.bitlinear_backward_workspace_bytes(4, 64, 12) == 0
+    assert L.bitlinear_backward_workspace_bytes(-1, 64, 64) == 0
+    small = L.bitlinear_backward_workspace_bytes(1, 16, 16)
+    big = L.bitlinear_backward_workspace_bytes(8192, 2048, 2048)
+    assert 0 < small < big and big % 256 == 0
