@@ -476,6 +476,24 @@ def pin_backward_weight_gradient(orc):
     assert np.allclose(out["dW"], parts[0] + parts[1], rtol=0, atol=1e-15 * np.abs(out["dW"]).max())
 
 
+def pin_backward_single_feature_closed_form(orc):
+    """K = 1: xn = g x / sqrt(x^2 + eps), so d xn / d x = g eps r^3 with
+    r = (x^2 + eps)^-1/2, and dx = g dxn eps r^3, dg = dxn x r, where
+    dxn = gamma sum_n dy[n] w[n][0]."""
+    eps = float(np.float32(1e-3))  # large enough that eps r^3 is far from rounding noise
+    x = wl.f32_to_bf16_bits(np.array([[0.75], [-0.125], [2.0]], np.float32))
+    g = np.array([1.5], np.float32)
+    w = np.array([[1], [-1], [0], [1]], np.int8)
+    gamma = 0.25
+    dy = np.array([[1.0, 2.0, 4.0, -0.5], [0.0, 1.0, 0.0, 0.0], [3.0, 0.0, 1.0, 1.0]], np.float32)
+    out = orc.backward(x, g, w, gamma, dy, eps)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)[:, 0]
+    dxn = gamma * (dy.astype(np.float64) @ w.astype(np.float64))[:, 0]
+    r = 1.0 / np.sqrt(xf ** 2 + eps)
+    assert np.allclose(out["dx"][:, 0], 1.5 * dxn * eps * r ** 3, rtol=1e-9, atol=0)
+    assert math.isclose(out["dg"][0], float((dxn * xf * r).sum()), rel_tol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
