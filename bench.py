@@ -407,7 +407,59 @@ def vendor_int8_gemm_us(torch, M, N, K, steps, warmup, stream):
 # CPU oracle baseline
 # --------------------------------------------------------------------------
 
-def cpu_baseline(wl, M, N, K, seconds):
+def host_cpu():
+    """This host's CPU model, logical CPU count and the CPUs this process may
+    run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return dict(cpu_model=model, nproc=os.cpu_count(), usable_cpus=usable)
+
+
+def _oracle_threads(threads, work, seconds, min_items):
+    """Run work(i) for i = 0, 1, ... on `threads` Python threads until
+    `seconds` have passed and at least `min_items` items are done; the oracle
+    is C behind ctypes, which releases the interpreter lock during each call,
+    so the threads run in parallel.  Returns (items done, elapsed s)."""
+    import threading
+
+    lock = threading.Lock()
+    state = dict(next=0, done=0)
+    t0 = time.perf_counter()
+
+    def worker():
+        while True:
+            with lock:
+                if time.perf_counter() - t0 >= seconds and state["next"] >= min_items:
+                    return
+                i = state["next"]
+                state["next"] += 1
+            work(i)
+            with lock:
+                state["done"] += 1
+
+    ts = [threading.Thread(target=worker) for _ in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return state["done"], time.perf_counter() - t0
+
+
+def cpu_baseline(wl, M, N, K, seconds, threads):
+    """The CPU oracle (plain C, -O2, one add/subtract per weight) on this
+    host, unchanged: the headline's decode layers on one thread and on
+    `threads` threads (independent layers per thread), and a row sample of
+    the 8192 x 2048 x 2048 prefill on as many threads, scaled to all 8192
+    rows (the oracle's cost is linear in the rows).  `value` is the
+    all-threads decode rate in the headline's unit."""
     import numpy as np
     import oracle
 
@@ -419,19 +471,41 @@ def cpu_baseline(wl, M, N, K, seconds):
         gm = orc.gamma(W)
         pool.append((x, orc.ternarize(W, gm), gm))
     g = np.ones(K, np.float32)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        x, w, gm = pool[n % len(pool)]
+
+    def decode(i):
+        x, w, gm = pool[i % len(pool)]
         orc.bitlinear_ternary(x, g, w, gm)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds and n >= 4:
-            break
-    nbytes = n * layer_bytes(M, N, K)
-    return dict(value=nbytes / el / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"{n} layers of the M={M} K={K} N={N} decode workload (4 seeded layers cycled), "
-                       f"single thread, {el:.1f} s", seconds=el)
+
+    n1, el1 = _oracle_threads(1, decode, seconds / 2, 4)
+    nt, elt = _oracle_threads(threads, decode, seconds / 4, 4 * threads)
+    one = dict(value=n1 * layer_bytes(M, N, K) / el1 / 1e9, unit="GB/s", cores=1,
+               sample=f"{n1} layers of the decode workload, {el1:.1f} s")
+
+    # prefill: 8192 x 2048 x 2048, Student-t x; blocks of 32 token rows
+    PM, PN, PK, rows = 8192, 2048, 2048, 32
+    Wp = wl.w_normal(PN, PK, seed=0)
+    gp = orc.gamma(Wp)
+    wp = orc.ternarize(Wp, gp)
+    xp = wl.x_student_t(PM, PK, seed=0)
+    gpk = np.ones(PK, np.float32)
+
+    def prefill(i):
+        r0 = (i * rows) % PM
+        orc.bitlinear_ternary(xp[r0:r0 + rows], gpk, wp, gp)
+
+    blocks, elp = _oracle_threads(threads, prefill, seconds / 4, max(8, threads))
+    done_rows = blocks * rows
+    ops = 2.0 * done_rows * PN * PK
+    prefill = dict(value=ops / elp / 1e12, unit="int8 TOPS", cores=threads,
+                   extrapolated_ms_per_8192_rows=elp * 1e3 * PM / done_rows,
+                   sample=f"{done_rows} of the 8192 token rows of the prefill (blocks of {rows} rows over "
+                          f"{threads} threads), {elp:.1f} s; the full layer's time extrapolated linearly "
+                          f"in rows (extrapolated)")
+    return dict(value=nt * layer_bytes(M, N, K) / elt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{nt} layers of the M={M} K={K} N={N} decode workload (4 seeded layers cycled) on "
+                       f"{threads} threads, {elt:.1f} s",
+                single_thread=one, prefill_8192=prefill, host=host_cpu(),
+                seconds=el1 + elt + elp)
 
 
 # --------------------------------------------------------------------------
@@ -442,7 +516,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=1024)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="total seconds of oracle work for cpu_baseline (split over its three samples)")
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="threads for the all-cores oracle samples (capped at the CPUs this process may use)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
@@ -528,7 +605,9 @@ def main():
     cpu = None
     if not args.no_cpu:
         log(f"[bench] cpu oracle for ~{args.cpu_seconds:.0f} s")
-        cpu = cpu_baseline(wl, M, N, K, args.cpu_seconds)
+        usable = host_cpu()["usable_cpus"] or 1
+        threads = max(1, min(args.cpu_threads or usable, usable))
+        cpu = cpu_baseline(wl, M, N, K, args.cpu_seconds, threads)
         cpu.pop("seconds")
 
     digest = source_digest(*DECODE_SOURCES)

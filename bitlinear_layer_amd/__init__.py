@@ -140,12 +140,52 @@ def _dev(t, name, dtypes, ndim=None):
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
-def _workspace(nbytes, ws, device):
+def _out(t, name, dtypes, shape, like):
+    """Check a caller-supplied output (or allocate nothing: returns t).
+
+    Outputs reach the kernels as raw pointers, so each is checked before any
+    call: dtype, exact shape, contiguity, then that it lives on the same GPU
+    as the input `like`.  The checks run in that order, so the shape and
+    dtype rejections are testable with CPU tensors."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda" or t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, is on {t.device}")
+    return t
+
+
+def _new_or_out(t, name, dtype, shape, like, dtypes=None):
+    """A fresh output tensor on like's device, or the caller's, checked."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return _out(t, name, dtypes or (dtype,), shape, like)
+
+
+def _workspace(nbytes, ws, like):
+    """Workspace of at least nbytes (the library checks the size): a fresh
+    byte tensor, or the caller's, which must be a contiguous tensor on like's
+    GPU."""
     if nbytes == 0:
         return None, 0
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    else:
+        _out(ws, "ws", (ws.dtype,), tuple(ws.shape), like)
     return ws, ws.numel() * ws.element_size()
+
+
+def _scalar(t, name, n=1):
+    """A device fp32 vector of exactly n values (gamma)."""
+    _dev(t, name, (torch.float32,))
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} value(s), holds {t.numel()}")
+    return t
 
 
 # --------------------------------------------------------------------------
@@ -164,11 +204,9 @@ def bitlinear_pack_weights(W, packed=None, gamma=None, ws=None, stream=None):
     """fp32 W [N, K] -> (packed uint8 [N, K/4], gamma fp32 [1])."""
     _dev(W, "W", (torch.float32,), 2)
     N, K = W.shape
-    if packed is None:
-        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
-    if gamma is None:
-        gamma = torch.empty(1, dtype=torch.float32, device=W.device)
-    ws, nbytes = _workspace(bitlinear_pack_workspace_bytes(N, K), ws, W.device)
+    packed = _new_or_out(packed, "packed", torch.uint8, (N, K // 4), W)
+    gamma = _new_or_out(gamma, "gamma", torch.float32, (1,), W)
+    ws, nbytes = _workspace(bitlinear_pack_workspace_bytes(N, K), ws, W)
     _check(lib().bitlinear_pack_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(ws), nbytes,
                                         _stream(stream)))
     return packed, gamma
@@ -183,11 +221,9 @@ def bitlinear_pack_weights_batched(W, packed=None, gamma=None, ws=None, stream=N
     gamma per matrix."""
     _dev(W, "W", (torch.float32,), 3)
     B, N, K = W.shape
-    if packed is None:
-        packed = torch.empty((B, N, K // 4), dtype=torch.uint8, device=W.device)
-    if gamma is None:
-        gamma = torch.empty(B, dtype=torch.float32, device=W.device)
-    ws, nbytes = _workspace(bitlinear_pack_batched_workspace_bytes(B, N, K), ws, W.device)
+    packed = _new_or_out(packed, "packed", torch.uint8, (B, N, K // 4), W)
+    gamma = _new_or_out(gamma, "gamma", torch.float32, (B,), W)
+    ws, nbytes = _workspace(bitlinear_pack_batched_workspace_bytes(B, N, K), ws, W)
     _check(lib().bitlinear_pack_weights_batched(_ptr(W), B, N, K, _ptr(packed), _ptr(gamma), _ptr(ws), nbytes,
                                                 _stream(stream)))
     return packed, gamma
@@ -197,8 +233,9 @@ def bitlinear_unpack_weights(packed, K, w=None, stream=None):
     """packed uint8 [N, K/4] -> int8 [N, K] (code - 1 per weight)."""
     _dev(packed, "packed", (torch.uint8,), 2)
     N = packed.shape[0]
-    if w is None:
-        w = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    if packed.shape[1] * 4 != K:
+        raise ValueError("packed does not hold K/4 bytes per row")
+    w = _new_or_out(w, "w", torch.int8, (N, K), packed)
     _check(lib().bitlinear_unpack_weights(_ptr(packed), N, K, _ptr(w), _stream(stream)))
     return w
 
@@ -217,14 +254,13 @@ def bitlinear_forward(x, rms_weight, packed, gamma, eps=1e-6, y=None, ws=None, s
     _dev(x, "x", _BF16, 2)
     _dev(rms_weight, "rms_weight", (torch.float32,), 1)
     _dev(packed, "packed", (torch.uint8,), 2)
-    _dev(gamma, "gamma", (torch.float32,))
+    _scalar(gamma, "gamma")
     M, K = x.shape
     N = packed.shape[0]
     if packed.shape[1] * 4 != K or rms_weight.shape[0] != K:
         raise ValueError("x, rms_weight and packed disagree on K")
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, N, K), ws, x.device)
+    y = _new_or_out(y, "y", torch.float32, (M, N), x)
+    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, N, K), ws, x)
     _check(lib().bitlinear_forward_ex(_ptr(x), _ptr(rms_weight), _ptr(packed), _ptr(gamma), M, N, K,
                                       float(eps), _ptr(y), _ptr(ws), nbytes, _stream(stream),
                                       int(kernel)))
@@ -236,7 +272,9 @@ def bitlinear_prepare_activations(x, rms_weight, eps=1e-6, N=0, ws=None, stream=
     _dev(x, "x", _BF16, 2)
     _dev(rms_weight, "rms_weight", (torch.float32,), 1)
     M, K = x.shape
-    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, N, K), ws, x.device)
+    if rms_weight.shape[0] != K:
+        raise ValueError("x and rms_weight disagree on K")
+    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, N, K), ws, x)
     _check(lib().bitlinear_prepare_activations(_ptr(x), _ptr(rms_weight), M, K, float(eps), _ptr(ws),
                                                nbytes, _stream(stream)))
     return ws
@@ -246,10 +284,11 @@ def bitlinear_forward_prepared(ws, packed, gamma, M, y=None, stream=None,
                                kernel=BITLINEAR_KERNEL_AUTO):
     """Ternary product + rescale from a prepared workspace -> y fp32 [M, N]."""
     _dev(packed, "packed", (torch.uint8,), 2)
-    _dev(gamma, "gamma", (torch.float32,))
+    _scalar(gamma, "gamma")
     N, K = packed.shape[0], packed.shape[1] * 4
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=packed.device)
+    y = _new_or_out(y, "y", torch.float32, (M, N), packed)
+    if ws is not None:
+        _out(ws, "ws", (ws.dtype,), tuple(ws.shape), packed)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().bitlinear_forward_prepared(_ptr(packed), _ptr(gamma), M, N, K, _ptr(y), _ptr(ws),
                                             nbytes, _stream(stream), int(kernel)))
@@ -266,16 +305,15 @@ def bitlinear_forward_batched(x, rms_weight, packed, gamma, eps=1e-6, y=None, ws
     _dev(x, "x", _BF16, 3)
     _dev(rms_weight, "rms_weight", (torch.float32,), 2)
     _dev(packed, "packed", (torch.uint8,), 3)
-    _dev(gamma, "gamma", (torch.float32,), 1)
     B, M, K = x.shape
+    _scalar(gamma, "gamma", B)
     N = packed.shape[1]
-    if packed.shape[0] != B or rms_weight.shape != (B, K) or gamma.shape[0] != B:
+    if packed.shape[0] != B or tuple(rms_weight.shape) != (B, K):
         raise ValueError("batch dimensions disagree")
     if packed.shape[2] * 4 != K:
         raise ValueError("x and packed disagree on K")
-    if y is None:
-        y = torch.empty((B, M, N), dtype=torch.float32, device=x.device)
-    ws, nbytes = _workspace(bitlinear_forward_batched_workspace_bytes(B, M, N, K), ws, x.device)
+    y = _new_or_out(y, "y", torch.float32, (B, M, N), x)
+    ws, nbytes = _workspace(bitlinear_forward_batched_workspace_bytes(B, M, N, K), ws, x)
     _check(lib().bitlinear_forward_batched(_ptr(x), _ptr(rms_weight), _ptr(packed), _ptr(gamma), B, M,
                                            N, K, float(eps), _ptr(y), _ptr(ws), nbytes,
                                            _stream(stream)))
@@ -297,17 +335,17 @@ def bitlinear_glu_forward(x, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_d
     _dev(x, "x", _BF16, 2)
     _dev(rms_w_gu, "rms_w_gu", (torch.float32,), 1)
     _dev(packed_gu, "packed_gu", (torch.uint8,), 2)
-    _dev(gamma_gu, "gamma_gu", (torch.float32,))
+    _scalar(gamma_gu, "gamma_gu")
     _dev(rms_w_down, "rms_w_down", (torch.float32,), 1)
     _dev(packed_down, "packed_down", (torch.uint8,), 2)
-    _dev(gamma_down, "gamma_down", (torch.float32,))
+    _scalar(gamma_down, "gamma_down")
     M, D = x.shape
     F = packed_down.shape[1] * 4
-    if packed_gu.shape != (2 * F, D // 4) or packed_down.shape[0] != D:
+    if (tuple(packed_gu.shape) != (2 * F, D // 4) or packed_down.shape[0] != D
+            or rms_w_gu.shape[0] != D or rms_w_down.shape[0] != F):
         raise ValueError("GLU matrix shapes disagree with x")
-    if y is None:
-        y = torch.empty((M, D), dtype=torch.float32, device=x.device)
-    ws, nbytes = _workspace(bitlinear_glu_workspace_bytes(M, D, F), ws, x.device)
+    y = _new_or_out(y, "y", torch.float32, (M, D), x)
+    ws, nbytes = _workspace(bitlinear_glu_workspace_bytes(M, D, F), ws, x)
     _check(lib().bitlinear_glu_forward(_ptr(x), _ptr(rms_w_gu), _ptr(packed_gu), _ptr(gamma_gu),
                                        _ptr(rms_w_down), _ptr(packed_down), _ptr(gamma_down), M, D, F,
                                        float(eps), _ptr(y), _ptr(ws), nbytes, _stream(stream)))
@@ -326,24 +364,41 @@ def bitlinear_glu_forward_batched(x, rms_w_gu, packed_gu, gamma_gu, rms_w_down, 
     _dev(x, "x", _BF16, 3)
     _dev(rms_w_gu, "rms_w_gu", (torch.float32,), 2)
     _dev(packed_gu, "packed_gu", (torch.uint8,), 3)
-    _dev(gamma_gu, "gamma_gu", (torch.float32,), 1)
     _dev(rms_w_down, "rms_w_down", (torch.float32,), 2)
     _dev(packed_down, "packed_down", (torch.uint8,), 3)
-    _dev(gamma_down, "gamma_down", (torch.float32,), 1)
     B, M, D = x.shape
+    _scalar(gamma_gu, "gamma_gu", B)
+    _scalar(gamma_down, "gamma_down", B)
     F = packed_down.shape[2] * 4
-    if (packed_gu.shape != (B, 2 * F, D // 4) or packed_down.shape[:2] != (B, D)
-            or rms_w_gu.shape != (B, D) or rms_w_down.shape != (B, F)
-            or gamma_gu.shape != (B,) or gamma_down.shape != (B,)):
+    if (tuple(packed_gu.shape) != (B, 2 * F, D // 4) or tuple(packed_down.shape[:2]) != (B, D)
+            or tuple(rms_w_gu.shape) != (B, D) or tuple(rms_w_down.shape) != (B, F)):
         raise ValueError("batched GLU shapes disagree with x")
-    if y is None:
-        y = torch.empty((B, M, D), dtype=torch.float32, device=x.device)
-    ws, nbytes = _workspace(bitlinear_glu_batched_workspace_bytes(B, M, D, F), ws, x.device)
+    y = _new_or_out(y, "y", torch.float32, (B, M, D), x)
+    ws, nbytes = _workspace(bitlinear_glu_batched_workspace_bytes(B, M, D, F), ws, x)
     _check(lib().bitlinear_glu_forward_batched(_ptr(x), _ptr(rms_w_gu), _ptr(packed_gu), _ptr(gamma_gu),
                                                _ptr(rms_w_down), _ptr(packed_down), _ptr(gamma_down), B,
                                                M, D, F, float(eps), _ptr(y), _ptr(ws), nbytes,
                                                _stream(stream)))
     return y
+
+
+def bitlinear_glu_hidden(x, rms_w_gu, packed_gu, gamma_gu, eps=1e-6, h=None, ws=None, stream=None,
+                         kernel=BITLINEAR_KERNEL_AUTO):
+    """First half of the mixer: h = bf16(SiLU(gate) * up) as int16 bits [M, F]."""
+    _dev(x, "x", _BF16, 2)
+    _dev(rms_w_gu, "rms_w_gu", (torch.float32,), 1)
+    _dev(packed_gu, "packed_gu", (torch.uint8,), 2)
+    _scalar(gamma_gu, "gamma_gu")
+    M, D = x.shape
+    F = packed_gu.shape[0] // 2
+    if packed_gu.shape[0] != 2 * F or packed_gu.shape[1] * 4 != D or rms_w_gu.shape[0] != D:
+        raise ValueError("GLU gate|up shapes disagree with x")
+    h = _new_or_out(h, "h", torch.int16, (M, F), x, _BF16)
+    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, 2 * F, D), ws, x)
+    _check(lib().bitlinear_glu_hidden(_ptr(x), _ptr(rms_w_gu), _ptr(packed_gu), _ptr(gamma_gu), M, D,
+                                      F, float(eps), _ptr(h), _ptr(ws), nbytes, _stream(stream),
+                                      int(kernel)))
+    return h
 
 
 # --------------------------------------------------------------------------
@@ -362,41 +417,20 @@ def bitlinear_backward(x, rms_weight, packed, gamma, dy, eps=1e-6, dx=None, dg=N
     _dev(x, "x", _BF16, 2)
     _dev(rms_weight, "rms_weight", (torch.float32,), 1)
     _dev(packed, "packed", (torch.uint8,), 2)
-    _dev(gamma, "gamma", (torch.float32,), 1)
+    _scalar(gamma, "gamma")
     _dev(dy, "dy", (torch.float32,), 2)
     M, K = x.shape
     N = packed.shape[0]
-    if packed.shape[1] * 4 != K or dy.shape != (M, N) or rms_weight.shape != (K,):
+    if packed.shape[1] * 4 != K or tuple(dy.shape) != (M, N) or tuple(rms_weight.shape) != (K,):
         raise ValueError("backward shapes disagree with x")
-    if dx is None:
-        dx = torch.empty((M, K), dtype=torch.float32, device=x.device)
-    if dg is None:
-        dg = torch.empty(K, dtype=torch.float32, device=x.device)
-    if dW is None:
-        dW = torch.empty((N, K), dtype=torch.float32, device=x.device)
-    ws, nbytes = _workspace(bitlinear_backward_workspace_bytes(M, N, K), ws, x.device)
+    dx = _new_or_out(dx, "dx", torch.float32, (M, K), x)
+    dg = _new_or_out(dg, "dg", torch.float32, (K,), x)
+    dW = _new_or_out(dW, "dW", torch.float32, (N, K), x)
+    ws, nbytes = _workspace(bitlinear_backward_workspace_bytes(M, N, K), ws, x)
     _check(lib().bitlinear_backward(_ptr(x), _ptr(rms_weight), _ptr(packed), _ptr(gamma), _ptr(dy), M, N, K,
                                     float(eps), _ptr(dx), _ptr(dg), _ptr(dW), _ptr(ws), nbytes,
                                     _stream(stream)))
     return dx, dg, dW
-
-
-def bitlinear_glu_hidden(x, rms_w_gu, packed_gu, gamma_gu, eps=1e-6, h=None, ws=None, stream=None,
-                         kernel=BITLINEAR_KERNEL_AUTO):
-    """First half of the mixer: h = bf16(SiLU(gate) * up) as int16 bits [M, F]."""
-    _dev(x, "x", _BF16, 2)
-    _dev(rms_w_gu, "rms_w_gu", (torch.float32,), 1)
-    _dev(packed_gu, "packed_gu", (torch.uint8,), 2)
-    _dev(gamma_gu, "gamma_gu", (torch.float32,))
-    M, D = x.shape
-    F = packed_gu.shape[0] // 2
-    if h is None:
-        h = torch.empty((M, F), dtype=torch.int16, device=x.device)
-    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, 2 * F, D), ws, x.device)
-    _check(lib().bitlinear_glu_hidden(_ptr(x), _ptr(rms_w_gu), _ptr(packed_gu), _ptr(gamma_gu), M, D,
-                                      F, float(eps), _ptr(h), _ptr(ws), nbytes, _stream(stream),
-                                      int(kernel)))
-    return h
 
 
 # --------------------------------------------------------------------------
@@ -408,10 +442,10 @@ def bitlinear_quantize(x, rms_weight, eps=1e-6, q=None, s=None, stream=None):
     _dev(x, "x", _BF16, 2)
     _dev(rms_weight, "rms_weight", (torch.float32,), 1)
     M, K = x.shape
-    if q is None:
-        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if s is None:
-        s = torch.empty(M, dtype=torch.float32, device=x.device)
+    if rms_weight.shape[0] != K:
+        raise ValueError("x and rms_weight disagree on K")
+    q = _new_or_out(q, "q", torch.int8, (M, K), x)
+    s = _new_or_out(s, "s", torch.float32, (M,), x)
     _check(lib().bitlinear_quantize(_ptr(x), _ptr(rms_weight), M, K, float(eps), _ptr(q), _ptr(s),
                                     _stream(stream)))
     return q, s
@@ -424,9 +458,10 @@ def bitlinear_ternary_matmul_i32(q, packed, acc=None, ws=None, stream=None,
     _dev(packed, "packed", (torch.uint8,), 2)
     M, K = q.shape
     N = packed.shape[0]
-    if acc is None:
-        acc = torch.empty((M, N), dtype=torch.int32, device=q.device)
-    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, N, K), ws, q.device)
+    if packed.shape[1] * 4 != K:
+        raise ValueError("q and packed disagree on K")
+    acc = _new_or_out(acc, "acc", torch.int32, (M, N), q)
+    ws, nbytes = _workspace(bitlinear_forward_workspace_bytes(M, N, K), ws, q)
     _check(lib().bitlinear_ternary_matmul_i32(_ptr(q), _ptr(packed), M, N, K, _ptr(acc), _ptr(ws),
                                               nbytes, _stream(stream), int(kernel)))
     return acc

@@ -515,7 +515,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     for (int i = 0; i < kADma; ++i) {
         const int r = (wave * kADma + i) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ (r & 7);
-        aoffs[i] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + 16 * chunk);
+        // unsigned: (BM - 1) * K + 112 < 2^32 for K <= 2^24, where the
+        // signed product would overflow from K > 2^31 / 255
+        aoffs[i] = (uint32_t)(min(m0 + r, M - 1) - m0) * (uint32_t)K + 16u * (uint32_t)chunk;
     }
     const int64_t brow0 = b_row<BN, kGlu>(tn, 0, N);
 #pragma unroll
@@ -858,7 +860,12 @@ hipError_t launch_ep(const ProductArgs& a, hipStream_t stream) {
     // that fewer padded rows are computed.
     const bool whole_stages = a.K % kBK == 0;
     if (a.M > 128) {
-        if (!whole_stages) return launch_tile<256, 256, 4, 2, EP>(a, stream);
+        // gemm_x32_kernel addresses a tile's weight rows as 32-bit byte
+        // offsets from its first row; for the GLU the up rows sit N rows
+        // further on.  Matrices too large for that take the 64-bit path.
+        const int64_t span = (EP == Epilogue::kGluBf16 ? (int64_t)a.N : 0) + 256;
+        const bool offs32 = span * (a.K / 4) < ((int64_t)1 << 32);
+        if (!whole_stages || !offs32) return launch_tile<256, 256, 4, 2, EP>(a, stream);
         // 256 x 256 tiles (8 waves of 64 x 128) unless they would leave at
         // least half of the 256 CUs idle; then 128 x 256 (8 waves of 64 x 64).
         constexpr int kCols = EP == Epilogue::kGluBf16 ? 128 : 256;

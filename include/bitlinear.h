@@ -269,13 +269,20 @@ int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu,
  * Stages (exposed so that each step can be compared on its own).
  * ------------------------------------------------------------------------- */
 
-/* RMSNorm + per-token absmax quantisation: q int8 [M][K] and s fp32 [M]
- * (q ~= s * RMSNorm(x)). */
+/* RMSNorm + per-token absmax quantisation ([jiqizhixin, "具有三值权重的
+ * MatMul-free 密集层", Algorithm 1: the activation quantiser fused with
+ * RMSNorm]; [datacamp, "Các thành phần lõi: MLGRU và GLU", panel "RMS norm":
+ * normalise before quantising]): q int8 [M][K] and s fp32 [M]
+ * (q ~= s * RMSNorm(x)).  Same arithmetic as the first half of
+ * bitlinear_forward. */
 int bitlinear_quantize(const uint16_t* x, const float* rms_weight, int64_t M, int64_t K,
                        float eps, int8_t* q, float* s, void* stream);
 
-/* Ternary accumulation alone: acc int32 [M][N] = sum_k q[m][k] * w[n][k]
- * from int8 q [M][K] and packed [N][K/4].  Workspace:
+/* Ternary accumulation alone ([ld246, "三值权重的应用"]: +1 adds the input,
+ * -1 subtracts it, 0 skips it; [jiqizhixin, "具有三值权重的 MatMul-free
+ * 密集层"]: the ternary product as additions and subtractions):
+ * acc int32 [M][N] = sum_k q[m][k] * w[n][k] from int8 q [M][K] and packed
+ * [N][K/4], exact.  Workspace:
  * bitlinear_forward_workspace_bytes(M, N, K). */
 int bitlinear_ternary_matmul_i32(const int8_t* q, const uint8_t* packed, int64_t M,
                                  int64_t N, int64_t K, int32_t* acc, void* ws,

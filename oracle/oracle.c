@@ -240,7 +240,10 @@ void orc_bitlinear(const uint16_t* x, const float* g, const float* W, int64_t M,
  * one gamma (gate = rows 0..F-1), SiLU(v) = v / (1 + exp(-v)) in fp64, and
  * the product is stored as bf16 (activations between layers are BF16,
  * [jiqizhixin, "MatMul-free 语言模型的扩展规律"]) before the down layer, which
- * applies its own RMSNorm and quantisation. */
+ * applies its own RMSNorm and quantisation.  The other reading of "two
+ * BitLinear layers" -- a gamma and an RMSNorm weight for each of gate and up
+ * -- ternarises differently wherever the two gammas differ; it is not the
+ * one implemented here. */
 void orc_glu_ternary(const uint16_t* x, const float* g_gu, const int8_t* w_gu,
                      float gamma_gu, const float* g_down, const int8_t* w_down,
                      float gamma_down, int64_t M, int64_t D, int64_t F, float eps,

@@ -163,3 +163,52 @@ def test_backward_workspace_query():
     small = L.bitlinear_backward_workspace_bytes(1, 16, 16)
     big = L.bitlinear_backward_workspace_bytes(8192, 2048, 2048)
     assert 0 < small < big and big % 256 == 0
+
+
+# --------------------------------------------------------------------------
+# The binding checks every caller-supplied output before a pointer reaches the
+# library.  The checks run dtype -> shape -> contiguity -> device, so CPU
+# tensors exercise every rejection except the device one, and the last case
+# shows a well-formed CPU tensor is still refused (it is not on the GPU).
+# --------------------------------------------------------------------------
+
+import torch  # noqa: E402
+
+
+def test_output_check_rejects_wrong_dtype():
+    like = torch.empty(4, 8)
+    with pytest.raises(TypeError):
+        bl._out(torch.empty(4, 8, dtype=torch.bfloat16), "y", (torch.float32,), (4, 8), like)
+    with pytest.raises(TypeError):
+        bl._out(None, "y", (torch.float32,), (4, 8), like)
+
+
+@pytest.mark.parametrize("shape", [(4, 7), (8, 4), (32,), (4, 8, 1), (5, 8)])
+def test_output_check_rejects_wrong_shape(shape):
+    like = torch.empty(4, 8)
+    with pytest.raises(ValueError, match="shape"):
+        bl._out(torch.empty(shape), "y", (torch.float32,), (4, 8), like)
+
+
+def test_output_check_rejects_non_contiguous():
+    like = torch.empty(4, 8)
+    t = torch.empty(8, 4).t()
+    assert t.shape == (4, 8) and not t.is_contiguous()
+    with pytest.raises(ValueError, match="contiguous"):
+        bl._out(t, "y", (torch.float32,), (4, 8), like)
+
+
+def test_output_check_rejects_host_tensor():
+    like = torch.empty(4, 8)
+    with pytest.raises(ValueError, match="must be on"):
+        bl._out(torch.empty(4, 8), "y", (torch.float32,), (4, 8), like)
+    with pytest.raises(ValueError, match="must be on"):
+        bl._new_or_out(torch.empty(4, 8), "y", torch.float32, (4, 8), like)
+    # a caller's workspace goes through the same device check
+    with pytest.raises(ValueError, match="must be on"):
+        bl._workspace(64, torch.empty(64, dtype=torch.uint8), like)
+
+
+def test_gamma_must_hold_one_value_per_matrix():
+    with pytest.raises(ValueError):  # a host tensor fails the device check first
+        bl._scalar(torch.ones(1), "gamma")

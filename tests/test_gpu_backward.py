@@ -93,6 +93,10 @@ SHAPES = [
     # RMSNorm backward: rows held in registers up to K = 4096 (full and
     # ragged last chunk), the two-pass form above
     (37, 64, 4096), (21, 40, 3856), (40, 50, 4160),
+    # dg from more than 64 partial sums, so the reduction over partials runs
+    # its chained steps: 128 partials on the register form, 138 on the
+    # two-pass form
+    (2048, 64, 256), (1100, 40, 4160),
 ]
 
 

@@ -248,6 +248,35 @@ def test_ternary_matmul_extremes():
         assert np.array_equal(acc, acc_ref)
 
 
+def test_ternary_matmul_tile_path_long_rows():
+    """The 256-row tile kernel at K = 8421632, where the byte offset of a
+    tile's last row, 255 * K, passes 2^31: 129 tiles of 256 x 256 (so the
+    256-row tiles are chosen), 256 x 33024 outputs.  The operands repeat a
+    seeded pattern -- q row m repeats its own 128 codes along k, weight row n
+    repeats pattern row n % 64 -- so acc[m][n] = (K / 128) * (the oracle's
+    product of the patterns)[m][n % 64], every one of the 8.5 M outputs
+    known.  About 72 GB of device memory."""
+    P, REP, M, NREP = 128, 65794, 256, 516
+    K, N = P * REP, 64 * NREP
+    assert 255 * K > 2 ** 31 and (N // 256) * (M // 256) > 128
+    r = wl.rng(11, wl.STREAM_X)
+    q_pat = r.integers(-127, 128, size=(M, P), dtype=np.int8)
+    w_pat = (r.integers(0, 3, size=(64, P)) - 1).astype(np.int8)
+    acc_pat = gu.orc().accumulate(q_pat, w_pat).astype(np.int64)
+    expect = (acc_pat * REP)[:, np.arange(N) % 64]
+    assert np.abs(expect).max() < 2 ** 31
+    _say("tile path, long rows: filling", M, N, K)
+    q = torch.empty((M, K), dtype=torch.int8, device=gu.DEV)
+    q.view(M, REP, P).copy_(gu.to_dev(q_pat).view(M, 1, P).expand(M, REP, P))
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=gu.DEV)
+    p_pat = gu.to_dev(gu.orc().pack(w_pat))  # [64, 32]: one 128-weight period per row
+    packed.view(NREP, 64, REP, P // 4).copy_(p_pat.view(1, 64, 1, P // 4).expand(NREP, 64, REP, P // 4))
+    acc = bl.bitlinear_ternary_matmul_i32(q, packed, kernel=MFMA).cpu().numpy()
+    del q, packed
+    torch.cuda.empty_cache()
+    assert np.array_equal(acc, expect.astype(np.int32))
+
+
 # --------------------------------------------------------------------------
 # end-to-end forward
 # --------------------------------------------------------------------------
