@@ -38,6 +38,11 @@ _SIGS = {
     "orc_glu": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P]),
     "orc_glu_ternary": (None, [_P, _P, _P, _F, _P, _P, _F, _I, _I, _I, _F, _P, _P]),
     "orc_bitlinear_backward": (None, [_P, _P, _P, _F, _P, _I, _I, _I, _F, _P, _P, _P]),
+    "orc_mlgru_scan": (None, [_P, _I, _I, _I, _P, _P]),
+    "orc_mlgru_ternary": (None, [_P, _P, _P, _F, _P, _P, _F, _I, _I, _I, _F, _P, _P, _P]),
+    "orc_mlgru": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P]),
+    "orc_lm_layer_ternary": (None, [_P, _P, _P, _F, _P, _P, _F, _P, _P, _F, _P, _P, _F, _I, _I, _I, _I,
+                                    _F, _P, _P, _P]),
 }
 
 
@@ -195,6 +200,69 @@ class Oracle:
                                _ptr(_c(w_down, np.int8)), float(gamma_down), M, D, F,
                                float(eps), _ptr(y), _ptr(h))
         return dict(y=y, h=h)
+
+    # MLGRU token mixer and the layer --------------------------------------
+    def mlgru_scan(self, z, state=None):
+        """z [B, T, 3d] pre-activations (z_f | z_c | z_g per token) ->
+        dict(p bf16 [B, T, d], state fp64 [B, d] = h_T); state holds h_0
+        (zeros when None)."""
+        z = _c(z, np.float64)
+        B, T, d3 = z.shape
+        d = d3 // 3
+        st = np.zeros((B, d), np.float64) if state is None else _c(state, np.float64).copy()
+        p = np.empty((B, T, d), np.uint16)
+        self.h.orc_mlgru_scan(_ptr(z), B, T, d, _ptr(st), _ptr(p))
+        return dict(p=p, state=st)
+
+    def mlgru_ternary(self, x_bits, g_in, w_in, gamma_in, g_out, w_out, gamma_out, state=None,
+                      eps=1e-6):
+        """x bf16 [B, T, d] -> dict(y fp64 [B, T, d], p bf16 [B, T, d],
+        state [B, d])."""
+        x_bits = _c(x_bits, np.uint16)
+        B, T, d = x_bits.shape
+        assert w_in.shape == (3 * d, d) and w_out.shape == (d, d)
+        st = np.zeros((B, d), np.float64) if state is None else _c(state, np.float64).copy()
+        y = np.empty((B, T, d), np.float64)
+        p = np.empty((B, T, d), np.uint16)
+        self.h.orc_mlgru_ternary(_ptr(x_bits), _ptr(_c(g_in, np.float32)), _ptr(_c(w_in, np.int8)),
+                                 float(gamma_in), _ptr(_c(g_out, np.float32)), _ptr(_c(w_out, np.int8)),
+                                 float(gamma_out), B, T, d, float(eps), _ptr(st), _ptr(y), _ptr(p))
+        return dict(y=y, p=p, state=st)
+
+    def mlgru(self, x_bits, g_in, W_in, g_out, W_out, state=None, eps=1e-6):
+        x_bits = _c(x_bits, np.uint16)
+        B, T, d = x_bits.shape
+        assert W_in.shape == (3 * d, d) and W_out.shape == (d, d)
+        st = np.zeros((B, d), np.float64) if state is None else _c(state, np.float64).copy()
+        y = np.empty((B, T, d), np.float64)
+        p = np.empty((B, T, d), np.uint16)
+        self.h.orc_mlgru(_ptr(x_bits), _ptr(_c(g_in, np.float32)), _ptr(_c(W_in, np.float32)),
+                         _ptr(_c(g_out, np.float32)), _ptr(_c(W_out, np.float32)), B, T, d, float(eps),
+                         _ptr(st), _ptr(y), _ptr(p))
+        return dict(y=y, p=p, state=st)
+
+    def lm_layer_ternary(self, x_bits, mlgru_w, glu_w, state=None, eps=1e-6):
+        """One layer, u = bf16(x + MLGRU(x)), out = bf16(u + GLU(u)).
+        mlgru_w = (g_in, w_in, gamma_in, g_out, w_out, gamma_out), glu_w =
+        (g_gu, w_gu, gamma_gu, g_down, w_down, gamma_down), ternary.  x bf16
+        [B, T, d] -> dict(out bf16 [B, T, d], u bf16 [B, T, d], state)."""
+        x_bits = _c(x_bits, np.uint16)
+        B, T, d = x_bits.shape
+        g_in, w_in, gamma_in, g_out, w_out, gamma_out = mlgru_w
+        g_gu, w_gu, gamma_gu, g_dn, w_dn, gamma_dn = glu_w
+        F = w_dn.shape[1]
+        assert w_in.shape == (3 * d, d) and w_out.shape == (d, d)
+        assert w_gu.shape == (2 * F, d) and w_dn.shape == (d, F)
+        st = np.zeros((B, d), np.float64) if state is None else _c(state, np.float64).copy()
+        out = np.empty((B, T, d), np.uint16)
+        u = np.empty((B, T, d), np.uint16)
+        self.h.orc_lm_layer_ternary(
+            _ptr(x_bits), _ptr(_c(g_in, np.float32)), _ptr(_c(w_in, np.int8)), float(gamma_in),
+            _ptr(_c(g_out, np.float32)), _ptr(_c(w_out, np.int8)), float(gamma_out),
+            _ptr(_c(g_gu, np.float32)), _ptr(_c(w_gu, np.int8)), float(gamma_gu),
+            _ptr(_c(g_dn, np.float32)), _ptr(_c(w_dn, np.int8)), float(gamma_dn),
+            B, T, d, F, float(eps), _ptr(st), _ptr(out), _ptr(u))
+        return dict(out=out, u=u, state=st)
 
     def backward(self, x_bits, g, w, gamma, dy, eps=1e-6):
         """Straight-through backward of the layer (w ternary [N, K], dy fp32

@@ -280,6 +280,115 @@ void orc_glu(const uint16_t* x, const float* g_gu, const float* W_gu,
 }
 
 /* ------------------------------------------------------------------------ */
+/* MLGRU token mixer                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* [datacamp, "Các thành phần lõi: MLGRU và GLU"]: the MLGRU takes the tokens
+ * of a sequence one at a time; each step combines the current token's
+ * embedding with the previous hidden state, the memory of earlier tokens,
+ * through element-wise operations and gates -- vectors of values between 0
+ * and 1 -- that decide how much of the previous state and of the current
+ * token carry on; [jiqizhixin, "MatMul-free 语言模型架构"]: a ternary RNN of
+ * element-wise products and accumulation, with the GRU as its base;
+ * [ld246, "线性操作的引入"]: the GRU's matrix products become element-wise
+ * operations (a linear GRU).  Readings (the pages print no equations):
+ *   - the state enters element-wise only (no state-to-state product), so
+ *     the gates are functions of the token alone, through BitLinear;
+ *   - one BitLinear of the token gives z = [z_f | z_c | z_g]: rows 0..d-1,
+ *     d..2d-1 and 2d..3d-1 of one [3d][d] ternary matrix with one gamma and
+ *     one RMSNorm weight, as for the GLU's fused gate|up;
+ *   - forget gate f = sigmoid(z_f), in (0, 1); candidate c = SiLU(z_c) (the
+ *     activation the pages name for the model); output gate
+ *     g = sigmoid(z_g);
+ *   - h_t = f * h_{t-1} + (1 - f) * c, element-wise, from a given h_0 (zero
+ *     for a new sequence);
+ *   - p_t = g * h_t is stored as bf16 (the activation type between BitLinear
+ *     layers) and mapped by a second BitLinear, [d][d], to the output.
+ * Everything here is fp64. */
+static double orc_sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+static double orc_silu(double v) { return v / (1.0 + exp(-v)); }
+
+void orc_mlgru_scan(const double* z, int64_t B, int64_t T, int64_t d, double* state,
+                    uint16_t* p) {
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t n = 0; n < d; ++n) {
+            double h = state[b * d + n];
+            for (int64_t t = 0; t < T; ++t) {
+                const double* zt = z + (b * T + t) * 3 * d;
+                double f = orc_sigmoid(zt[n]);
+                double c = orc_silu(zt[d + n]);
+                double g = orc_sigmoid(zt[2 * d + n]);
+                h = f * h + (1.0 - f) * c;
+                p[(b * T + t) * d + n] = orc_double_to_bf16(g * h);
+            }
+            state[b * d + n] = h;
+        }
+    }
+}
+
+void orc_mlgru_ternary(const uint16_t* x, const float* g_in, const int8_t* w_in,
+                       float gamma_in, const float* g_out, const int8_t* w_out,
+                       float gamma_out, int64_t B, int64_t T, int64_t d, float eps,
+                       double* state, double* y, uint16_t* p_out) {
+    int64_t M = B * T;
+    double* z = (double*)malloc((size_t)(M * 3 * d) * sizeof(double));
+    uint16_t* p = p_out ? p_out : (uint16_t*)malloc((size_t)(M * d) * sizeof(uint16_t));
+    orc_bitlinear_ternary(x, g_in, w_in, gamma_in, M, 3 * d, d, eps, z, NULL, NULL, NULL);
+    orc_mlgru_scan(z, B, T, d, state, p);
+    orc_bitlinear_ternary(p, g_out, w_out, gamma_out, M, d, d, eps, y, NULL, NULL, NULL);
+    free(z);
+    if (!p_out) free(p);
+}
+
+void orc_mlgru(const uint16_t* x, const float* g_in, const float* W_in, const float* g_out,
+               const float* W_out, int64_t B, int64_t T, int64_t d, float eps, double* state,
+               double* y, uint16_t* p_out) {
+    int8_t* w_in = (int8_t*)malloc((size_t)(3 * d * d));
+    int8_t* w_out = (int8_t*)malloc((size_t)(d * d));
+    float gamma_in = orc_absmean_gamma(W_in, 3 * d, d);
+    float gamma_out = orc_absmean_gamma(W_out, d, d);
+    orc_ternarize(W_in, 3 * d, d, gamma_in, w_in);
+    orc_ternarize(W_out, d, d, gamma_out, w_out);
+    orc_mlgru_ternary(x, g_in, w_in, gamma_in, g_out, w_out, gamma_out, B, T, d, eps, state,
+                      y, p_out);
+    free(w_in);
+    free(w_out);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One layer: token mixer, then channel mixer                                */
+/* ------------------------------------------------------------------------ */
+
+/* [jiqizhixin, "MatMul-free 语言模型架构"]: in the Metaformer view a layer is
+ * a token mixer followed by a channel mixer; here the MLGRU and the GLU.
+ * Readings: each mixer's output is added to its input (the residual
+ * connections of a Metaformer block; the normalisation is the RMSNorm inside
+ * each BitLinear), and the residual stream is bf16 between the mixers and
+ * at the layer output:
+ *   u = bf16(x + MLGRU(x)),   out = bf16(u + GLU(u)).
+ * u_out (bf16 [B*T][d]) may be NULL. */
+void orc_lm_layer_ternary(const uint16_t* x, const float* g_in, const int8_t* w_in,
+                          float gamma_in, const float* g_out, const int8_t* w_out,
+                          float gamma_out, const float* g_gu, const int8_t* w_gu,
+                          float gamma_gu, const float* g_down, const int8_t* w_down,
+                          float gamma_down, int64_t B, int64_t T, int64_t d, int64_t F,
+                          float eps, double* state, uint16_t* out, uint16_t* u_out) {
+    int64_t M = B * T;
+    double* y = (double*)malloc((size_t)(M * d) * sizeof(double));
+    uint16_t* u = u_out ? u_out : (uint16_t*)malloc((size_t)(M * d) * sizeof(uint16_t));
+    orc_mlgru_ternary(x, g_in, w_in, gamma_in, g_out, w_out, gamma_out, B, T, d, eps, state,
+                      y, NULL);
+    for (int64_t i = 0; i < M * d; ++i)
+        u[i] = orc_double_to_bf16((double)orc_bf16_to_float(x[i]) + y[i]);
+    orc_glu_ternary(u, g_gu, w_gu, gamma_gu, g_down, w_down, gamma_down, M, d, F, eps, y,
+                    NULL);
+    for (int64_t i = 0; i < M * d; ++i)
+        out[i] = orc_double_to_bf16((double)orc_bf16_to_float(u[i]) + y[i]);
+    free(y);
+    if (!u_out) free(u);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Backward pass through BitLinear (straight-through estimator)              */
 /* ------------------------------------------------------------------------ */
 

@@ -92,6 +92,37 @@ void orc_glu_ternary(const uint16_t* x, const float* g_gu, const int8_t* w_gu,
                      float gamma_down, int64_t M, int64_t D, int64_t F, float eps,
                      double* y, uint16_t* h_out);
 
+/* MLGRU recurrence from the pre-activations z [B][T][3d] (rows of each
+ * token: z_f | z_c | z_g): f = sigmoid(z_f), c = SiLU(z_c),
+ * g = sigmoid(z_g), h_t = f h_{t-1} + (1 - f) c, p_t = bf16(g h_t).
+ * state [B][d] holds h_0 on entry and h_T on return; p is bf16 [B][T][d].
+ * Readings in oracle.c. */
+void orc_mlgru_scan(const double* z, int64_t B, int64_t T, int64_t d, double* state,
+                    uint16_t* p);
+
+/* MLGRU token mixer: z = BitLinear(x; g_in, w_in [3d][d], gamma_in), the
+ * recurrence above, y = BitLinear(p; g_out, w_out [d][d], gamma_out).
+ * x bf16 [B][T][d], y fp64 [B][T][d], state as above, p_out (bf16
+ * [B][T][d]) may be NULL. */
+void orc_mlgru_ternary(const uint16_t* x, const float* g_in, const int8_t* w_in,
+                       float gamma_in, const float* g_out, const int8_t* w_out,
+                       float gamma_out, int64_t B, int64_t T, int64_t d, float eps,
+                       double* state, double* y, uint16_t* p_out);
+
+/* The same from the fp32 master weights W_in [3d][d] and W_out [d][d]. */
+void orc_mlgru(const uint16_t* x, const float* g_in, const float* W_in, const float* g_out,
+               const float* W_out, int64_t B, int64_t T, int64_t d, float eps, double* state,
+               double* y, uint16_t* p_out);
+
+/* One layer: u = bf16(x + MLGRU(x)), out = bf16(u + GLU(u)) (bf16 [B][T][d]);
+ * the GLU as orc_glu_ternary with inner size F. */
+void orc_lm_layer_ternary(const uint16_t* x, const float* g_in, const int8_t* w_in,
+                          float gamma_in, const float* g_out, const int8_t* w_out,
+                          float gamma_out, const float* g_gu, const int8_t* w_gu,
+                          float gamma_gu, const float* g_down, const int8_t* w_down,
+                          float gamma_down, int64_t B, int64_t T, int64_t d, int64_t F,
+                          float eps, double* state, uint16_t* out, uint16_t* u_out);
+
 /* Backward pass of BitLinear with the straight-through estimator, from a
  * ternarised w and its gamma: given dy [M][N] (fp32), writes dx [M][K],
  * dg [K] and dW [N][K] (fp64).  Readings in oracle.c. */

@@ -494,6 +494,176 @@ def pin_backward_single_feature_closed_form(orc):
     assert math.isclose(out["dg"][0], float((dxn * xf * r).sum()), rel_tol=1e-12)
 
 
+# --------------------------------------------------------------------------
+# MLGRU token mixer and the layer
+# --------------------------------------------------------------------------
+
+def _np_gates(z):
+    """f, c, g from z [..., 3d] straight from the definitions (numpy, fp64)."""
+    d = z.shape[-1] // 3
+    zf, zc, zg = z[..., :d], z[..., d:2 * d], z[..., 2 * d:]
+    return 1.0 / (1.0 + np.exp(-zf)), zc / (1.0 + np.exp(-zc)), 1.0 / (1.0 + np.exp(-zg))
+
+
+def _bf16_half_ulp(v):
+    """Half the bf16 spacing at |v| (8 significant bits)."""
+    _, e = np.frexp(np.abs(v))
+    return np.ldexp(1.0, e - 9)
+
+
+def pin_mlgru_scan_unrolled_sum(orc):
+    """The recurrence h_t = f_t h_{t-1} + (1 - f_t) c_t unrolled:
+    h_t = (prod_{r<=t} f_r) h_0 + sum_{s<=t} (prod_{s<r<=t} f_r)(1 - f_s) c_s,
+    evaluated term by term; p_t is g_t h_t rounded to the nearest bf16."""
+    r = wl.rng(21, 0)
+    B, T, d = 2, 13, 8
+    z = r.standard_normal((B, T, 3 * d)) * 2.0
+    h0 = r.standard_normal((B, d))
+    out = orc.mlgru_scan(z, h0)
+    f, c, g = _np_gates(z)
+    for b in range(B):
+        for t in range(T):
+            h = np.prod(f[b, :t + 1], axis=0) * h0[b]
+            for s_ in range(t + 1):
+                h = h + np.prod(f[b, s_ + 1:t + 1], axis=0) * (1.0 - f[b, s_]) * c[b, s_]
+            v = g[b, t] * h
+            pv = wl.bf16_bits_to_f32(out["p"][b, t]).astype(np.float64)
+            assert np.all(np.abs(pv - v) <= _bf16_half_ulp(v) * (1 + 1e-9) + 1e-300), (b, t)
+            if t == T - 1:
+                assert np.allclose(out["state"][b], h, rtol=1e-12, atol=1e-14)
+
+
+def pin_mlgru_constant_gates_closed_form(orc):
+    """Constant pre-activations: h_t = f^t h_0 + (1 - f^t) c (a geometric
+    approach to the candidate)."""
+    B, T, d = 1, 40, 4
+    zf, zc = np.array([-1.0, 0.3, 2.0, 0.0]), np.array([0.7, -2.0, 1.5, 3.0])
+    z = np.zeros((B, T, 3 * d))
+    z[..., :d], z[..., d:2 * d] = zf, zc
+    h0 = np.array([[1.0, -0.5, 0.25, 2.0]])
+    out = orc.mlgru_scan(z, h0)
+    f = 1.0 / (1.0 + np.exp(-zf))
+    c = zc / (1.0 + np.exp(-zc))
+    assert np.allclose(out["state"][0], f ** T * h0[0] + (1 - f ** T) * c, rtol=1e-12, atol=1e-15)
+
+
+def pin_mlgru_steps_convex_and_split(orc):
+    """Gates lie in (0, 1), so each new state lies between the previous state
+    and the candidate; and running the tokens one call at a time, carrying
+    the state, gives exactly the state of one call over the whole sequence."""
+    r = wl.rng(22, 0)
+    B, T, d = 3, 17, 12
+    z = r.standard_normal((B, T, 3 * d)) * 3.0
+    h = r.standard_normal((B, d))
+    whole = orc.mlgru_scan(z, h)
+    _, c, _ = _np_gates(z)
+    for t in range(T):
+        step = orc.mlgru_scan(z[:, t:t + 1], h)
+        lo, hi = np.minimum(h, c[:, t]), np.maximum(h, c[:, t])
+        assert np.all(step["state"] >= lo - 1e-15) and np.all(step["state"] <= hi + 1e-15)
+        assert np.array_equal(step["p"][:, 0], whole["p"][:, t])
+        h = step["state"]
+    assert np.array_equal(h, whole["state"])
+
+
+def _mlgru_case(r, d, gain=True):
+    g_in = (0.5 + r.random(d)).astype(np.float32) if gain else np.ones(d, np.float32)
+    g_out = (0.5 + r.random(d)).astype(np.float32) if gain else np.ones(d, np.float32)
+    W_in = (r.standard_normal((3 * d, d)) * 0.02).astype(np.float32)
+    W_out = (r.standard_normal((d, d)) * 0.02).astype(np.float32)
+    return g_in, W_in, g_out, W_out
+
+
+def pin_mlgru_zero_input(orc):
+    """x = 0: every code is 0, so z = 0, f = g = 1/2 and c = 0; the state
+    halves each step (exact powers of two) and p_t = 2^-(t+2) h_0 exactly."""
+    r = wl.rng(23, 0)
+    B, T, d = 2, 6, 32
+    g_in, W_in, g_out, W_out = _mlgru_case(r, d)
+    h0 = r.standard_normal((B, d))
+    out = orc.mlgru(np.zeros((B, T, d), np.uint16), g_in, W_in, g_out, W_out, h0)
+    assert np.array_equal(out["state"], h0 * 0.5 ** T)
+    for t in range(T):
+        v = h0 * 0.5 ** (t + 2)
+        pv = wl.bf16_bits_to_f32(out["p"][:, t]).astype(np.float64)
+        assert np.all(np.abs(pv - v) <= _bf16_half_ulp(v) * (1 + 1e-9))
+    h0z = orc.mlgru(np.zeros((B, T, d), np.uint16), g_in, W_in, g_out, W_out)
+    assert np.all(h0z["y"] == 0) and np.all(h0z["state"] == 0)
+
+
+def pin_mlgru_is_bitlinear_scan_bitlinear(orc):
+    """The token mixer maps every token of every sequence through the pinned
+    BitLinear with the input matrix (gain g_in), runs the pinned recurrence
+    along each sequence, and maps p through BitLinear with the output matrix
+    (gain g_out); from master weights it ternarises each matrix with its own
+    gamma."""
+    r = wl.rng(24, 0)
+    B, T, d = 2, 5, 48
+    g_in, W_in, g_out, W_out = _mlgru_case(r, d)
+    x = wl.x_normal(B * T, d, seed=24).reshape(B, T, d)
+    h0 = r.standard_normal((B, d))
+    out = orc.mlgru(x, g_in, W_in, g_out, W_out, h0)
+    gi, go = orc.gamma(W_in), orc.gamma(W_out)
+    wi, wo = orc.ternarize(W_in, gi), orc.ternarize(W_out, go)
+    z = orc.bitlinear_ternary(x.reshape(B * T, d), g_in, wi, gi)["y"].reshape(B, T, 3 * d)
+    sc = orc.mlgru_scan(z, h0)
+    assert np.array_equal(sc["p"], out["p"]) and np.array_equal(sc["state"], out["state"])
+    y = orc.bitlinear_ternary(sc["p"].reshape(B * T, d), g_out, wo, go)["y"].reshape(B, T, d)
+    assert np.array_equal(y, out["y"])
+    tern = orc.mlgru_ternary(x, g_in, wi, gi, g_out, wo, go, h0)
+    assert np.array_equal(tern["y"], out["y"])
+
+
+def _layer_weights(orc, r, d, F, zero_in=False, zero_gu=False):
+    g_in, W_in, g_out, W_out = _mlgru_case(r, d)
+    if zero_in:
+        W_in[:] = 0
+    g_gu = (0.5 + r.random(d)).astype(np.float32)
+    g_dn = (0.5 + r.random(F)).astype(np.float32)
+    W_gu = (r.standard_normal((2 * F, d)) * 0.02).astype(np.float32)
+    if zero_gu:
+        W_gu[:] = 0
+    W_dn = (r.standard_normal((d, F)) * 0.02).astype(np.float32)
+    t = []
+    for gain, W in ((g_in, W_in), (g_out, W_out), (g_gu, W_gu), (g_dn, W_dn)):
+        gm = orc.gamma(W)
+        t.append((gain, orc.ternarize(W, gm), gm))
+    return (t[0] + t[1]), (t[2] + t[3])
+
+
+def pin_layer_residual_identity(orc):
+    """With all-zero input and gate|up matrices both mixers output exactly 0
+    (z = 0 gives c = 0, hence p = 0, and SiLU(0) * 0 = 0), so the layer is
+    the identity on x, bit for bit, whatever the other matrices hold."""
+    r = wl.rng(25, 0)
+    B, T, d, F = 2, 4, 32, 48
+    mw, gw = _layer_weights(orc, r, d, F, zero_in=True, zero_gu=True)
+    x = wl.x_normal(B * T, d, seed=25).reshape(B, T, d)
+    out = orc.lm_layer_ternary(x, mw, gw)
+    assert np.array_equal(out["out"], x) and np.array_equal(out["u"], x)
+
+
+def pin_layer_is_token_then_channel_mixer(orc):
+    """u = bf16(x + MLGRU(x)) and out = bf16(u + GLU(u)), each sum rounded
+    once to the nearest bf16 (checked as within half a bf16 spacing), with
+    the pinned mixers; the state is the MLGRU's."""
+    r = wl.rng(26, 0)
+    B, T, d, F = 2, 3, 32, 64
+    mw, gw = _layer_weights(orc, r, d, F)
+    x = wl.x_normal(B * T, d, seed=26).reshape(B, T, d)
+    h0 = r.standard_normal((B, d))
+    out = orc.lm_layer_ternary(x, mw, gw, h0)
+    m = orc.mlgru_ternary(x, *mw, state=h0)
+    assert np.array_equal(out["state"], m["state"])
+    v = wl.bf16_bits_to_f32(x).astype(np.float64) + m["y"]
+    uf = wl.bf16_bits_to_f32(out["u"]).astype(np.float64)
+    assert np.all(np.abs(uf - v) <= _bf16_half_ulp(v) * (1 + 1e-9) + 1e-300)
+    gl = orc.glu_ternary(out["u"].reshape(B * T, d), *gw)["y"].reshape(B, T, d)
+    v2 = uf + gl
+    of = wl.bf16_bits_to_f32(out["out"]).astype(np.float64)
+    assert np.all(np.abs(of - v2) <= _bf16_half_ulp(v2) * (1 + 1e-9) + 1e-300)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -45,6 +45,23 @@ MUTANTS = [
     ("bwd_dxn_drops_gamma", "dxn[m * K + k] = (double)gamma * a;", "dxn[m * K + k] = a;"),
     ("bwd_sum_drops_gain", "S += dxn[m * K + k] * (double)g[k] * (double)orc_bf16_to_float(row[k]);",
      "S += dxn[m * K + k] * (double)orc_bf16_to_float(row[k]);"),
+    ("mlgru_forget_from_candidate_rows", "double f = orc_sigmoid(zt[n]);", "double f = orc_sigmoid(zt[d + n]);"),
+    ("mlgru_candidate_sigmoid", "double c = orc_silu(zt[d + n]);", "double c = orc_sigmoid(zt[d + n]);"),
+    ("mlgru_output_gate_silu", "double g = orc_sigmoid(zt[2 * d + n]);", "double g = orc_silu(zt[2 * d + n]);"),
+    ("mlgru_drops_one_minus_f", "h = f * h + (1.0 - f) * c;", "h = f * h + c;"),
+    ("mlgru_gate_roles_swapped", "h = f * h + (1.0 - f) * c;", "h = (1.0 - f) * h + f * c;"),
+    ("mlgru_no_output_gate", "p[(b * T + t) * d + n] = orc_double_to_bf16(g * h);",
+     "p[(b * T + t) * d + n] = orc_double_to_bf16(h);"),
+    ("mlgru_state_not_carried_in", "double h = state[b * d + n];", "double h = 0.0;"),
+    ("mlgru_state_not_returned", "            state[b * d + n] = h;\n", "            state[b * d + n] += 0.0 * h;\n"),
+    ("mlgru_token_stride", "const double* zt = z + (b * T + t) * 3 * d;", "const double* zt = z + (b * T + t) * d;"),
+    ("mlgru_out_gain_from_input", "orc_bitlinear_ternary(p, g_out, w_out, gamma_out,", "orc_bitlinear_ternary(p, g_in, w_out, gamma_out,"),
+    ("mlgru_master_one_gamma", "float gamma_out = orc_absmean_gamma(W_out, d, d);", "float gamma_out = orc_absmean_gamma(W_in, d, d);"),
+    ("layer_glu_reads_x", "orc_glu_ternary(u, g_gu, w_gu, gamma_gu,", "orc_glu_ternary(x, g_gu, w_gu, gamma_gu,"),
+    ("layer_drops_first_residual", "u[i] = orc_double_to_bf16((double)orc_bf16_to_float(x[i]) + y[i]);",
+     "u[i] = orc_double_to_bf16(y[i]);"),
+    ("layer_drops_second_residual", "out[i] = orc_double_to_bf16((double)orc_bf16_to_float(u[i]) + y[i]);",
+     "out[i] = orc_double_to_bf16(y[i]);"),
     ("bwd_dw_transposed_token", "a += (double)dy[m * N + n] * ((double)q[m * K + k]", "a += (double)dy[((m + 1) % M) * N + n] * ((double)q[m * K + k]"),
 ]
 
