@@ -52,6 +52,7 @@ _SIGNATURES = {
     "bitlinear_forward_workspace_bytes": (_S, [_I, _I, _I]),
     "bitlinear_forward": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P]),
     "bitlinear_forward_ex": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P, _INT]),
+    "bitlinear_forward_noalloc": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P]),
     "bitlinear_prepare_activations": (_INT, [_P, _P, _I, _I, _F, _P, _S, _P]),
     "bitlinear_forward_prepared": (_INT, [_P, _P, _I, _I, _I, _P, _P, _S, _P, _INT]),
     "bitlinear_forward_batched_workspace_bytes": (_S, [_I, _I, _I, _I]),
@@ -264,6 +265,24 @@ def bitlinear_forward(x, rms_weight, packed, gamma, eps=1e-6, y=None, ws=None, s
     _check(lib().bitlinear_forward_ex(_ptr(x), _ptr(rms_weight), _ptr(packed), _ptr(gamma), M, N, K,
                                       float(eps), _ptr(y), _ptr(ws), nbytes, _stream(stream),
                                       int(kernel)))
+    return y
+
+
+def bitlinear_forward_noalloc(x, rms_weight, packed, gamma, y, eps=1e-6, stream=None):
+    """bitlinear_forward without a workspace or any allocation: the caller
+    passes y fp32 [M, N]; the library's per-GPU scratch holds the activation
+    stage (at most BITLINEAR_NOALLOC_SCRATCH_BYTES)."""
+    _dev(x, "x", _BF16, 2)
+    _dev(rms_weight, "rms_weight", (torch.float32,), 1)
+    _dev(packed, "packed", (torch.uint8,), 2)
+    _scalar(gamma, "gamma")
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K or rms_weight.shape[0] != K:
+        raise ValueError("x, rms_weight and packed disagree on K")
+    _out(y, "y", (torch.float32,), (M, N), x)
+    _check(lib().bitlinear_forward_noalloc(_ptr(x), _ptr(rms_weight), _ptr(packed), _ptr(gamma), M, N, K,
+                                           float(eps), _ptr(y), _stream(stream)))
     return y
 
 

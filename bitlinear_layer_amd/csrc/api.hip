@@ -4,10 +4,19 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "bitlinear.h"
 #include "launch.h"
+
+// Scratch of bitlinear_forward_noalloc (the activation stage: int8 codes,
+// per-token scales and code sums), resident on every GPU the library runs
+// on from module load until the process ends.  In host code this name is a
+// host-side stand-in, not a device address: the address of each device's
+// copy comes from hipGetSymbolAddress (noalloc_scratch below), and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[BITLINEAR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -257,6 +266,30 @@ int pack_impl(const float* W, int64_t B, int64_t N, int64_t K, uint8_t* packed, 
                       "pack launch");
 }
 
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) on the first no-allocation call there.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+int noalloc_scratch(void** out) {
+    int dev = -1;
+    TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+    CHECK(dev >= 0 && dev < kMaxScratchDevices, BITLINEAR_ERR_UNSUPPORTED,
+          "device %d is beyond the %d devices the no-allocation scratch is tracked for", dev,
+          kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+        CHECK(p != nullptr && aligned(p, 256), BITLINEAR_ERR_HIP,
+              "the scratch array has no usable device address on device %d", dev);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BITLINEAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -322,6 +355,26 @@ int bitlinear_forward(const uint16_t* x, const float* rms_weight, const uint8_t*
                       const float* gamma, int64_t M, int64_t N, int64_t K, float eps, float* y,
                       void* ws, size_t ws_bytes, void* stream) {
     return forward_impl(x, rms_weight, packed, gamma, 1, M, N, K, eps, y, ws, ws_bytes, stream,
+                        BITLINEAR_KERNEL_AUTO);
+}
+
+int bitlinear_forward_noalloc(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                              const float* gamma, int64_t M, int64_t N, int64_t K, float eps,
+                              float* y, void* stream) {
+    // Sizes first: a call beyond the scratch is refused before any HIP call.
+    TRY(check_rows(M, "M"));
+    TRY(check_rows(N, "N"));
+    TRY(check_k(K, "K"));
+    if (M == 0 || N == 0) return BITLINEAR_OK;
+    CHECK(M * K <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    const size_t need = bl::act_stage_bytes(M, K);
+    CHECK(need <= (size_t)BITLINEAR_NOALLOC_SCRATCH_BYTES, BITLINEAR_ERR_INVALID_ARG,
+          "bitlinear_forward_noalloc: M=%lld, K=%lld need %zu bytes of scratch, more than the %zu it "
+          "holds (use bitlinear_forward with a workspace)",
+          (long long)M, (long long)K, need, (size_t)BITLINEAR_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    TRY(noalloc_scratch(&ws));
+    return forward_impl(x, rms_weight, packed, gamma, 1, M, N, K, eps, y, ws, need, stream,
                         BITLINEAR_KERNEL_AUTO);
 }
 

@@ -37,8 +37,10 @@
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers to caller-owned memory; the library
- *     allocates nothing and keeps no device state.  All matrices are
- *     row-major and densely packed (row stride = row length).
+ *     allocates nothing and keeps no device state, apart from the fixed
+ *     scratch array of bitlinear_forward_noalloc (part of the loaded code,
+ *     one per GPU).  All matrices are row-major and densely packed (row
+ *     stride = row length).
  *   - x and h are bf16 stored as uint16 bit patterns.  W and rms weights are
  *     fp32.  gamma is a device fp32 scalar (no host round trip).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
@@ -196,6 +198,28 @@ int bitlinear_forward_ex(const uint16_t* x, const float* rms_weight,
                          const uint8_t* packed, const float* gamma, int64_t M, int64_t N,
                          int64_t K, float eps, float* y, void* ws, size_t ws_bytes,
                          void* stream, int kernel);
+
+/* Bytes of device scratch that bitlinear_forward_noalloc holds per GPU. */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+
+/* bitlinear_forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without a workspace, the same kernels and bit-identical y.  The
+ * activation stage lives in a static device array of
+ * BITLINEAR_NOALLOC_SCRATCH_BYTES (48 MiB), one per GPU, held from the
+ * library's load until the process ends; the call allocates nothing and
+ * calls no allocating routine.  Limit: bitlinear_forward_workspace_bytes(M,
+ * N, K) <= BITLINEAR_NOALLOC_SCRATCH_BYTES (M * K up to about 50 M codes,
+ * e.g. 16384 x 2560); larger calls return BITLINEAR_ERR_INVALID_ARG before
+ * touching the GPU.  The first call on each device looks up that device's
+ * array (hipGetSymbolAddress) with the device current: make it before any
+ * graph capture, on the stream's device.  Every call on one GPU shares its
+ * array, and nothing in it needs clearing (each call writes every byte it
+ * reads); calls that overlap in time on one GPU (other streams, other
+ * threads) race on it, so order them. */
+int bitlinear_forward_noalloc(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
+                              const float* gamma, int64_t M, int64_t N, int64_t K, float eps,
+                              float* y, void* stream);
 
 /* The two halves of bitlinear_forward, for callers that feed one input to
  * several weight matrices (quantise once, multiply many times) or that time

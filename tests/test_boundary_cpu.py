@@ -212,3 +212,16 @@ def test_output_check_rejects_host_tensor():
 def test_gamma_must_hold_one_value_per_matrix():
     with pytest.raises(ValueError):  # a host tensor fails the device check first
         bl._scalar(torch.ones(1), "gamma")
+
+
+def test_noalloc_rejects_before_touching_the_gpu():
+    """bitlinear_forward_noalloc refuses a stage larger than its fixed
+    scratch (and bad sizes) before any HIP call."""
+    L = bl.lib()
+    big_m = (48 << 20) // 2048 + 1
+    assert L.bitlinear_forward_noalloc(FAKE, FAKE, FAKE, FAKE, big_m, 64, 2048, 1e-6, FAKE, None) == \
+        bl.BITLINEAR_ERR_INVALID_ARG
+    assert "scratch" in bl.bitlinear_last_error()
+    assert L.bitlinear_forward_noalloc(FAKE, FAKE, FAKE, FAKE, 4, 64, 24, 1e-6, FAKE, None) == \
+        bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_forward_noalloc(None, None, None, None, 0, 64, 64, 1e-6, None, None) == bl.BITLINEAR_OK
