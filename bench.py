@@ -403,6 +403,157 @@ def vendor_int8_gemm_us(torch, M, N, K, steps, warmup, stream):
     return ev * 1e3
 
 
+def bench_mlgru_scan(torch, bl, wl, B, T, d, steps, warmup, stream):
+    """The MLGRU recurrence alone (bitlinear_mlgru_scan) from fp32
+    pre-activations z [B, T, 3d]: algorithmic bytes are z read once (12 per
+    token and channel), p written once (2) and the state read and written
+    (8 per channel)."""
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    z = torch.randn((B, T, 3 * d), generator=gen, device=DEV, dtype=torch.float32) * 2.0
+    state = torch.zeros((B, d), dtype=torch.float32, device=DEV)
+    p = torch.empty((B, T, d), dtype=torch.int16, device=DEV)
+    ws = torch.empty(max(1, bl.bitlinear_mlgru_scan_workspace_bytes(B, T, d)), dtype=torch.uint8, device=DEV)
+    wall, ev = timed_loop(torch, lambda: bl.bitlinear_mlgru_scan(z, state, p=p, ws=ws), steps, warmup, stream)
+    nbytes = 14 * B * T * d + 8 * B * d
+    del z, state, p, ws
+    torch.cuda.empty_cache()
+    return dict(B=B, T=T, d=d, us=ev * 1e3, us_wall=wall * 1e3, algorithmic_bytes=nbytes,
+                gbps=nbytes / (ev * 1e-3) / 1e9, frac_hbm=nbytes / (ev * 1e-3) / HBM_PEAK)
+
+
+def make_layer(torch, bl, wl, d, F, seed=0):
+    """One layer's weights, packed on the device: MLGRU in [3d, d] and out
+    [d, d], GLU gate|up [2F, d] and down [d, F]; RMSNorm gains of 1."""
+    def packed(N, K, layer):
+        return bl.bitlinear_pack_weights(wl.w_normal_device(N, K, seed=seed, layer=layer, device=DEV))
+
+    ones = lambda n: torch.ones(n, dtype=torch.float32, device=DEV)  # noqa: E731
+    pin, gin = packed(3 * d, d, 0)
+    pout, gout = packed(d, d, 1)
+    pgu, ggu = packed(2 * F, d, 2)
+    pdn, gdn = packed(d, F, 3)
+    mw = (ones(d), pin, gin, ones(d), pout, gout)
+    gw = (ones(d), pgu, ggu, ones(F), pdn, gdn)
+    weight_bytes = sum(t.numel() * t.element_size() for t in mw + gw)
+    return mw, gw, weight_bytes
+
+
+def bench_layer_prefill(torch, bl, wl, B, T, d, F, steps, warmup, stream):
+    """One layer (MLGRU token mixer, then GLU channel mixer, residuals in
+    bf16) over B sequences of T tokens, the pages' inference setting at B =
+    1, T = 2048: latency per layer and the device memory one layer holds
+    (packed weights and gains, input, output, state and workspace)."""
+    mw, gw, wbytes = make_layer(torch, bl, wl, d, F)
+    x = torch.from_numpy(wl.x_normal(B * T, d, seed=3).view("int16")).to(DEV).view(B, T, d)
+    state = torch.zeros((B, d), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, T, d), dtype=torch.int16, device=DEV)
+    wsb = bl.bitlinear_layer_workspace_bytes(B, T, d, F)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+
+    def step():
+        state.zero_()
+        bl.bitlinear_layer_forward(x, mw, gw, state, out=out, ws=ws)
+
+    wall, ev = timed_loop(torch, step, steps, warmup, stream)
+    ops = 2.0 * B * T * d * (3 * d + d + 3 * F)
+    act = 2 * x.numel() * 2 + 4 * state.numel()
+    del x, state, out, ws, mw, gw
+    torch.cuda.empty_cache()
+    return dict(B=B, T=T, d=d, F=F, us=ev * 1e3, us_wall=wall * 1e3, ms=ev, tokens_per_s=B * T / (ev * 1e-3),
+                int8_ops=ops, tops=ops / (ev * 1e-3) / 1e12, weight_bytes=wbytes, activation_bytes=act,
+                workspace_bytes=wsb, memory_gb=(wbytes + act + wsb) / 1e9)
+
+
+def bench_layer_decode(torch, bl, wl, d, F, tokens, steps, warmup, stream):
+    """Decoding one sequence through one layer, one token per call with the
+    state carried (T = 1, B = 1): `tokens` consecutive calls captured into
+    one HIP graph and replayed, and the same calls issued eagerly."""
+    mw, gw, wbytes = make_layer(torch, bl, wl, d, F, seed=1)
+    x = torch.from_numpy(wl.x_normal(tokens, d, seed=4).view("int16")).to(DEV).view(1, tokens, d)
+    xs = [x[:, t:t + 1].contiguous() for t in range(tokens)]
+    state = torch.zeros((1, d), dtype=torch.float32, device=DEV)
+    outs = [torch.empty((1, 1, d), dtype=torch.int16, device=DEV) for _ in range(tokens)]
+    ws = torch.empty(bl.bitlinear_layer_workspace_bytes(1, 1, d, F), dtype=torch.uint8, device=DEV)
+
+    def calls():
+        for t in range(tokens):
+            bl.bitlinear_layer_forward(xs[t], mw, gw, state, out=outs[t], ws=ws)
+
+    wall_e, ev_e = timed_loop(torch, calls, 3, 1, stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    wall, ev = timed_loop(torch, graph.replay, steps, warmup, stream)
+    del graph, x, xs, state, outs, ws, mw, gw
+    torch.cuda.empty_cache()
+    return dict(d=d, F=F, tokens=tokens, us_per_token_graph=ev * 1e3 / tokens,
+                us_per_token_eager=ev_e * 1e3 / tokens, weight_bytes=wbytes,
+                weight_gbps_graph=wbytes / (ev * 1e-3 / tokens) / 1e9,
+                ms_per_2048_tokens_graph=ev / tokens * 2048)
+
+
+def bench_crossover(torch, bl, wl, K, N, Ms, steps, warmup, stream):
+    """Each kernel choice of bitlinear_forward_ex at M tokens of one layer
+    shape: about 1 GiB of cold weights, one call per layer captured into a
+    HIP graph and replayed; microseconds per call.  The crossover is the
+    smallest M at which the int8 MFMA path beats the best streaming path
+    (the fused decode kernel or the GEMV)."""
+    L = max(32, (1 << 30) // (N * K // 4))
+    packed = torch.empty((L, N, K // 4), dtype=torch.uint8, device=DEV)
+    gamma = torch.empty(L, dtype=torch.float32, device=DEV)
+    wsp = torch.empty(bl.bitlinear_pack_workspace_bytes(N, K), dtype=torch.uint8, device=DEV)
+    for layer in range(L):
+        W = wl.w_normal_device(N, K, seed=5, layer=layer, device=DEV)
+        bl.bitlinear_pack_weights(W, packed=packed[layer], gamma=gamma[layer:layer + 1], ws=wsp)
+        del W
+    g = torch.ones(K, dtype=torch.float32, device=DEV)
+    names = {bl.BITLINEAR_KERNEL_AUTO: "auto", bl.BITLINEAR_KERNEL_DECODE: "decode",
+             bl.BITLINEAR_KERNEL_GEMV: "gemv", bl.BITLINEAR_KERNEL_MFMA: "mfma"}
+    table = {}
+    for M in Ms:
+        x = torch.from_numpy(wl.x_normal(M, K, seed=M).view("int16")).to(DEV)
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        ws = torch.empty(bl.bitlinear_forward_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+        kernels = [bl.BITLINEAR_KERNEL_AUTO, bl.BITLINEAR_KERNEL_MFMA]
+        if M <= 8:
+            kernels.append(bl.BITLINEAR_KERNEL_GEMV)
+        if bl.bitlinear_decode_supported(M, K):
+            kernels.append(bl.BITLINEAR_KERNEL_DECODE)
+        row = {}
+        for kern in kernels:
+            def calls(kern=kern):
+                for layer in range(L):
+                    bl.bitlinear_forward(x, g, packed[layer], gamma[layer:layer + 1], y=y, ws=ws, kernel=kern)
+
+            calls()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                calls()
+            torch.cuda.synchronize()
+            _, ev = timed_loop(torch, graph.replay, steps, warmup, stream)
+            row[names[kern]] = round(ev * 1e3 / L, 3)
+            del graph
+        stream_best = min([row[k] for k in ("decode", "gemv") if k in row], default=None)
+        row["fastest"] = min((v, k) for k, v in row.items() if k != "auto")[1]
+        row["auto_vs_fastest"] = round(row["auto"] / row[row["fastest"]], 3)
+        row["mfma_beats_streaming"] = None if stream_best is None else bool(row["mfma"] < stream_best)
+        table[M] = row
+        del x, y, ws
+    crossover = next((M for M in Ms if table[M]["mfma_beats_streaming"]), None)
+    del packed, gamma, wsp
+    torch.cuda.empty_cache()
+    return dict(K=K, N=N, layers=L, us_per_call=table, crossover_m=crossover)
+
+
 # --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
@@ -524,7 +675,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="run only these secondary workloads after the headline (comma-separated; "
-                         "available: backward)")
+                         "available: backward, layer, crossover)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay line (its 1024-node graphs are slow under counter collection)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -596,6 +747,21 @@ def main():
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
+
+    if (not args.no_secondary and not only) or "layer" in only:
+        log("[bench] MLGRU scan, one sequence of 2048 tokens, d = 2048")
+        secondary["mlgru_scan_b1_t2048_d2048"] = bench_mlgru_scan(torch, bl, wl, 1, 2048, 2048, 20, 3, stream)
+        secondary["mlgru_scan_b64_t256_d2048"] = bench_mlgru_scan(torch, bl, wl, 64, 256, 2048, 10, 2, stream)
+        log("[bench] one layer (MLGRU + GLU), batch 1, 2048 tokens")
+        secondary["layer_prefill_b1_t2048"] = bench_layer_prefill(torch, bl, wl, 1, 2048, 2048, 5632, 10, 2, stream)
+        log("[bench] one layer, decoding 64 tokens one call each")
+        secondary["layer_decode_b1"] = bench_layer_decode(torch, bl, wl, 2048, 5632, 64, 10, 2, stream)
+
+    if (not args.no_secondary and not only) or "crossover" in only:
+        for K2, N2 in ((2560, 2560), (2560, 6912), (6912, 2560)):
+            log(f"[bench] kernel crossover K={K2} N={N2}")
+            secondary[f"crossover_k{K2}_n{N2}"] = bench_crossover(torch, bl, wl, K2, N2,
+                                                                  (1, 2, 4, 8, 16, 32, 64, 128), 5, 1, stream)
 
     if (not args.no_secondary and not only) or "backward" in only:
         log("[bench] backward (straight-through) 8192 x 2048 x 2048")

@@ -65,6 +65,12 @@ _SIGNATURES = {
     "bitlinear_glu_hidden": (_INT, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _S, _P, _INT]),
     "bitlinear_quantize": (_INT, [_P, _P, _I, _I, _F, _P, _P, _P]),
     "bitlinear_ternary_matmul_i32": (_INT, [_P, _P, _I, _I, _I, _P, _P, _S, _P, _INT]),
+    "bitlinear_mlgru_scan_workspace_bytes": (_S, [_I, _I, _I]),
+    "bitlinear_mlgru_scan": (_INT, [_P, _I, _I, _I, _P, _P, _P, _S, _P]),
+    "bitlinear_mlgru_workspace_bytes": (_S, [_I, _I, _I]),
+    "bitlinear_mlgru_forward": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
+    "bitlinear_layer_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "bitlinear_layer_forward": (_INT, [_P] * 13 + [_I, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "bitlinear_backward_workspace_bytes": (_S, [_I, _I, _I]),
     "bitlinear_backward": (_INT, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _S, _P]),
 }
@@ -418,6 +424,97 @@ def bitlinear_glu_hidden(x, rms_w_gu, packed_gu, gamma_gu, eps=1e-6, h=None, ws=
                                       F, float(eps), _ptr(h), _ptr(ws), nbytes, _stream(stream),
                                       int(kernel)))
     return h
+
+
+# --------------------------------------------------------------------------
+# MLGRU token mixer and one layer
+# --------------------------------------------------------------------------
+
+def bitlinear_mlgru_scan_workspace_bytes(B, T, d):
+    return lib().bitlinear_mlgru_scan_workspace_bytes(B, T, d)
+
+
+def bitlinear_mlgru_scan(z, state, p=None, ws=None, stream=None):
+    """The recurrence from pre-activations z fp32 [B, T, 3d]: returns p bf16
+    (int16 bits) [B, T, d]; state fp32 [B, d] is updated in place (h_0 in,
+    h_T out)."""
+    _dev(z, "z", (torch.float32,), 3)
+    B, T, d3 = z.shape
+    d = d3 // 3
+    if d3 != 3 * d:
+        raise ValueError("z must hold 3d pre-activations per token")
+    _out(state, "state", (torch.float32,), (B, d), z)
+    p = _new_or_out(p, "p", torch.int16, (B, T, d), z, _BF16)
+    ws, nbytes = _workspace(bitlinear_mlgru_scan_workspace_bytes(B, T, d), ws, z)
+    _check(lib().bitlinear_mlgru_scan(_ptr(z), B, T, d, _ptr(state), _ptr(p), _ptr(ws), nbytes,
+                                      _stream(stream)))
+    return p
+
+
+def bitlinear_mlgru_workspace_bytes(B, T, d):
+    return lib().bitlinear_mlgru_workspace_bytes(B, T, d)
+
+
+def _mlgru_weights(d, rms_w_in, packed_in, gamma_in, rms_w_out, packed_out, gamma_out):
+    _dev(rms_w_in, "rms_w_in", (torch.float32,), 1)
+    _dev(packed_in, "packed_in", (torch.uint8,), 2)
+    _scalar(gamma_in, "gamma_in")
+    _dev(rms_w_out, "rms_w_out", (torch.float32,), 1)
+    _dev(packed_out, "packed_out", (torch.uint8,), 2)
+    _scalar(gamma_out, "gamma_out")
+    if (tuple(packed_in.shape) != (3 * d, d // 4) or tuple(packed_out.shape) != (d, d // 4)
+            or rms_w_in.shape[0] != d or rms_w_out.shape[0] != d):
+        raise ValueError("MLGRU matrix shapes disagree with x")
+
+
+def bitlinear_mlgru_forward(x, rms_w_in, packed_in, gamma_in, rms_w_out, packed_out, gamma_out, state,
+                            eps=1e-6, y=None, ws=None, stream=None):
+    """Token mixer: x bf16 [B, T, d] -> y fp32 [B, T, d]; packed_in [3d, d/4]
+    (rows f | c | g), packed_out [d, d/4]; state fp32 [B, d] updated in
+    place (h_0 in, h_T out)."""
+    _dev(x, "x", _BF16, 3)
+    B, T, d = x.shape
+    _mlgru_weights(d, rms_w_in, packed_in, gamma_in, rms_w_out, packed_out, gamma_out)
+    _out(state, "state", (torch.float32,), (B, d), x)
+    y = _new_or_out(y, "y", torch.float32, (B, T, d), x)
+    ws, nbytes = _workspace(bitlinear_mlgru_workspace_bytes(B, T, d), ws, x)
+    _check(lib().bitlinear_mlgru_forward(_ptr(x), _ptr(rms_w_in), _ptr(packed_in), _ptr(gamma_in),
+                                         _ptr(rms_w_out), _ptr(packed_out), _ptr(gamma_out), B, T, d,
+                                         float(eps), _ptr(state), _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def bitlinear_layer_workspace_bytes(B, T, d, F):
+    return lib().bitlinear_layer_workspace_bytes(B, T, d, F)
+
+
+def bitlinear_layer_forward(x, mlgru_w, glu_w, state, eps=1e-6, out=None, ws=None, stream=None):
+    """One layer, u = bf16(x + MLGRU(x)), out = bf16(u + GLU(u)): x bf16
+    [B, T, d] -> out bf16 (int16 bits) [B, T, d].  mlgru_w = (rms_w_in,
+    packed_in, gamma_in, rms_w_out, packed_out, gamma_out); glu_w = (rms_w_gu,
+    packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down); state fp32
+    [B, d] updated in place."""
+    _dev(x, "x", _BF16, 3)
+    B, T, d = x.shape
+    _mlgru_weights(d, *mlgru_w)
+    rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down = glu_w
+    _dev(rms_w_gu, "rms_w_gu", (torch.float32,), 1)
+    _dev(packed_gu, "packed_gu", (torch.uint8,), 2)
+    _scalar(gamma_gu, "gamma_gu")
+    _dev(rms_w_down, "rms_w_down", (torch.float32,), 1)
+    _dev(packed_down, "packed_down", (torch.uint8,), 2)
+    _scalar(gamma_down, "gamma_down")
+    F = packed_down.shape[1] * 4
+    if (tuple(packed_gu.shape) != (2 * F, d // 4) or packed_down.shape[0] != d
+            or rms_w_gu.shape[0] != d or rms_w_down.shape[0] != F):
+        raise ValueError("GLU matrix shapes disagree with x")
+    _out(state, "state", (torch.float32,), (B, d), x)
+    out = _new_or_out(out, "out", torch.int16, (B, T, d), x, _BF16)
+    ws, nbytes = _workspace(bitlinear_layer_workspace_bytes(B, T, d, F), ws, x)
+    _check(lib().bitlinear_layer_forward(_ptr(x), *[_ptr(t) for t in mlgru_w], *[_ptr(t) for t in glu_w],
+                                         B, T, d, F, float(eps), _ptr(state), _ptr(out), _ptr(ws), nbytes,
+                                         _stream(stream)))
+    return out
 
 
 # --------------------------------------------------------------------------

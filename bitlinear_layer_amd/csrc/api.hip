@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -266,6 +267,91 @@ int pack_impl(const float* W, int64_t B, int64_t N, int64_t K, uint8_t* packed, 
                       "pack launch");
 }
 
+// Workspace of the MLGRU token mixer over M = B * T tokens: one activation
+// stage (reused by the input and the output projection), the
+// pre-activations z fp32 [M][3d], the gated state p bf16 [M][d] and the
+// scan's chunk summaries; each part 256-byte aligned.
+struct MlgruWs {
+    char* act;
+    float* z;
+    uint16_t* p;
+    void* scan;
+    size_t act_bytes;
+};
+
+size_t mlgru_ws_bytes(int64_t B, int64_t T, int64_t d) {
+    const int64_t M = B * T;
+    return bl::act_stage_bytes(M, d) + (size_t)bl::round_up(M * 3 * d * 4, 256) +
+           (size_t)bl::round_up(M * d * 2, 256) + bl::mlgru_scan_workspace_bytes(B, T, d);
+}
+
+MlgruWs mlgru_ws_carve(void* base, int64_t B, int64_t T, int64_t d) {
+    const int64_t M = B * T;
+    char* w = static_cast<char*>(base);
+    MlgruWs m;
+    m.act = w;
+    m.act_bytes = bl::act_stage_bytes(M, d);
+    w += m.act_bytes;
+    m.z = reinterpret_cast<float*>(w);
+    w += bl::round_up(M * 3 * d * 4, 256);
+    m.p = reinterpret_cast<uint16_t*>(w);
+    w += bl::round_up(M * d * 2, 256);
+    m.scan = w;
+    return m;
+}
+
+int check_mlgru_shape(int64_t B, int64_t T, int64_t d) {
+    TRY(check_rows(B, "B"));
+    TRY(check_rows(T, "T"));
+    TRY(check_k(d, "d"));
+    CHECK(B * T <= BITLINEAR_MAX_DIM, BITLINEAR_ERR_INVALID_ARG, "B*T exceeds BITLINEAR_MAX_DIM");
+    CHECK(B * T * 3 * d <= kMaxElems && 3 * d * d <= kMaxElems, BITLINEAR_ERR_INVALID_ARG,
+          "matrix too large");
+    return BITLINEAR_OK;
+}
+
+// The token mixer: z = BitLinear_in(x) over all B*T tokens, the recurrence,
+// y = BitLinear_out(p).  The projections go through the forward's own
+// dispatch (fused decode kernel for a few tokens, MFMA tiles for many).
+int mlgru_impl(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
+               const float* gamma_in, const float* rms_w_out, const uint8_t* packed_out,
+               const float* gamma_out, int64_t B, int64_t T, int64_t d, float eps, float* state,
+               float* y, void* ws, size_t ws_bytes, hipStream_t st) {
+    TRY(check_mlgru_shape(B, T, d));
+    TRY(check_eps(eps));
+    if (B == 0 || T == 0) return BITLINEAR_OK;
+    CHECK_PTR(x);
+    CHECK_PTR(rms_w_in);
+    CHECK_PTR(packed_in);
+    CHECK_SCALAR(gamma_in);
+    CHECK_PTR(rms_w_out);
+    CHECK_PTR(packed_out);
+    CHECK_SCALAR(gamma_out);
+    CHECK_PTR(state);
+    CHECK_PTR(y);
+    TRY(check_ws(ws, ws_bytes, mlgru_ws_bytes(B, T, d)));
+    const MlgruWs w = mlgru_ws_carve(ws, B, T, d);
+    const int64_t M = B * T;
+    TRY(forward_impl(x, rms_w_in, packed_in, gamma_in, 1, M, 3 * d, d, eps, w.z, w.act, w.act_bytes,
+                     st, BITLINEAR_KERNEL_AUTO));
+    TRY(hip_status(bl::launch_mlgru_scan(w.z, B, T, d, state, w.p, w.scan, st), "mlgru scan launch"));
+    return forward_impl(w.p, rms_w_out, packed_out, gamma_out, 1, M, d, d, eps, y, w.act, w.act_bytes, st,
+                        BITLINEAR_KERNEL_AUTO);
+}
+
+// Workspace of one layer: a region shared by the two mixers (each needs it
+// only while it runs), the mixers' fp32 outputs [M][d] and the bf16 residual
+// stream u [M][d] between them.
+size_t layer_shared_bytes(int64_t B, int64_t T, int64_t d, int64_t F) {
+    return std::max(mlgru_ws_bytes(B, T, d), bitlinear_glu_workspace_bytes(B * T, d, F));
+}
+
+size_t layer_ws_bytes(int64_t B, int64_t T, int64_t d, int64_t F) {
+    const int64_t M = B * T;
+    return bl::round_up((int64_t)layer_shared_bytes(B, T, d, F), 256) + (size_t)bl::round_up(M * d * 4, 256) +
+           (size_t)bl::round_up(M * d * 2, 256);
+}
+
 // Device address of this GPU's copy of `scratch`, looked up once per device
 // (with that device current) on the first no-allocation call there.
 constexpr int kMaxScratchDevices = 64;
@@ -288,6 +374,38 @@ int noalloc_scratch(void** out) {
     }
     *out = g_scratch_ptr[dev];
     return BITLINEAR_OK;
+}
+
+int layer_impl(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
+               const float* gamma_in, const float* rms_w_out, const uint8_t* packed_out,
+               const float* gamma_out, const float* rms_w_gu, const uint8_t* packed_gu,
+               const float* gamma_gu, const float* rms_w_down, const uint8_t* packed_down,
+               const float* gamma_down, int64_t B, int64_t T, int64_t d, int64_t F, float eps,
+               float* state, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t st) {
+    TRY(check_mlgru_shape(B, T, d));
+    TRY(check_k(F, "F"));
+    TRY(check_eps(eps));
+    CHECK(B * T * F <= kMaxElems && 2 * F * d <= kMaxElems, BITLINEAR_ERR_INVALID_ARG, "matrix too large");
+    if (B == 0 || T == 0) return BITLINEAR_OK;
+    CHECK_PTR(out);
+    CHECK_PTR(rms_w_gu);
+    CHECK_PTR(packed_gu);
+    CHECK_SCALAR(gamma_gu);
+    CHECK_PTR(rms_w_down);
+    CHECK_PTR(packed_down);
+    CHECK_SCALAR(gamma_down);
+    TRY(check_ws(ws, ws_bytes, layer_ws_bytes(B, T, d, F)));
+    const int64_t M = B * T;
+    char* base = static_cast<char*>(ws);
+    const size_t shared = (size_t)bl::round_up((int64_t)layer_shared_bytes(B, T, d, F), 256);
+    float* ymix = reinterpret_cast<float*>(base + shared);
+    uint16_t* u = reinterpret_cast<uint16_t*>(base + shared + bl::round_up(M * d * 4, 256));
+    TRY(mlgru_impl(x, rms_w_in, packed_in, gamma_in, rms_w_out, packed_out, gamma_out, B, T, d, eps, state,
+                   ymix, base, mlgru_ws_bytes(B, T, d), st));
+    TRY(hip_status(bl::launch_residual_bf16(x, ymix, u, M * d, st), "residual launch"));
+    TRY(glu_impl(u, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down, 1, M, d, F, eps,
+                 ymix, base, bitlinear_glu_workspace_bytes(M, d, F), st));
+    return hip_status(bl::launch_residual_bf16(u, ymix, out, M * d, st), "residual launch");
 }
 
 }  // namespace
@@ -556,6 +674,54 @@ int bitlinear_backward(const uint16_t* x, const float* rms_weight, const uint8_t
     TRY(check_ws(ws, ws_bytes, bl::backward_workspace_bytes(M, N, K)));
     bl::BackwardArgs a{x, rms_weight, packed, gamma, dy, M, N, K, eps, dx, dg, dW, ws};
     return hip_status(bl::launch_backward(a, as_stream(stream)), "backward launch");
+}
+
+size_t bitlinear_mlgru_scan_workspace_bytes(int64_t B, int64_t T, int64_t d) {
+    if (B <= 0 || T <= 0 || d <= 0 || d % 16 != 0 || d > BITLINEAR_MAX_K || B * T > BITLINEAR_MAX_DIM) return 0;
+    return bl::mlgru_scan_workspace_bytes(B, T, d);
+}
+
+int bitlinear_mlgru_scan(const float* z, int64_t B, int64_t T, int64_t d, float* state, uint16_t* p,
+                         void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_mlgru_shape(B, T, d));
+    if (B == 0 || T == 0) return BITLINEAR_OK;
+    CHECK_PTR(z);
+    CHECK_PTR(state);
+    CHECK_PTR(p);
+    TRY(check_ws(ws, ws_bytes, bl::mlgru_scan_workspace_bytes(B, T, d)));
+    return hip_status(bl::launch_mlgru_scan(z, B, T, d, state, p, ws, as_stream(stream)), "mlgru scan launch");
+}
+
+size_t bitlinear_mlgru_workspace_bytes(int64_t B, int64_t T, int64_t d) {
+    if (B <= 0 || T <= 0 || d <= 0 || d % 16 != 0 || d > BITLINEAR_MAX_K || B * T > BITLINEAR_MAX_DIM) return 0;
+    return mlgru_ws_bytes(B, T, d);
+}
+
+int bitlinear_mlgru_forward(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
+                            const float* gamma_in, const float* rms_w_out, const uint8_t* packed_out,
+                            const float* gamma_out, int64_t B, int64_t T, int64_t d, float eps,
+                            float* state, float* y, void* ws, size_t ws_bytes, void* stream) {
+    return mlgru_impl(x, rms_w_in, packed_in, gamma_in, rms_w_out, packed_out, gamma_out, B, T, d, eps,
+                      state, y, ws, ws_bytes, as_stream(stream));
+}
+
+size_t bitlinear_layer_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t F) {
+    if (B <= 0 || T <= 0 || d <= 0 || F <= 0 || d % 16 != 0 || F % 16 != 0 || d > BITLINEAR_MAX_K ||
+        F > BITLINEAR_MAX_K || B * T > BITLINEAR_MAX_DIM)
+        return 0;
+    return layer_ws_bytes(B, T, d, F);
+}
+
+int bitlinear_layer_forward(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
+                            const float* gamma_in, const float* rms_w_out, const uint8_t* packed_out,
+                            const float* gamma_out, const float* rms_w_gu, const uint8_t* packed_gu,
+                            const float* gamma_gu, const float* rms_w_down, const uint8_t* packed_down,
+                            const float* gamma_down, int64_t B, int64_t T, int64_t d, int64_t F,
+                            float eps, float* state, uint16_t* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+    return layer_impl(x, rms_w_in, packed_in, gamma_in, rms_w_out, packed_out, gamma_out, rms_w_gu, packed_gu,
+                      gamma_gu, rms_w_down, packed_down, gamma_down, B, T, d, F, eps, state, out, ws, ws_bytes,
+                      as_stream(stream));
 }
 
 }  // extern "C"

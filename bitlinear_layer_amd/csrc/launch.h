@@ -106,6 +106,18 @@ hipError_t launch_decode(const DecodeArgs& a, Epilogue ep, hipStream_t stream);
 bool decode_few_supported(int M, int K);
 hipError_t launch_decode_few(const DecodeArgs& a, hipStream_t stream);
 
+// --- MLGRU token mixer and the layer's residual stream ---------------------------
+// Recurrence of the token mixer from its pre-activations z fp32 [B][T][3d]
+// (z_f | z_c | z_g per token): p bf16 [B][T][d]; state fp32 [B][d] holds h_0
+// on entry and h_T on return.  ws: mlgru_scan_workspace_bytes(B, T, d)
+// bytes, 256-byte aligned (0 when one chunk suffices).
+size_t mlgru_scan_workspace_bytes(int64_t B, int64_t T, int64_t d);
+hipError_t launch_mlgru_scan(const float* z, int64_t B, int64_t T, int64_t d, float* state,
+                             uint16_t* p, void* ws, hipStream_t stream);
+// out = bf16(float(x) + y) over n elements (n % 16 == 0).
+hipError_t launch_residual_bf16(const uint16_t* x, const float* y, uint16_t* out, int64_t n,
+                                hipStream_t stream);
+
 // --- backward (straight-through estimator) -------------------------------------
 // x bf16 [M][K], g fp32 [K], packed [N][K/4], gamma (device scalar), dy fp32
 // [M][N] -> dx fp32 [M][K], dg fp32 [K], dW fp32 [N][K]; ws of

@@ -290,6 +290,73 @@ int bitlinear_glu_hidden(const uint16_t* x, const float* rms_w_gu,
                          size_t ws_bytes, void* stream, int kernel);
 
 /* ---------------------------------------------------------------------------
+ * MLGRU token mixer.  [datacamp, "Các thành phần lõi: MLGRU và GLU"]: the
+ * MLGRU takes a sequence token by token, updating a hidden state, the
+ * memory of earlier tokens, through element-wise operations and gates with
+ * values between 0 and 1; [jiqizhixin, "MatMul-free 语言模型架构"]: a ternary
+ * RNN of element-wise products and accumulation built on the GRU; [ld246,
+ * "线性操作的引入"]: element-wise operations in place of the GRU's matrix
+ * products.  Readings (the pages print no equations): the gates depend on
+ * the token only, through one BitLinear whose fused [3d][d] matrix (one
+ * gamma, one RMSNorm weight) gives z = z_f | z_c | z_g (rows 0..d-1, d..2d-1,
+ * 2d..3d-1); per channel
+ *   f = sigmoid(z_f), c = SiLU(z_c), g = sigmoid(z_g),
+ *   h_t = f h_{t-1} + (1 - f) c,  p_t = bf16(g h_t),  y_t = BitLinear_out(p_t)
+ * with a second BitLinear [d][d].  Sigmoid and SiLU are evaluated in fp32
+ * from 2^x and a reciprocal (about one ulp each); the state is fp32.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes for bitlinear_mlgru_scan (0 when the sequence needs no
+ * chunk summaries, or for an invalid shape). */
+size_t bitlinear_mlgru_scan_workspace_bytes(int64_t B, int64_t T, int64_t d);
+
+/* The recurrence alone, from the pre-activations: z fp32 [B][T][3d] (device),
+ * state fp32 [B][d] (device; h_0 on entry, h_T on return), p bf16 [B][T][d]
+ * (device, written).  The tokens of a sequence are cut into chunks that run
+ * in parallel (summaries, then chunk start states, then each chunk again),
+ * which equals the token-by-token recurrence up to fp32 rounding.  d % 16 ==
+ * 0; B = 0 or T = 0 leaves the state as it is. */
+int bitlinear_mlgru_scan(const float* z, int64_t B, int64_t T, int64_t d, float* state,
+                         uint16_t* p, void* ws, size_t ws_bytes, void* stream);
+
+size_t bitlinear_mlgru_workspace_bytes(int64_t B, int64_t T, int64_t d);
+
+/* The token mixer: x bf16 [B][T][d]; rms_w_in fp32 [d], packed_in [3d][d/4]
+ * (rows f | c | g) and gamma_in; rms_w_out fp32 [d], packed_out [d][d/4] and
+ * gamma_out; state fp32 [B][d] (h_0 in, h_T out; zero it for new
+ * sequences); y fp32 [B][T][d].  The two projections run through the
+ * forward's dispatch over all B*T tokens (one fused kernel each for a
+ * single token).  Decoding token by token is this call with T = 1, carrying
+ * the state. */
+int bitlinear_mlgru_forward(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
+                            const float* gamma_in, const float* rms_w_out,
+                            const uint8_t* packed_out, const float* gamma_out, int64_t B,
+                            int64_t T, int64_t d, float eps, float* state, float* y, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * One layer: the MLGRU token mixer, then the GLU channel mixer
+ * ([jiqizhixin, "MatMul-free 语言模型架构"]: a layer is a token mixer and a
+ * channel mixer, in the Metaformer view).  Reading: each mixer adds its
+ * output to its input, and the residual stream is bf16:
+ *   u = bf16(x + MLGRU(x)),   out = bf16(u + GLU(u)).
+ * ------------------------------------------------------------------------- */
+
+size_t bitlinear_layer_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t F);
+
+/* x bf16 [B][T][d]; the MLGRU's weights as for bitlinear_mlgru_forward; the
+ * GLU's as for bitlinear_glu_forward (inner size F); state fp32 [B][d] (in
+ * and out); out bf16 [B][T][d]. */
+int bitlinear_layer_forward(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
+                            const float* gamma_in, const float* rms_w_out,
+                            const uint8_t* packed_out, const float* gamma_out,
+                            const float* rms_w_gu, const uint8_t* packed_gu, const float* gamma_gu,
+                            const float* rms_w_down, const uint8_t* packed_down,
+                            const float* gamma_down, int64_t B, int64_t T, int64_t d, int64_t F,
+                            float eps, float* state, uint16_t* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
  * Stages (exposed so that each step can be compared on its own).
  * ------------------------------------------------------------------------- */
 

@@ -214,6 +214,78 @@ def test_gamma_must_hold_one_value_per_matrix():
         bl._scalar(torch.ones(1), "gamma")
 
 
+# --------------------------------------------------------------------------
+# MLGRU token mixer and the layer: validation before any launch
+# --------------------------------------------------------------------------
+
+def test_mlgru_scan_rejects():
+    L = bl.lib()
+    assert L.bitlinear_mlgru_scan(FAKE, 1, 4, 24, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_mlgru_scan(None, 1, 4, 32, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_mlgru_scan(FAKE, 1, 4, 32, None, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_mlgru_scan(FAKE, 1, 4, 32, FAKE, MISALIGNED, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert L.bitlinear_mlgru_scan(FAKE, -1, 4, 32, FAKE, FAKE, FAKE, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    # a long single sequence needs chunk summaries: refused without them
+    need = L.bitlinear_mlgru_scan_workspace_bytes(1, 2048, 2048)
+    assert need > 0
+    assert L.bitlinear_mlgru_scan(FAKE, 1, 2048, 2048, FAKE, FAKE, None, 0, None) == bl.BITLINEAR_ERR_WORKSPACE
+    assert L.bitlinear_mlgru_scan(FAKE, 1, 2048, 2048, FAKE, FAKE, FAKE, need - 1, None) == bl.BITLINEAR_ERR_WORKSPACE
+    # empty sequences are valid no-ops
+    assert L.bitlinear_mlgru_scan(None, 3, 0, 32, None, None, None, 0, None) == bl.BITLINEAR_OK
+    assert L.bitlinear_mlgru_scan(None, 0, 5, 32, None, None, None, 0, None) == bl.BITLINEAR_OK
+
+
+def test_mlgru_and_layer_workspace_queries():
+    L = bl.lib()
+    assert L.bitlinear_mlgru_scan_workspace_bytes(1, 1, 2048) == 0          # one token: one pass
+    assert L.bitlinear_mlgru_scan_workspace_bytes(64, 5, 2048) == 0         # many channels: one pass
+    assert L.bitlinear_mlgru_scan_workspace_bytes(1, 2048, 24) == 0         # d % 16 != 0: invalid
+    m = L.bitlinear_mlgru_workspace_bytes(1, 2048, 2048)
+    assert m >= 2048 * 3 * 2048 * 4 + 2048 * 2048 * 3 and m % 256 == 0
+    assert L.bitlinear_mlgru_workspace_bytes(0, 5, 32) == 0
+    lw = L.bitlinear_layer_workspace_bytes(1, 2048, 2048, 5632)
+    assert lw >= max(m, L.bitlinear_glu_workspace_bytes(2048, 2048, 5632)) + 2048 * 2048 * 6
+    assert L.bitlinear_layer_workspace_bytes(1, 8, 2048, 100) == 0
+
+
+def _mlgru_call(x=FAKE, w=FAKE, B=1, T=4, d=64, eps=1e-6, state=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return bl.lib().bitlinear_mlgru_forward(x, w, w, w, w, w, w, B, T, d, eps, state, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(w=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(state=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(y=None), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(d=40), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(d=(1 << 24) + 16), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(T=-2), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(eps=0.0), bl.BITLINEAR_ERR_INVALID_ARG),
+    (dict(ws=None), bl.BITLINEAR_ERR_WORKSPACE),
+    (dict(ws_bytes=4096), bl.BITLINEAR_ERR_WORKSPACE),
+])
+def test_mlgru_forward_rejects(kwargs, status):
+    assert _mlgru_call(**kwargs) == status
+    assert bl.bitlinear_last_error() != ""
+
+
+def test_layer_forward_rejects():
+    L = bl.lib()
+    args = [FAKE] * 13
+
+    def call(a=args, B=1, T=4, d=64, F=96, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return L.bitlinear_layer_forward(*a, B, T, d, F, 1e-6, FAKE, out, ws, ws_bytes, None)
+
+    assert call(F=100) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert call(out=None) == bl.BITLINEAR_ERR_INVALID_ARG
+    for i in range(13):
+        bad = list(args)
+        bad[i] = None
+        assert call(a=bad) == bl.BITLINEAR_ERR_INVALID_ARG, i
+    assert call(ws_bytes=64) == bl.BITLINEAR_ERR_WORKSPACE
+    assert call(T=0, out=None, ws=None) == bl.BITLINEAR_OK
+
+
 def test_noalloc_rejects_before_touching_the_gpu():
     """bitlinear_forward_noalloc refuses a stage larger than its fixed
     scratch (and bad sizes) before any HIP call."""
