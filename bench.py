@@ -675,7 +675,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="run only these secondary workloads after the headline (comma-separated; "
-                         "available: backward, layer, crossover)")
+                         "available: backward, layer, crossover, prefill)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay line (its 1024-node graphs are slow under counter collection)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -745,6 +745,17 @@ def main():
         log("[bench] re-ternarisation of 64 x 2048 x 2048 fp32 master weights")
         secondary["repack_64x2048x2048"] = bench_repack(torch, bl, wl, 64, 2048, 2048, 10, 2, stream)
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
+        secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
+                                           args.warmup, stream)
+
+    if only and "prefill" in only:
+        log("[bench] prefill 8192 and the MFMA-tile sweep shapes")
+        secondary["prefill_8192"] = bench_prefill(torch, bl, wl, 8192, 2048, 2048, max(10, args.steps // 2),
+                                                  args.warmup, stream)
+        for K2, N2 in ((2560, 2560), (2560, 6912), (6912, 2560)):
+            for M2 in (4096, 16384):
+                secondary[f"sweep_m{M2}_k{K2}_n{N2}"] = bench_prefill(torch, bl, wl, M2, N2, K2,
+                                                                      max(5, args.steps // 5), args.warmup, stream)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
 

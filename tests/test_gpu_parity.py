@@ -248,6 +248,23 @@ def test_ternary_matmul_extremes():
         assert np.array_equal(acc, acc_ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(4224, 2304, 512), (8192, 4096, 1024), (4096, 2560, 2560)])
+def test_ternary_matmul_many_tiles(M, N, K):
+    """The 256 x 256 tile kernel over more tiles than CUs (153, 512 and 160
+    tiles), K of 4, 8 and 20 stages: int32 bit-exact on rows sampled across
+    the tiles, including the first and last rows of tiles."""
+    _say("many tiles", M, N, K)
+    r = wl.rng(M + N + K, wl.STREAM_X)
+    q = r.integers(-127, 128, size=(M, K), dtype=np.int8)
+    w = (r.integers(0, 3, size=(N, K)) - 1).astype(np.int8)
+    packed = gu.to_dev(gu.orc().pack(w))
+    acc = bl.bitlinear_ternary_matmul_i32(gu.to_dev(q), packed, kernel=MFMA).cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, M, 127), [1, 126, 127, 128, 129, 255, 256, M - 129, M - 2, M - 1]]))
+    rows = rows[(rows >= 0) & (rows < M)]
+    ref = gu.orc().accumulate(q[rows], w)
+    assert np.array_equal(acc[rows], ref)
+
+
 def test_ternary_matmul_tile_path_long_rows():
     """The 256-row tile kernel at K = 8421632, where the byte offset of a
     tile's last row, 255 * K, passes 2^31: 129 tiles of 256 x 256 (so the
