@@ -131,8 +131,10 @@ int check_kernel(int kernel, int64_t M, int64_t K, bool fused_allowed, bool glu 
 
 int run_decode(const uint16_t* x, const float* g, int64_t g_stride, const uint8_t* packed,
                const float* gamma, int64_t B, int64_t M, int64_t N, int64_t K, float eps, void* out,
-               bl::Epilogue ep, hipStream_t stream) {
+               bl::Epilogue ep, hipStream_t stream, const uint16_t* res = nullptr, float* state = nullptr) {
     bl::DecodeArgs d;
+    d.res = res;
+    d.state = state;
     d.x = x;
     d.g = g;
     d.g_stride = g_stride;
@@ -201,10 +203,14 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
 }
 
 // B independent GLU mixers of one shape (B = 1 for bitlinear_glu_forward).
+// With res (bf16 [B][M][D]) the mixer adds its output to res and writes the
+// bf16 sum to out_res instead of y (fused into the down projection when
+// that runs on the one-token decode kernel; y is then scratch).
 int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
              const float* gamma_gu, const float* rms_w_down, const uint8_t* packed_down,
              const float* gamma_down, int64_t B, int64_t M, int64_t D, int64_t F, float eps,
-             float* y, void* ws, size_t ws_bytes, void* stream) {
+             float* y, void* ws, size_t ws_bytes, void* stream, const uint16_t* res = nullptr,
+             uint16_t* out_res = nullptr) {
     TRY(check_rows(M, "M"));
     TRY(check_k(D, "D"));
     TRY(check_k(F, "F"));
@@ -240,12 +246,20 @@ int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
         TRY(run_product(act_x, packed_gu, gamma_gu, M, F, D, B, h, bl::Epilogue::kGluBf16,
                         BITLINEAR_KERNEL_AUTO, st));
     }
-    if (use_decode(M, F, BITLINEAR_KERNEL_AUTO, false))
-        return run_decode(h, rms_w_down, B > 1 ? F : 0, packed_down, gamma_down, B, M, D, F, eps, y,
-                          bl::Epilogue::kF32, st);
-    TRY(hip_status(bl::launch_quant(h, rms_w_down, rows, M, (int)F, eps, act_h, st), "quantise launch"));
-    return run_product(act_h, packed_down, gamma_down, M, D, F, B, y, bl::Epilogue::kF32,
-                       BITLINEAR_KERNEL_AUTO, st);
+    if (res != nullptr && bl::decode_supported((int)M, (int)F))
+        return run_decode(h, rms_w_down, B > 1 ? F : 0, packed_down, gamma_down, B, M, D, F, eps, out_res,
+                          bl::Epilogue::kResBf16, st, res);
+    if (use_decode(M, F, BITLINEAR_KERNEL_AUTO, false)) {
+        TRY(run_decode(h, rms_w_down, B > 1 ? F : 0, packed_down, gamma_down, B, M, D, F, eps, y,
+                       bl::Epilogue::kF32, st));
+    } else {
+        TRY(hip_status(bl::launch_quant(h, rms_w_down, rows, M, (int)F, eps, act_h, st), "quantise launch"));
+        TRY(run_product(act_h, packed_down, gamma_down, M, D, F, B, y, bl::Epilogue::kF32,
+                        BITLINEAR_KERNEL_AUTO, st));
+    }
+    if (res != nullptr)
+        return hip_status(bl::launch_residual_bf16(res, y, out_res, rows * D, st), "residual launch");
+    return BITLINEAR_OK;
 }
 
 // B matrices of one shape, back to back (B = 1 for bitlinear_pack_weights).
@@ -313,10 +327,18 @@ int check_mlgru_shape(int64_t B, int64_t T, int64_t d) {
 // The token mixer: z = BitLinear_in(x) over all B*T tokens, the recurrence,
 // y = BitLinear_out(p).  The projections go through the forward's own
 // dispatch (fused decode kernel for a few tokens, MFMA tiles for many).
+// With res (bf16 [B][T][d]) the mixer adds its output to res and writes the
+// bf16 sum to out_res instead of y (y is then scratch).  One token per
+// sequence (T = 1, B <= 4) runs as two launches: the input projection's
+// decode kernel gathers the f, c and g rows of each channel and applies the
+// recurrence step in its epilogue, and the output projection's adds the
+// residual in its epilogue (same fp32 arithmetic as the separate kernels,
+// so the same bits).
 int mlgru_impl(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
                const float* gamma_in, const float* rms_w_out, const uint8_t* packed_out,
                const float* gamma_out, int64_t B, int64_t T, int64_t d, float eps, float* state,
-               float* y, void* ws, size_t ws_bytes, hipStream_t st) {
+               float* y, void* ws, size_t ws_bytes, hipStream_t st, const uint16_t* res = nullptr,
+               uint16_t* out_res = nullptr) {
     TRY(check_mlgru_shape(B, T, d));
     TRY(check_eps(eps));
     if (B == 0 || T == 0) return BITLINEAR_OK;
@@ -332,11 +354,22 @@ int mlgru_impl(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_i
     TRY(check_ws(ws, ws_bytes, mlgru_ws_bytes(B, T, d)));
     const MlgruWs w = mlgru_ws_carve(ws, B, T, d);
     const int64_t M = B * T;
-    TRY(forward_impl(x, rms_w_in, packed_in, gamma_in, 1, M, 3 * d, d, eps, w.z, w.act, w.act_bytes,
-                     st, BITLINEAR_KERNEL_AUTO));
-    TRY(hip_status(bl::launch_mlgru_scan(w.z, B, T, d, state, w.p, w.scan, st), "mlgru scan launch"));
-    return forward_impl(w.p, rms_w_out, packed_out, gamma_out, 1, M, d, d, eps, y, w.act, w.act_bytes, st,
-                        BITLINEAR_KERNEL_AUTO);
+    if (T == 1 && bl::decode_supported((int)B, (int)d)) {
+        TRY(run_decode(x, rms_w_in, 0, packed_in, gamma_in, 1, B, d, d, eps, w.p, bl::Epilogue::kMlgruStep, st,
+                       nullptr, state));
+    } else {
+        TRY(forward_impl(x, rms_w_in, packed_in, gamma_in, 1, M, 3 * d, d, eps, w.z, w.act, w.act_bytes,
+                         st, BITLINEAR_KERNEL_AUTO));
+        TRY(hip_status(bl::launch_mlgru_scan(w.z, B, T, d, state, w.p, w.scan, st), "mlgru scan launch"));
+    }
+    if (res != nullptr && bl::decode_supported((int)M, (int)d))
+        return run_decode(w.p, rms_w_out, 0, packed_out, gamma_out, 1, M, d, d, eps, out_res,
+                          bl::Epilogue::kResBf16, st, res);
+    TRY(forward_impl(w.p, rms_w_out, packed_out, gamma_out, 1, M, d, d, eps, y, w.act, w.act_bytes, st,
+                     BITLINEAR_KERNEL_AUTO));
+    if (res != nullptr)
+        return hip_status(bl::launch_residual_bf16(res, y, out_res, M * d, st), "residual launch");
+    return BITLINEAR_OK;
 }
 
 // Workspace of one layer: a region shared by the two mixers (each needs it
@@ -401,11 +434,9 @@ int layer_impl(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_i
     float* ymix = reinterpret_cast<float*>(base + shared);
     uint16_t* u = reinterpret_cast<uint16_t*>(base + shared + bl::round_up(M * d * 4, 256));
     TRY(mlgru_impl(x, rms_w_in, packed_in, gamma_in, rms_w_out, packed_out, gamma_out, B, T, d, eps, state,
-                   ymix, base, mlgru_ws_bytes(B, T, d), st));
-    TRY(hip_status(bl::launch_residual_bf16(x, ymix, u, M * d, st), "residual launch"));
-    TRY(glu_impl(u, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down, 1, M, d, F, eps,
-                 ymix, base, bitlinear_glu_workspace_bytes(M, d, F), st));
-    return hip_status(bl::launch_residual_bf16(u, ymix, out, M * d, st), "residual launch");
+                   ymix, base, mlgru_ws_bytes(B, T, d), st, x, u));
+    return glu_impl(u, rms_w_gu, packed_gu, gamma_gu, rms_w_down, packed_down, gamma_down, 1, M, d, F, eps,
+                    ymix, base, bitlinear_glu_workspace_bytes(M, d, F), st, u, out);
 }
 
 }  // namespace

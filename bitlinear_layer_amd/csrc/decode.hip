@@ -182,9 +182,16 @@ __device__ __forceinline__ void quantise_row_regs(const uint16_t* __restrict__ x
     scale_out = scale;
 }
 
+// Weight rows that feed one output: the GLU pairs gate row n with up row
+// N + n; one MLGRU token gathers rows n, N + n and 2N + n (z_f, z_c, z_g).
+template <Epilogue EP>
+constexpr int rows_per_output() {
+    return EP == Epilogue::kGluBf16 ? 2 : (EP == Epilogue::kMlgruStep ? 3 : 1);
+}
+
 template <int MAXM, int S, int U, int LPR, Epilogue EP>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows_per_block) {
-    constexpr bool kGlu = EP == Epilogue::kGluBf16;
+    constexpr int kR = rows_per_output<EP>();
     constexpr int RW = kWave / LPR;     // rows per wave-wide load
     constexpr int kSpread = LPR / U;    // lanes holding one finished row sum
     extern __shared__ __attribute__((aligned(16))) int8_t qlds[];  // [M][K]
@@ -202,32 +209,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
     const int lr = lane & (LPR - 1);
     const int grp = lane / LPR;
 
-    const int64_t nrows = kGlu ? 2 * (int64_t)N : (int64_t)N;
+    const int64_t nrows = kR * (int64_t)N;
     const uint32_t* P = reinterpret_cast<const uint32_t*>(a.packed) + (int64_t)b * nrows * nwords;
     const int n0 = blockIdx.x * rows_per_block;
     const int n_end = min(N, n0 + rows_per_block);
     const int step = kWaves * U * RW;
 
-    uint4 wa[U][S], wb[U][S], ua[U][S], ub[U][S];
-    // Weights of rows base + u*RW + grp, this lane's chunks.  Loads are
-    // unconditional from clamped addresses: a row past the end is computed
-    // and never stored, and a chunk past the end of K meets zero codes in
-    // qreg, so it adds nothing.
-    auto load = [&](uint4 (&w)[U][S], uint4 (&wu)[U][S], int base) {
+    uint4 wa[kR][U][S], wb[kR][U][S];
+    // Weights of rows base + u*RW + grp (and their partner rows N and 2N
+    // further on), this lane's chunks.  Loads are unconditional from clamped
+    // addresses: a row past the end is computed and never stored, and a
+    // chunk past the end of K meets zero codes in qreg, so it adds nothing.
+    auto load = [&](uint4 (&w)[kR][U][S], int base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t n = min(base + u * RW + grp, n_end - 1);
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const int c = min(lr + s * LPR, nchunks - 1);
-                w[u][s] = load_stream16(P + n * nwords + 4 * c);
-                if (kGlu) wu[u][s] = load_stream16(P + ((int64_t)N + n) * nwords + 4 * c);
+#pragma unroll
+                for (int rr = 0; rr < kR; ++rr)
+                    w[rr][u][s] = load_stream16(P + ((int64_t)rr * N + n) * nwords + 4 * c);
             }
         }
     };
     // Issue the first weight loads before quantising: they do not depend on it.
     const int base0 = n0 + wave * U * RW;
-    load(wa, ua, base0);
+    load(wa, base0);
 
     // 1. quantise the block's token rows into LDS
     const uint16_t* X = a.x + (int64_t)b * M * K;
@@ -303,15 +311,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
     };
     const int u_out = lr / kSpread;
     const bool writer = (lr % kSpread) == 0;
-    auto finish = [&](const uint4 (&w)[U][S], const uint4 (&wu)[U][S], int base) {
-        int32_t part[MAXM][U], partu[MAXM][U];
-        dot_rows(w, part);
-        if (kGlu) dot_rows(wu, partu);
-        int32_t tot[MAXM], totu[MAXM];
+    auto finish = [&](const uint4 (&w)[kR][U][S], int base) {
+        int32_t tot[kR][MAXM];
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) {
-            tot[m] = group_row_sums<LPR, U>(part[m], lane);
-            totu[m] = kGlu ? group_row_sums<LPR, U>(partu[m], lane) : 0;
+        for (int rr = 0; rr < kR; ++rr) {
+            int32_t part[MAXM][U];
+            dot_rows(w[rr], part);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) tot[rr][m] = group_row_sums<LPR, U>(part[m], lane);
         }
         const int n = base + u_out * RW + grp;
         if (writer && n < n_end) {
@@ -319,11 +326,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
             for (int m = 0; m < MAXM; ++m) {
                 if (m >= M) continue;
                 const int64_t o = ((int64_t)b * M + m) * N + n;
-                if (kGlu)
+                const float z0 = rescale(tot[0][m] - sumq[m], cs[m]);
+                if constexpr (EP == Epilogue::kGluBf16) {
+                    static_cast<uint16_t*>(a.out)[o] = glu_bf16(z0, rescale(tot[1][m] - sumq[m], cs[m]));
+                } else if constexpr (EP == Epilogue::kResBf16) {
+                    // the residual stream: u = bf16(res + y), as the stand-alone
+                    // residual pass forms it
                     static_cast<uint16_t*>(a.out)[o] =
-                        glu_bf16(rescale(tot[m] - sumq[m], cs[m]), rescale(totu[m] - sumq[m], cs[m]));
-                else
-                    static_cast<float*>(a.out)[o] = rescale(tot[m] - sumq[m], cs[m]);
+                        (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)a.res[o] << 16) + z0);
+                } else if constexpr (EP == Epilogue::kMlgruStep) {
+                    // one token of its own sequence: state in and out
+                    float h = a.state[o];
+                    const uint32_t p = mlgru_token(z0, rescale(tot[1][m] - sumq[m], cs[m]),
+                                                   rescale(tot[2][m] - sumq[m], cs[m]), h);
+                    a.state[o] = h;
+                    static_cast<uint16_t*>(a.out)[o] = (uint16_t)p;
+                } else {
+                    static_cast<float*>(a.out)[o] = z0;
+                }
             }
         }
     };
@@ -331,11 +351,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
     // Software pipeline: the loads of the next set are in flight while the
     // current set is decoded and reduced.
     for (int base = base0; base < n_end; base += 2 * step) {
-        load(wb, ub, base + step);
-        finish(wa, ua, base);
+        load(wb, base + step);
+        finish(wa, base);
         if (base + step >= n_end) break;
-        load(wa, ua, base + 2 * step);
-        finish(wb, ub, base + step);
+        load(wa, base + 2 * step);
+        finish(wb, base + step);
     }
 }
 
@@ -369,9 +389,10 @@ Plan plan_for(int nchunks, int maxm) {
 template <int MAXM, int S, int LPR, Epilogue EP>
 hipError_t launch_msl(const DecodeArgs& a, hipStream_t stream) {
     // Loads in flight per lane, double buffered: U row sets of S 16-byte
-    // chunks, U = 8 / S for S <= 2 and 2 beyond (half that for the GLU,
-    // which loads a gate and an up row per set).
-    constexpr int kBufRows = 8 / (EP == Epilogue::kGluBf16 ? 2 : 1) / (S >= 3 ? 4 : S);
+    // chunks, U = 8 / S for S <= 2 and 2 beyond (divided by the rows per
+    // output: the GLU loads a gate and an up row per set, an MLGRU token
+    // three rows).
+    constexpr int kBufRows = 8 / rows_per_output<EP>() / (S >= 3 ? 4 : S);
     constexpr int U = kBufRows < 1 ? 1 : (kBufRows > LPR ? LPR : kBufRows);
     constexpr int RW = kWave / LPR;
     const int64_t rpb = balanced_rows_per_block(a.N, a.batch, (int64_t)kWaves * RW);
@@ -474,6 +495,12 @@ hipError_t launch_decode(const DecodeArgs& a, Epilogue ep, hipStream_t stream) {
     switch (ep) {
         case Epilogue::kF32: return launch_ep<Epilogue::kF32>(a, stream);
         case Epilogue::kGluBf16: return launch_ep<Epilogue::kGluBf16>(a, stream);
+        case Epilogue::kResBf16:
+            if (a.res == nullptr) return hipErrorInvalidValue;
+            return launch_ep<Epilogue::kResBf16>(a, stream);
+        case Epilogue::kMlgruStep:
+            if (a.state == nullptr) return hipErrorInvalidValue;
+            return launch_ep<Epilogue::kMlgruStep>(a, stream);
         default: break;
     }
     return hipErrorInvalidValue;

@@ -34,4 +34,30 @@ __device__ __forceinline__ uint16_t glu_bf16(float zg, float zu) {
     return (uint16_t)f32_to_bf16_bits(silu_f32(zg) * zu);
 }
 
+// sigmoid(v) and 1 - sigmoid(v) = sigmoid(-v), each from e = 2^(-|v| log2 e)
+// in (0, 1] and the reciprocal of 1 + e (as silu_f32 does): for v >= 0,
+// sigmoid(v) = 1 / (1 + e) and sigmoid(-v) = e / (1 + e); mirrored for
+// v < 0.  Neither value is formed as 1 - x, so both keep their relative
+// precision when the other is close to 1.
+__device__ __forceinline__ void sigmoid_pair(float v, float& s, float& oms) {
+    constexpr float kNegLog2e = -1.44269502e+00f;
+    const float e = __builtin_amdgcn_exp2f(fabsf(v) * kNegLog2e);
+    const float q = __builtin_amdgcn_rcpf(1.0f + e);
+    const float eq = e * q;
+    s = v < 0.0f ? eq : q;
+    oms = v < 0.0f ? q : eq;
+}
+
+// One token of the MLGRU recurrence for one channel ([datacamp, "Các thành
+// phần lõi: MLGRU và GLU"]: gates in (0, 1) mix the previous state and the
+// current token): forget gate f = sigmoid(zf), candidate c = SiLU(zc),
+// output gate g = sigmoid(zg); h = f h + (1 - f) c; returns bf16(g h).
+__device__ __forceinline__ uint32_t mlgru_token(float zf, float zc, float zg, float& h) {
+    float f, omf, g, omg;
+    sigmoid_pair(zf, f, omf);
+    sigmoid_pair(zg, g, omg);
+    h = fmaf(f, h, omf * silu_f32(zc));
+    return f32_to_bf16_bits(g * h);
+}
+
 }  // namespace bl

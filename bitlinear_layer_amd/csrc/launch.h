@@ -51,9 +51,12 @@ hipError_t launch_row_sums(const int8_t* q, int64_t rows, int K, int32_t* sumq,
 
 // --- ternary product -----------------------------------------------------------
 enum class Epilogue {
-    kF32,      // y[m][n] = float(acc) * (gamma / s[m])
-    kI32,      // acc[m][n]
-    kGluBf16,  // h[m][f] = bf16(silu(z[m][f]) * z[m][F + f]), z = float(acc) * gamma / s
+    kF32,        // y[m][n] = float(acc) * (gamma / s[m])
+    kI32,        // acc[m][n]
+    kGluBf16,    // h[m][f] = bf16(silu(z[m][f]) * z[m][F + f]), z = float(acc) * gamma / s
+    kResBf16,    // u[m][n] = bf16(res[m][n] + y[m][n]): a residual added (fused decode kernel only)
+    kMlgruStep,  // one MLGRU token per row m (its own sequence): z = y over rows n, d + n, 2d + n,
+                 // state[m][n] updated, p[m][n] = bf16(g h) (fused decode kernel only)
 };
 
 // One problem, or `batch` problems of the same shape laid out back to back:
@@ -98,6 +101,8 @@ struct DecodeArgs {
     int batch;
     float eps;
     void* out;
+    const uint16_t* res = nullptr;  // kResBf16: bf16 [batch][M][N]
+    float* state = nullptr;         // kMlgruStep: fp32 [batch][M][N], read and written
 };
 bool decode_supported(int M, int K);
 hipError_t launch_decode(const DecodeArgs& a, Epilogue ep, hipStream_t stream);

@@ -40,20 +40,6 @@ constexpr int kMaxChunks = 2 * kWave;      // two per lane of the chunk-start sc
 constexpr int64_t kTargetThreads = 131072;  // pairs of channels: about 8 waves per CU over 256 CUs
 constexpr int64_t kSinglePassThreads = 32768;
 
-// sigmoid(v) and 1 - sigmoid(v) = sigmoid(-v), each from e = 2^(-|v| log2 e)
-// in (0, 1] and the reciprocal of 1 + e (as silu_f32 does): for v >= 0,
-// sigmoid(v) = 1 / (1 + e) and sigmoid(-v) = e / (1 + e); mirrored for
-// v < 0.  Neither value is formed as 1 - x, so both keep their relative
-// precision when the other is close to 1.
-__device__ __forceinline__ void sigmoid_pair(float v, float& s, float& oms) {
-    constexpr float kNegLog2e = -1.44269502e+00f;
-    const float e = __builtin_amdgcn_exp2f(fabsf(v) * kNegLog2e);
-    const float q = __builtin_amdgcn_rcpf(1.0f + e);
-    const float eq = e * q;
-    s = v < 0.0f ? eq : q;
-    oms = v < 0.0f ? q : eq;
-}
-
 // One thread owns two adjacent channels (d is even), so each wave moves
 // 512 contiguous bytes per token and per stream.
 struct ScanArgs {
@@ -188,12 +174,9 @@ __global__ __launch_bounds__(kScanThreads) void mlgru_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             if (t + u < t1) {
-                float unused = 1.0f, g0, g1, omg;
-                step(zf[u].x, zc[u].x, h.x, unused);
-                step(zf[u].y, zc[u].y, h.y, unused);
-                sigmoid_pair(zg[u].x, g0, omg);
-                sigmoid_pair(zg[u].y, g1, omg);
-                pb[(int64_t)(t + u) * (a.d / 2)] = f32_to_bf16_bits(g0 * h.x) | (f32_to_bf16_bits(g1 * h.y) << 16);
+                const uint32_t p0 = mlgru_token(zf[u].x, zc[u].x, zg[u].x, h.x);
+                const uint32_t p1 = mlgru_token(zf[u].y, zc[u].y, zg[u].y, h.y);
+                pb[(int64_t)(t + u) * (a.d / 2)] = p0 | (p1 << 16);
             }
         }
     }

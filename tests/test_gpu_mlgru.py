@@ -342,3 +342,43 @@ def test_layer_full_sequence_properties():
     assert torch.isfinite(o1.view(torch.bfloat16).float()).all()
     scale = s1.abs().max().item()
     assert (s1 - s3).abs().max().item() <= 1e-4 * scale
+
+
+def _bf16_add(a_bits, y):
+    """bf16(a + y) in fp32, rounded to nearest even (torch's conversion)."""
+    return (a_bits.view(torch.bfloat16).float() + y).to(torch.bfloat16).view(torch.int16)
+
+
+# (B, d, F): one token per sequence, so every projection runs on the fused
+# decode kernel with the recurrence step or a residual add in its epilogue.
+ONE_TOKEN = [(1, 64, 96), (3, 128, 192), (4, 256, 384), (1, 2048, 5632), (2, 2048, 5632)]
+
+
+@pytest.mark.parametrize("B,d,F", ONE_TOKEN)
+def test_layer_one_token_fused_equals_composed(B, d, F):
+    """A one-token step of the layer fuses the recurrence step into the
+    input projection and the two residual adds into the output and down
+    projections.  Each epilogue uses the arithmetic of the kernel it
+    replaces, so the layer's output and state must equal, bit for bit, the
+    same step composed from the separate entry points (projection, scan,
+    projection, bf16(x + y), GLU, bf16(u + y))."""
+    _say("one-token fused vs composed", B, d, F)
+    (_, _), (mdev, gdev) = _layer(d, F, seed=7 * B + d)
+    x = gu.to_dev_bf16(wl.x_normal(B, d, seed=B + d).reshape(B, 1, d))
+    h0 = wl.rng(B + d, 8).standard_normal((B, d)).astype(np.float32)
+    s_fused = gu.to_dev(h0.copy())
+    out = bl.bitlinear_layer_forward(x, mdev, gdev, s_fused)
+    y_mix = bl.bitlinear_mlgru_forward(x, *mdev, gu.to_dev(h0.copy()))
+
+    s_comp = gu.to_dev(h0.copy())
+    g_in, p_in, gm_in, g_out, p_out, gm_out = mdev
+    z = bl.bitlinear_forward(x.reshape(B, d), g_in, p_in, gm_in)
+    p = bl.bitlinear_mlgru_scan(z.reshape(B, 1, 3 * d), s_comp)
+    y = bl.bitlinear_forward(p.reshape(B, d), g_out, p_out, gm_out)
+    u = _bf16_add(x.reshape(B, d), y)
+    yg = bl.bitlinear_glu_forward(u, *gdev)
+    ref = _bf16_add(u, yg)
+    torch.cuda.synchronize()
+    assert torch.equal(y_mix.reshape(B, d), y)
+    assert torch.equal(out.reshape(B, d), ref)
+    assert torch.equal(s_fused, s_comp)
