@@ -38,13 +38,32 @@ constexpr int kMaxRowChunks = 4;  // rows up to 4 * 8 * kThreads = 8192 wide sta
 // quantisation), instead of a block reduction with two more barriers here.
 // The integer sum does not depend on the order.
 __device__ __forceinline__ void put_wave_sum(int32_t v, int32_t* qpart) {
-    v = wave_sum(v);
+    v = wave_sum_dpp(v);
     if ((threadIdx.x & (kWave - 1)) == 0) qpart[threadIdx.x / kWave] = v;
+}
+
+// The mean of the squares, ss / K rounded to fp32.  For K a power of two
+// the quotient is the exact scaling ldexp(ss, -log2 K) (the same bits as the
+// division, which is also exact there), one instruction instead of the fp64
+// division sequence on the prologue's critical path.
+__device__ __forceinline__ float mean_square(double ss, int K) {
+    if ((K & (K - 1)) == 0) return (float)ldexp(ss, -__builtin_ctz((unsigned)K));
+    return (float)(ss / (double)K);
+}
+
+// Codes in LDS are grouped by 16-byte unit: unit j (k in [64c + 16j,
+// 64c + 16j + 16)) of every 64-wide chunk c lies at (j * nchunks + c) * 16,
+// so the lanes reading unit j of consecutive chunks read consecutive
+// 16-byte words (no bank conflicts).  Element block i (k in [8i, 8i + 8)) is
+// the low or high half of unit (i / 2) % 4 of chunk i / 8.
+__device__ __forceinline__ int code_offset(int i, int nchunks) {
+    return (((i >> 1) & 3) * nchunks + (i >> 3)) * 16 + (i & 1) * 8;
 }
 
 // Block-cooperative RMSNorm + absmax int8 of one token row into LDS; the
 // same arithmetic and reduction order as the block-per-row quant_kernel, so
-// the codes agree with it.
+// the codes agree with it.  dscr and fscr are this row's own scratch slots
+// (used once per launch), so the reductions skip their leading barrier.
 __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__ xr,
                                                     const float* __restrict__ gr, int K, float eps,
                                                     int8_t* __restrict__ qrow, double* dscr,
@@ -63,8 +82,8 @@ __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < 8; ++j) ss += (double)v[j] * (double)v[j];
     }
-    ss = block_sum(ss, dscr);
-    const float ms = (float)(ss / (double)K);
+    ss = block_sum<true, kWaves>(ss, dscr);
+    const float ms = mean_square(ss, K);
     const float r = 1.0f / sqrtf(ms + eps);
     float amax = 0.0f;
     for (int i = threadIdx.x; i < nchunks; i += kThreads) {
@@ -79,7 +98,7 @@ __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__
             amax = fmaxf(amax, fabsf((xv * r) * gv[j]));
         }
     }
-    amax = block_max(amax, fscr);
+    amax = block_max<true, kWaves>(amax, fscr);
     const float scale = 127.0f / fmaxf(amax, 1e-5f);
     int32_t qsum = 0;
     for (int i = threadIdx.x; i < nchunks; i += kThreads) {
@@ -97,7 +116,7 @@ __device__ __forceinline__ void quantise_row_to_lds(const uint16_t* __restrict__
             qsum += qi;
             packed[j >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (j & 3));
         }
-        *reinterpret_cast<uint2*>(qrow + 8 * i) = make_uint2(packed[0], packed[1]);
+        *reinterpret_cast<uint2*>(qrow + code_offset(i, K / 64)) = make_uint2(packed[0], packed[1]);
     }
     put_wave_sum(qsum, qpart);
     scale_out = scale;
@@ -151,8 +170,8 @@ __device__ __forceinline__ void quantise_row_regs(const uint16_t* __restrict__ x
             ss += (double)v * (double)v;
         }
     }
-    ss = block_sum(ss, dscr);
-    const float ms = (float)(ss / (double)K);
+    ss = block_sum<true, kWaves>(ss, dscr);
+    const float ms = mean_square(ss, K);
     const float r = 1.0f / sqrtf(ms + eps);
     float amax = 0.0f;
 #pragma unroll
@@ -161,7 +180,7 @@ __device__ __forceinline__ void quantise_row_regs(const uint16_t* __restrict__ x
 #pragma unroll
         for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((xval(c, j) * r) * gv[c][j]));
     }
-    amax = block_max(amax, fscr);
+    amax = block_max<true, kWaves>(amax, fscr);
     const float scale = 127.0f / fmaxf(amax, 1e-5f);
     int32_t qsum = 0;
 #pragma unroll
@@ -176,7 +195,7 @@ __device__ __forceinline__ void quantise_row_regs(const uint16_t* __restrict__ x
             qsum += qi;
             packed[j >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (j & 3));
         }
-        *reinterpret_cast<uint2*>(qrow + 8 * i) = make_uint2(packed[0], packed[1]);
+        *reinterpret_cast<uint2*>(qrow + code_offset(i, K / 64)) = make_uint2(packed[0], packed[1]);
     }
     put_wave_sum(qsum, qpart);
     scale_out = scale;
@@ -195,10 +214,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
     constexpr int RW = kWave / LPR;     // rows per wave-wide load
     constexpr int kSpread = LPR / U;    // lanes holding one finished row sum
     extern __shared__ __attribute__((aligned(16))) int8_t qlds[];  // [M][K]
-    __shared__ double dscr[kWaves];
-    __shared__ float fscr[kWaves];
+    __shared__ double dscr[MAXM][kWaves];
+    __shared__ float fscr[MAXM][kWaves];
     __shared__ int32_t s_qpart[MAXM][kWaves];
-    __shared__ float s_scale[MAXM];
 
     const int b = blockIdx.y;
     const int M = a.M, N = a.N, K = a.K;
@@ -233,14 +251,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
             }
         }
     };
-    // Issue the first weight loads before quantising: they do not depend on it.
+    // Issue the first weight loads and the gain before quantising: they do
+    // not depend on it, and each is one memory round trip.
     const int base0 = n0 + wave * U * RW;
     load(wa, base0);
+    const float gamma = a.gamma[b];
 
     // 1. quantise the block's token rows into LDS
     const uint16_t* X = a.x + (int64_t)b * M * K;
     const float* G = a.g + (int64_t)b * a.g_stride;
-    for (int m = 0; m < M; ++m) {
+    // Every thread ends a row's quantisation holding its scale, so the
+    // rescale factor gamma / s is formed here, in registers, before the
+    // barrier rather than after it.  The loop is unrolled over MAXM so cs
+    // stays in registers; M is the same for the whole block.
+    float cs[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        cs[m] = 0.0f;
+        if (m >= M) continue;
         float sc;
         const uint16_t* xr = X + (int64_t)m * K;
         int8_t* qr = qlds + (int64_t)m * K;
@@ -248,10 +276,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
         // 64 weights per lane, LPR lanes per row), so one form is compiled.
         constexpr int kRowChunks = (64 * S * LPR + 8 * kThreads - 1) / (8 * kThreads);
         if constexpr (kRowChunks <= kMaxRowChunks)
-            quantise_row_regs<kRowChunks>(xr, G, K, a.eps, qr, dscr, fscr, s_qpart[m], sc);
+            quantise_row_regs<kRowChunks>(xr, G, K, a.eps, qr, dscr[m], fscr[m], s_qpart[m], sc);
         else
-            quantise_row_to_lds(xr, G, K, a.eps, qr, dscr, fscr, s_qpart[m], sc);
-        if (threadIdx.x == 0) s_scale[m] = sc;
+            quantise_row_to_lds(xr, G, K, a.eps, qr, dscr[m], fscr[m], s_qpart[m], sc);
+        cs[m] = gamma / sc;
     }
     __syncthreads();
 
@@ -266,15 +294,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int rows
             for (int j = 0; j < 4; ++j) {
                 qreg[m][s][j] = make_int4(0, 0, 0, 0);
                 if (m < M && c < nchunks)
-                    qreg[m][s][j] = *reinterpret_cast<const int4*>(qlds + (int64_t)m * K + 64 * c + 16 * j);
+                    qreg[m][s][j] = *reinterpret_cast<const int4*>(qlds + (int64_t)m * K + (j * nchunks + c) * 16);
             }
         }
-    const float gamma = a.gamma[b];
-    float cs[MAXM];
     int32_t sumq[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
-        cs[m] = m < M ? gamma / s_scale[m] : 0.0f;
         sumq[m] = 0;
         if (m < M) {
 #pragma unroll
@@ -398,6 +423,16 @@ hipError_t launch_msl(const DecodeArgs& a, hipStream_t stream) {
     const int64_t rpb = balanced_rows_per_block(a.N, a.batch, (int64_t)kWaves * RW);
     const dim3 grid((unsigned)((a.N + rpb - 1) / rpb), (unsigned)a.batch);
     const size_t lds = (size_t)a.M * a.K;
+    // A block whose rows do not fill one set of U rows in every wave (a
+    // single small layer spread over all CUs) takes one row per wave-wide
+    // load instead: its rows then spread over the four waves, rather than
+    // one wave decoding them all while the others idle.
+    if constexpr (U > 1) {
+        if (rpb < (int64_t)kWaves * U * RW) {
+            decode_kernel<MAXM, S, 1, LPR, EP><<<grid, kThreads, lds, stream>>>(a, (int)rpb);
+            return hipGetLastError();
+        }
+    }
     decode_kernel<MAXM, S, U, LPR, EP><<<grid, kThreads, lds, stream>>>(a, (int)rpb);
     return hipGetLastError();
 }

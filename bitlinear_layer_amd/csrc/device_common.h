@@ -206,35 +206,47 @@ __device__ __forceinline__ int32_t wave_sum_dpp(int32_t v) {
     return wave_allreduce(v, [](int32_t a, int32_t b) { return a + b; });
 }
 
-// Block reductions: every thread returns the block-wide result.  `scratch`
-// holds at least blockDim.x / 64 elements; the helper synchronises before
-// reusing it, so consecutive calls may share one scratch array.
-template <typename T, typename WaveOp, typename Combine>
+// Block reductions: every thread returns the block-wide result.  Each wave
+// reduces over the register hypercube above (no LDS round trips), lane 0
+// leaves the wave's total in scratch[wave], and every thread combines the
+// wave totals in wave order, so all threads and all kernels using these
+// helpers get the same bits for the same data layout.  `scratch` holds at
+// least blockDim.x / 64 elements.  The default form synchronises before
+// writing, so consecutive calls may share one scratch array; with
+// kFresh = true the caller guarantees that no thread still reads this
+// scratch (a slot used once per launch) and the leading barrier is skipped.
+// kNW > 0 fixes the number of waves at compile time (the block size the
+// kernel is launched with), so the combine is unrolled.
+template <bool kFresh = false, int kNW = 0, typename T, typename WaveOp, typename Combine>
 __device__ __forceinline__ T block_reduce(T v, T* scratch, WaveOp wave_op, Combine combine) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nwaves = blockDim.x / kWave;
+    const int nwaves = kNW > 0 ? kNW : (int)(blockDim.x / kWave);
     v = wave_op(v);
-    __syncthreads();
+    if constexpr (!kFresh) __syncthreads();
     if (lane == 0) scratch[wave] = v;
     __syncthreads();
     T r = scratch[0];
+#pragma unroll
     for (int i = 1; i < nwaves; ++i) r = combine(r, scratch[i]);
     return r;
 }
 
+template <bool kFresh = false, int kNW = 0>
 __device__ __forceinline__ double block_sum(double v, double* scratch) {
-    return block_reduce<double>(
-        v, scratch, [](double a) { return wave_sum(a); }, [](double a, double b) { return a + b; });
+    return block_reduce<kFresh, kNW>(
+        v, scratch, [](double a) { return wave_sum_dpp(a); }, [](double a, double b) { return a + b; });
 }
+template <bool kFresh = false, int kNW = 0>
 __device__ __forceinline__ int32_t block_sum(int32_t v, int32_t* scratch) {
-    return block_reduce<int32_t>(
-        v, scratch, [](int32_t a) { return wave_sum(a); },
+    return block_reduce<kFresh, kNW>(
+        v, scratch, [](int32_t a) { return wave_sum_dpp(a); },
         [](int32_t a, int32_t b) { return a + b; });
 }
+template <bool kFresh = false, int kNW = 0>
 __device__ __forceinline__ float block_max(float v, float* scratch) {
-    return block_reduce<float>(
-        v, scratch, [](float a) { return wave_max(a); }, [](float a, float b) { return fmaxf(a, b); });
+    return block_reduce<kFresh, kNW>(
+        v, scratch, [](float a) { return wave_max_dpp(a); }, [](float a, float b) { return fmaxf(a, b); });
 }
 
 }  // namespace bl
