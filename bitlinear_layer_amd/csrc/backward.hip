@@ -20,11 +20,15 @@
 //   dxn [M][K] = gamma * A1 [M][Np] . wT [K][Np]^T,   A1 = bf16(dy),  wT = w^T
 //   dW  [N][K] =         A2 [N][Mp] . qT [K][Mp]^T,   A2 = bf16(dy / s)^T, qT = q^T
 // w and q are exact in bf16, so the only roundings besides the fp32
-// accumulation are those of dy and dy / s to bf16.
+// accumulation are those of dy and dy / s to bf16.  The second operands
+// stay compact until they reach registers: wT as 2-bit codes (16 reduction
+// indices per word) and qT as int8, each expanded to bf16 fragments right
+// before its MFMAs, which keeps the LDS traffic of a stage well below what
+// two bf16 operands take.
 //
-// Kernels: dy_prep (A1 and A2 from one read of dy), q_transpose, w_transpose
-// (2-bit codes to bf16), the NT GEMM, norm_backward (dx in place over dxn,
-// per-block dg partials) and dg_reduce (fixed order, fp64).
+// Kernels: dy_prep (A1 and A2 from one read of dy), q_transpose (int8),
+// w_transpose (2-bit codes, transposed), the NT GEMM, norm_backward (dx in
+// place over dxn, per-block dg partials) and dg_reduce (fixed order, fp64).
 #include "device_common.h"
 #include "launch.h"
 
@@ -99,9 +103,9 @@ __global__ __launch_bounds__(kPrepThreads) void dy_prep_kernel(const float* __re
     }
 }
 
-// qT[k][m] = bf16(q[m][k]) for k < K, m < Mp (zero past M).  K % 16 == 0.
+// qT[k][m] = q[m][k] (int8) for k < K, m < Mp (zero past M).  K % 16 == 0.
 __global__ __launch_bounds__(kPrepThreads) void q_transpose_kernel(const int8_t* __restrict__ q, int M, int K,
-                                                                   int Mp, uint32_t* __restrict__ qT) {
+                                                                   int Mp, int8_t* __restrict__ qT) {
     __shared__ int8_t tile[kT][kT + 4];
     const int64_t mt = Mp / kT;  // flat grid, m fastest
     const int m0 = (int)(blockIdx.x % mt) * kT, k0 = (int)(blockIdx.x / mt) * kT;
@@ -118,26 +122,29 @@ __global__ __launch_bounds__(kPrepThreads) void q_transpose_kernel(const int8_t*
         dst[3] = v.w;
     }
     __syncthreads();
-    // int8 -> fp32 is exact and |q| <= 128 has at most 8 significant bits, so
-    // the top half of the fp32 pattern is the bf16 value.
+    // 64 columns x 4 runs of 16 tokens: one 16-byte store per thread
+    const int c = t / 4, r0 = 16 * (t % 4);
+    const int k = k0 + c;
+    if (k < K) {
+        uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < kT / 8; ++i) {
-        const int c = t / 32 + 8 * i, r = 2 * (t % 32);
-        const int k = k0 + c;
-        if (k < K) {
-            const uint32_t lo = __float_as_uint((float)tile[r][c]) >> 16;
-            const uint32_t hi = __float_as_uint((float)tile[r + 1][c]) >> 16;
-            qT[((int64_t)k * Mp + m0 + r) / 2] = lo | (hi << 16);
-        }
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)(uint8_t)tile[r0 + 4 * i][c] | ((uint32_t)(uint8_t)tile[r0 + 4 * i + 1][c] << 8) |
+                   ((uint32_t)(uint8_t)tile[r0 + 4 * i + 2][c] << 16) | ((uint32_t)(uint8_t)tile[r0 + 4 * i + 3][c] << 24);
+        *reinterpret_cast<uint4*>(qT + (int64_t)k * Mp + m0 + r0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-// wT[k][n] = w[n][k] in bf16 (-1, 0, +1) for k < K, n < Np (zero past N),
-// from the packed rows [N][K/4]: weight j of a 16-weight group sits in byte
-// j % 4 of the group's word, bits 2 (j / 4) + 1 .. 2 (j / 4), as code w + 1.
+// wT[k] holds w[n][k] for n < Np (zero past N) as 2-bit codes, 16 values of
+// n per 32-bit word, from the packed rows [N][K/4] (weight j of a 16-weight
+// group sits in byte j % 4 of the group's word, bits 2 (j / 4) + 1 .. 2 (j / 4),
+// as code w + 1).  In a word of wT, value i = 2p + e (e = 0 or 1) has its
+// "nonzero" flag at bit 16 e + p and its "negative" flag at bit 16 e + 8 + p:
+// the two values of a bf16 pair (2p, 2p + 1) then sit 16 bits apart, which is
+// what the expansion to a pair of bf16 needs (expand_ternary).
 __global__ __launch_bounds__(kPrepThreads) void w_transpose_kernel(const uint32_t* __restrict__ packed, int N,
                                                                    int K, int Np, uint32_t* __restrict__ wT) {
-    __shared__ uint16_t tile[kT][kT + 2];
+    __shared__ uint8_t tile[kT][kT + 4];
     const int64_t nt = Np / kT;  // flat grid, n fastest
     const int n0 = (int)(blockIdx.x % nt) * kT, k0 = (int)(blockIdx.x / nt) * kT;
     const int t = threadIdx.x;
@@ -147,33 +154,49 @@ __global__ __launch_bounds__(kPrepThreads) void w_transpose_kernel(const uint32_
         uint32_t word = 0x55555555u;      // code 1 everywhere: weight 0
         if (n < N && k < K) word = packed[(int64_t)n * (K / 16) + k / 16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int code = (word >> (8 * (j & 3) + 2 * (j >> 2))) & 3;
-            tile[r][16 * wi + j] = code == 1 ? 0u : (code == 0 ? (uint16_t)(0x8000u | kBf16One) : (uint16_t)kBf16One);
-        }
+        for (int j = 0; j < 16; ++j) tile[r][16 * wi + j] = (uint8_t)((word >> (8 * (j & 3) + 2 * (j >> 2))) & 3u);
     }
     __syncthreads();
+    // 64 columns x 4 words of 16 rows: one word per thread
+    const int c = t / 4, g = t % 4;
+    const int k = k0 + c;
+    if (k < K) {
+        uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < kT / 8; ++i) {
-        const int c = t / 32 + 8 * i, r = 2 * (t % 32);
-        const int k = k0 + c;
-        if (k < K) wT[((int64_t)k * Np + n0 + r) / 2] = (uint32_t)tile[r][c] | ((uint32_t)tile[r + 1][c] << 16);
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t code = tile[16 * g + i][c];
+            const int bit = 16 * (i & 1) + (i >> 1);
+            word |= (uint32_t)(code != 1u) << bit;
+            word |= (uint32_t)(code == 0u) << (bit + 8);
+        }
+        wT[(int64_t)k * (Np / 16) + n0 / 16 + g] = word;
     }
 }
 
 // ---------------------------------------------------------------------------
 // C[rows][cols] = alpha * A[rows][R] . B[cols][R]^T on the bf16 matrix cores.
 // Block tile 256 x 256, eight waves as 2 x 4, each a 128 x 64 tile of 32 x 32
-// fragments (4 x 2): per 16-wide reduction step a wave reads six fragments
-// from LDS for eight MFMAs, 0.75 KiB of LDS per MFMA (a 64 x 64 wave tile
-// needs 1 KiB, which four busy SIMDs cannot get from LDS).  R advances in
-// stages of 64, double-buffered in LDS through registers: the next stage's
-// global loads are in flight while the current one is multiplied.  Operand
-// pairing: lane l of A supplies row l % 32 and lane l of B column l % 32,
-// both with the same eight reduction indices 8 (l / 32) + 0..7 of a 16-wide
-// step; accumulator element v of lane l holds C[(v % 4) + 8 (v / 4) +
-// 4 (l / 32)][l % 32].  R % 64 == 0 (zero-padded operands); rows and cols
-// are arbitrary (loads clamped, stores masked).
+// fragments (4 x 2): per 16-wide reduction step a wave reads four A
+// fragments from LDS for eight MFMAs.  R advances in stages of 64,
+// double-buffered in LDS through registers: the next stage's global loads
+// are in flight while the current one is multiplied.  Operand pairing:
+// lane l of A supplies row l % 32 and lane l of B column l % 32, both with
+// the same eight reduction indices 8 (l / 32) + 0..7 of a 16-wide step;
+// accumulator element v of lane l holds C[(v % 4) + 8 (v / 4) + 4 (l / 32)]
+// [l % 32].  R % 64 == 0 (zero-padded operands); rows and cols are
+// arbitrary (loads clamped, stores masked).
+//
+// A is bf16 [rows][R].  B comes in one of three forms (BKind):
+//   kBf16  -- bf16 [cols][R];
+//   kTern2 -- ternary values as 2-bit codes [cols][R / 16] words (the
+//             layout of w_transpose_kernel); a lane reads its column's four
+//             words of a stage once and expands half a word per step;
+//   kInt8  -- int8 [cols][R]; a lane reads 8 bytes per step and converts.
+// The compact forms cut a stage's LDS traffic (the writes of the staged
+// operand and the per-step fragment reads), which together with the
+// barrier is what bounds the bf16 form: per 64-deep stage it moved 192 KiB
+// of fragment reads and 64 KiB of writes through an LDS that delivers
+// 128 B per clock, as long as the MFMAs of the stage take.
 //
 // When the output has fewer tiles than the chip has compute units, the
 // reduction is split over `splits` blocks per tile (whole stages each); split
@@ -189,21 +212,65 @@ constexpr int kGPitch = kGK + 8;  // bf16 per LDS row: 144 bytes, 16-byte reads 
 constexpr int kGWM = 2, kGWN = 4; // wave grid
 constexpr int kGThreads = kGWM * kGWN * kWave;
 constexpr int kGFM = kGT / kGWM / 32, kGFN = kGT / kGWN / 32;  // fragments per wave: 4 x 2
-constexpr int kGLoads = kGT * kGK * 2 / 16 / kGThreads;          // 16-byte loads per thread per operand: 4
+constexpr int kGLoads = kGT * kGK * 2 / 16 / kGThreads;          // 16-byte loads per thread per bf16 operand: 4
 constexpr int kMaxSplits = 8;
+constexpr int kI8Pitch = kGK + 8;  // bytes per int8 LDS row: 8-byte reads of 32 rows hit distinct bank pairs
+
+enum class BKind { kBf16, kTern2, kInt8 };
+
+// Bytes of one B row of a stage in LDS.
+template <BKind BK>
+constexpr int b_lds_pitch() {
+    return BK == BKind::kBf16 ? kGPitch * 2 : (BK == BKind::kTern2 ? kGK / 4 : kI8Pitch);
+}
 
 struct GemmArgs {
     const uint16_t* A;
-    const uint16_t* B;
+    const void* B;
     float* C;            // final output (splits == 1)
     float* P;            // split partials (splits > 1)
     const float* alpha;  // device scalar, or nullptr for 1
     int rows, cols, R, splits;
 };
 
+// Eight ternary values of a w_transpose word as bf16 (-1, 0, +1): the half
+// h (values 8h .. 8h + 7), bf16 pair q = values 8h + 2q, 8h + 2q + 1.  The
+// "nonzero" flags of a pair sit at bits q and 16 + q of word >> 4h, the
+// "negative" flags 8 bits higher: the flags times 0x3F80 (the magnitude of
+// bf16 1.0) give the two magnitudes, and the negative flags shifted to bits
+// 15 and 31 give the signs.  A zero value has neither flag.
+__device__ __forceinline__ bf16x8 expand_ternary(uint32_t word, int h) {
+    const uint32_t w = word >> (4 * h);
+    uint32_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t mag = (w & (0x00010001u << q)) * (0x3F80u >> q);  // both under 2^24: v_mul_u32_u24
+        d[q] = mag | ((w & (0x01000100u << q)) << (7 - q));
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+}
+
+// Eight int8 values as bf16: int8 -> fp32 is exact and |q| <= 128 has at
+// most 8 significant bits, so the top half of the fp32 pattern is the bf16
+// value.
+__device__ __forceinline__ bf16x8 expand_int8(uint2 v) {
+    uint32_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t word = q < 2 ? v.x : v.y;
+        const int sh = 16 * (q & 1);
+        const uint32_t lo = __float_as_uint((float)(int8_t)(word >> sh));
+        const uint32_t hi = __float_as_uint((float)(int8_t)(word >> (sh + 8)));
+        d[q] = (lo >> 16) | (hi & 0xFFFF0000u);
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+}
+
+template <BKind BK>
 __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
+    constexpr int kBPitch = b_lds_pitch<BK>();
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kGT * kGPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGT * kGPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGT * kBPitch];
     const int ntc = (g.cols + kGT - 1) / kGT;
     const int tile = blockIdx.x / g.splits, split = blockIdx.x % g.splits;
     const int tr = tile / ntc, tc = tile % ntc;
@@ -216,45 +283,78 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     const int per = (nst + g.splits - 1) / g.splits;
     const int st0 = min(split * per, nst), st1 = min(st0 + per, nst);
 
-    // global -> register staging: rows t / 8 + 64 i, 16-byte chunk t % 8
+    // global -> register staging of A: rows t / 8 + 64 i, 16-byte chunk t % 8
     const int srow = t / 8, sch = t % 8;
     constexpr int kRowStep = kGThreads / 8;  // 64
-    static_assert(kGLoads == 4, "four staged loads per operand");
+    static_assert(kGLoads == 4, "four staged loads per bf16 operand");
     const int64_t aoff0 = (int64_t)min(row0 + srow, g.rows - 1) * g.R + 8 * sch;
     const int64_t aoff1 = (int64_t)min(row0 + srow + kRowStep, g.rows - 1) * g.R + 8 * sch;
     const int64_t aoff2 = (int64_t)min(row0 + srow + 2 * kRowStep, g.rows - 1) * g.R + 8 * sch;
     const int64_t aoff3 = (int64_t)min(row0 + srow + 3 * kRowStep, g.rows - 1) * g.R + 8 * sch;
-    const int64_t boff0 = (int64_t)min(col0 + srow, g.cols - 1) * g.R + 8 * sch;
-    const int64_t boff1 = (int64_t)min(col0 + srow + kRowStep, g.cols - 1) * g.R + 8 * sch;
-    const int64_t boff2 = (int64_t)min(col0 + srow + 2 * kRowStep, g.cols - 1) * g.R + 8 * sch;
-    const int64_t boff3 = (int64_t)min(col0 + srow + 3 * kRowStep, g.cols - 1) * g.R + 8 * sch;
     const int lds0 = srow * kGPitch + 8 * sch;
     constexpr int kLdsStep = kRowStep * kGPitch;
+
+    // Staging of B, per form (offsets in the form's own elements):
+    //   kBf16: as A;  kTern2: threads t < 256 one 16-byte row (four words);
+    //   kInt8: thread t two 16-byte pieces of row t / 2 (bytes 32 (t % 2) ..).
+    const uint16_t* B16 = static_cast<const uint16_t*>(g.B);
+    const uint32_t* B2 = static_cast<const uint32_t*>(g.B);
+    const int8_t* B8 = static_cast<const int8_t*>(g.B);
+    int64_t boff0 = 0, boff1 = 0, boff2 = 0, boff3 = 0;
+    if constexpr (BK == BKind::kBf16) {
+        boff0 = (int64_t)min(col0 + srow, g.cols - 1) * g.R + 8 * sch;
+        boff1 = (int64_t)min(col0 + srow + kRowStep, g.cols - 1) * g.R + 8 * sch;
+        boff2 = (int64_t)min(col0 + srow + 2 * kRowStep, g.cols - 1) * g.R + 8 * sch;
+        boff3 = (int64_t)min(col0 + srow + 3 * kRowStep, g.cols - 1) * g.R + 8 * sch;
+    } else if constexpr (BK == BKind::kTern2) {
+        boff0 = (int64_t)min(col0 + (t & (kGT - 1)), g.cols - 1) * (g.R / 16);
+    } else {
+        boff0 = (int64_t)min(col0 + t / 2, g.cols - 1) * g.R + 32 * (t % 2);
+    }
+    const bool b_stager = BK != BKind::kTern2 || t < kGT;
     // Named registers (not arrays): the staged values stay in VGPRs.
     uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define BWD_LOAD_STAGE(st)                                                      \
-    do {                                                                        \
-        const int64_t o_ = (int64_t)(st) * kGK;                                 \
-        ra0 = *reinterpret_cast<const uint4*>(g.A + aoff0 + o_);                \
-        ra1 = *reinterpret_cast<const uint4*>(g.A + aoff1 + o_);                \
-        ra2 = *reinterpret_cast<const uint4*>(g.A + aoff2 + o_);                \
-        ra3 = *reinterpret_cast<const uint4*>(g.A + aoff3 + o_);                \
-        rb0 = *reinterpret_cast<const uint4*>(g.B + boff0 + o_);                \
-        rb1 = *reinterpret_cast<const uint4*>(g.B + boff1 + o_);                \
-        rb2 = *reinterpret_cast<const uint4*>(g.B + boff2 + o_);                \
-        rb3 = *reinterpret_cast<const uint4*>(g.B + boff3 + o_);                \
-    } while (0)
-#define BWD_STORE_STAGE(buf)                                                    \
-    do {                                                                        \
-        *reinterpret_cast<uint4*>(&As[buf][lds0]) = ra0;                        \
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + kLdsStep]) = ra1;             \
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + 2 * kLdsStep]) = ra2;         \
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + 3 * kLdsStep]) = ra3;         \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0]) = rb0;                        \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + kLdsStep]) = rb1;             \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 2 * kLdsStep]) = rb2;         \
-        *reinterpret_cast<uint4*>(&Bs[buf][lds0 + 3 * kLdsStep]) = rb3;         \
-    } while (0)
+    auto load_stage = [&](int st) {
+        const int64_t o = (int64_t)st * kGK;
+        ra0 = *reinterpret_cast<const uint4*>(g.A + aoff0 + o);
+        ra1 = *reinterpret_cast<const uint4*>(g.A + aoff1 + o);
+        ra2 = *reinterpret_cast<const uint4*>(g.A + aoff2 + o);
+        ra3 = *reinterpret_cast<const uint4*>(g.A + aoff3 + o);
+        if constexpr (BK == BKind::kBf16) {
+            rb0 = *reinterpret_cast<const uint4*>(B16 + boff0 + o);
+            rb1 = *reinterpret_cast<const uint4*>(B16 + boff1 + o);
+            rb2 = *reinterpret_cast<const uint4*>(B16 + boff2 + o);
+            rb3 = *reinterpret_cast<const uint4*>(B16 + boff3 + o);
+        } else if constexpr (BK == BKind::kTern2) {
+            if (b_stager) rb0 = *reinterpret_cast<const uint4*>(B2 + boff0 + (int64_t)st * (kGK / 16));
+        } else {
+            rb0 = *reinterpret_cast<const uint4*>(B8 + boff0 + o);
+            rb1 = *reinterpret_cast<const uint4*>(B8 + boff0 + o + 16);
+        }
+    };
+    auto store_stage = [&](int buf) {
+        *reinterpret_cast<uint4*>(&As[buf][lds0]) = ra0;
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + kLdsStep]) = ra1;
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + 2 * kLdsStep]) = ra2;
+        *reinterpret_cast<uint4*>(&As[buf][lds0 + 3 * kLdsStep]) = ra3;
+        uint8_t* bs = Bs[buf];
+        if constexpr (BK == BKind::kBf16) {
+            uint16_t* b16 = reinterpret_cast<uint16_t*>(bs);
+            *reinterpret_cast<uint4*>(&b16[lds0]) = rb0;
+            *reinterpret_cast<uint4*>(&b16[lds0 + kLdsStep]) = rb1;
+            *reinterpret_cast<uint4*>(&b16[lds0 + 2 * kLdsStep]) = rb2;
+            *reinterpret_cast<uint4*>(&b16[lds0 + 3 * kLdsStep]) = rb3;
+        } else if constexpr (BK == BKind::kTern2) {
+            if (b_stager) *reinterpret_cast<uint4*>(bs + t * kBPitch) = rb0;
+        } else {
+            // 8-byte pieces: the 72-byte row pitch is 8-byte aligned only
+            uint2* d = reinterpret_cast<uint2*>(bs + (t / 2) * kBPitch + 32 * (t % 2));
+            d[0] = make_uint2(rb0.x, rb0.y);
+            d[1] = make_uint2(rb0.z, rb0.w);
+            d[2] = make_uint2(rb1.x, rb1.y);
+            d[3] = make_uint2(rb1.z, rb1.w);
+        }
+    };
 
     f32x16 acc[kGFM][kGFN];
 #pragma unroll
@@ -263,38 +363,90 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
         for (int j = 0; j < kGFN; ++j) acc[i][j] = f32x16{};
 
     const int afrag = (wm * (kGT / kGWM) + (lane & 31)) * kGPitch + 8 * (lane >> 5);
-    const int bfrag = (wn * (kGT / kGWN) + (lane & 31)) * kGPitch + 8 * (lane >> 5);
+    const int bcol = wn * (kGT / kGWN) + (lane & 31);  // B row (output column) of fragment 0
+    const int half = lane >> 5;
+    // Stage st sits in buffer (st - st0) % 2.  The loads of stage st + 1 are
+    // issued during stage st - 1 (or here); during stage st they are written
+    // to the other buffer ahead of its last 16-deep step, and the loads of
+    // stage st + 2 go out right after.  The last step's MFMAs then keep the
+    // matrix core busy while the waves meet at the barrier that publishes
+    // stage st + 1, instead of the core idling through the LDS writes, the
+    // barrier and the next stage's first reads.  Loads still get a whole
+    // stage to land.
     if (st0 < st1) {
-        BWD_LOAD_STAGE(st0);
-        BWD_STORE_STAGE(0);
+        load_stage(st0);
+        store_stage(0);
+        if (st0 + 1 < st1) load_stage(st0 + 1);
         __syncthreads();
     }
+    // Fragments of one 16-deep step.  The next step's LDS reads are issued
+    // before this step's MFMAs, behind a scheduling barrier (the waves of a
+    // block run in lockstep between barriers and cannot hide that latency
+    // for each other), and the compact B forms are expanded between the
+    // MFMAs: the ternary words are in registers already; the int8 bytes are
+    // expanded after the step's later MFMAs, by when their read has landed.
+    struct Frags {
+        bf16x8 a[kGFM], b[kGFN];
+    };
+    uint4 bw[kGFN];    // kTern2: the lane's four words of each B row this stage
+    uint2 b8[kGFN];    // kInt8: the next step's B bytes
+    auto read_frags = [&](int buf, int ks, Frags& f) {
+#pragma unroll
+        for (int i = 0; i < kGFM; ++i)
+            f.a[i] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + i * 32 * kGPitch + 16 * ks]));
+#pragma unroll
+        for (int j = 0; j < kGFN; ++j) {
+            if constexpr (BK == BKind::kBf16) {
+                const uint16_t* b16 = reinterpret_cast<const uint16_t*>(Bs[buf]);
+                f.b[j] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4*>(&b16[(bcol + j * 32) * kGPitch + 8 * half + 16 * ks]));
+            } else if constexpr (BK == BKind::kInt8) {
+                b8[j] = *reinterpret_cast<const uint2*>(&Bs[buf][(bcol + j * 32) * kBPitch + 16 * ks + 8 * half]);
+            }
+        }
+    };
+    auto expand_b = [&](int ks, Frags& f, int j) {
+        if constexpr (BK == BKind::kTern2) {
+            const uint32_t wd = ks == 0 ? bw[j].x : (ks == 1 ? bw[j].y : (ks == 2 ? bw[j].z : bw[j].w));
+            f.b[j] = expand_ternary(wd, half);
+        } else if constexpr (BK == BKind::kInt8) {
+            f.b[j] = expand_int8(b8[j]);
+        }
+    };
+    constexpr int KS = kGK / 16;
+    constexpr int kMf = kGFM * kGFN;
     for (int st = st0; st < st1; ++st) {
         const int buf = (st - st0) & 1;
         const bool more = st + 1 < st1;
-        if (more) BWD_LOAD_STAGE(st + 1);
+        Frags cur, nxt;
+        if constexpr (BK == BKind::kTern2) {
 #pragma unroll
-        for (int ks = 0; ks < kGK / 16; ++ks) {
-            bf16x8 av[kGFM], bv[kGFN];
-#pragma unroll
-            for (int i = 0; i < kGFM; ++i)
-                av[i] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + i * 32 * kGPitch + 16 * ks]));
-#pragma unroll
-            for (int j = 0; j < kGFN; ++j)
-                bv[j] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(&Bs[buf][bfrag + j * 32 * kGPitch + 16 * ks]));
-#pragma unroll
-            for (int i = 0; i < kGFM; ++i)
-#pragma unroll
-                for (int j = 0; j < kGFN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < kGFN; ++j) bw[j] = *reinterpret_cast<const uint4*>(&Bs[buf][(bcol + j * 32) * kBPitch]);
         }
-        if (more) BWD_STORE_STAGE(buf ^ 1);
+        read_frags(buf, 0, cur);
+#pragma unroll
+        for (int j = 0; j < kGFN; ++j) expand_b(0, cur, j);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bool ahead = ks + 1 < KS;
+            if (ahead) read_frags(buf, ks + 1, nxt);
+            if (ks == KS - 1 && more) {
+                store_stage(buf ^ 1);
+                if (st + 2 < st1) load_stage(st + 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int idx = 0; idx < kMf; ++idx) {
+                const int i = idx / kGFN, j = idx % kGFN;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+                if (ahead && idx >= kMf - kGFN) expand_b(ks + 1, nxt, idx - (kMf - kGFN));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (ahead) cur = nxt;
+        }
         __syncthreads();
     }
-#undef BWD_LOAD_STAGE
-#undef BWD_STORE_STAGE
 
     const bool direct = g.splits == 1;
     const float alpha = direct ? (g.alpha ? *g.alpha : 1.0f) : 1.0f;
@@ -547,7 +699,7 @@ size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t Mp = round_up(M, kT), Np = round_up(N, kT);
     const int64_t nparts = (M + kNormRows - 1) / kNormRows;
     return act_stage_bytes(M, K) + (size_t)round_up(M * Np * 2, 256) + (size_t)round_up(N * Mp * 2, 256) +
-           (size_t)round_up(K * Mp * 2, 256) + (size_t)round_up(K * Np * 2, 256) +
+           (size_t)round_up(K * Mp, 256) + (size_t)round_up(K * (Np / 4), 256) +
            (size_t)round_up(nparts * K * 4, 256) + split_bytes(M, N, K);
 }
 
@@ -576,11 +728,12 @@ hipError_t launch_norm_backward(const BackwardArgs& a, float* partial, int64_t n
     return hipGetLastError();
 }
 
-hipError_t run_gemm(const uint16_t* A, const uint16_t* B, float* C, float* P, const float* alpha, int64_t rows,
+template <BKind BK>
+hipError_t run_gemm(const uint16_t* A, const void* B, float* C, float* P, const float* alpha, int64_t rows,
                     int64_t cols, int64_t R, hipStream_t stream) {
     const int sp = gemm_splits(rows, cols, R, kTargetCUs);
     GemmArgs g{A, B, C, P, alpha, (int)rows, (int)cols, (int)R, sp};
-    bwd_gemm_kernel<<<cdiv(rows, kGT) * cdiv(cols, kGT) * sp, kGThreads, 0, stream>>>(g);
+    bwd_gemm_kernel<BK><<<cdiv(rows, kGT) * cdiv(cols, kGT) * sp, kGThreads, 0, stream>>>(g);
     if (sp > 1) {
         const int64_t n = rows * cols;
         split_reduce_kernel<<<cdiv(n / 4, 256), 256, 0, stream>>>(P, sp, n, alpha, C);
@@ -600,10 +753,10 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     base += round_up(M * Np * 2, 256);
     uint16_t* A2 = reinterpret_cast<uint16_t*>(base);
     base += round_up(N * Mp * 2, 256);
-    uint16_t* qT = reinterpret_cast<uint16_t*>(base);
-    base += round_up(K * Mp * 2, 256);
-    uint16_t* wT = reinterpret_cast<uint16_t*>(base);
-    base += round_up(K * Np * 2, 256);
+    int8_t* qT = reinterpret_cast<int8_t*>(base);
+    base += round_up(K * Mp, 256);
+    uint32_t* wT = reinterpret_cast<uint32_t*>(base);
+    base += round_up(K * (Np / 4), 256);
     float* partial = reinterpret_cast<float*>(base);
     base += round_up(nparts * K * 4, 256);
     float* splitbuf = reinterpret_cast<float*>(base);
@@ -623,17 +776,17 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
                 dy_prep_kernel<false><<<grid, kPrepThreads, 0, stream>>>(
                     a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint2*>(A1), reinterpret_cast<uint2*>(A2));
             w_transpose_kernel<<<cdiv(Np, kT) * cdiv(K, kT), kPrepThreads, 0, stream>>>(
-                reinterpret_cast<const uint32_t*>(a.packed), (int)N, (int)K, (int)Np, reinterpret_cast<uint32_t*>(wT));
+                reinterpret_cast<const uint32_t*>(a.packed), (int)N, (int)K, (int)Np, wT);
         }
         q_transpose_kernel<<<cdiv(Mp, kT) * cdiv(K, kT), kPrepThreads, 0, stream>>>(
-            act.q, (int)M, (int)K, (int)Mp, reinterpret_cast<uint32_t*>(qT));
-        e = run_gemm(A1, wT, a.dx, splitbuf, a.gamma, M, K, Np, stream);
+            act.q, (int)M, (int)K, (int)Mp, qT);
+        e = run_gemm<BKind::kTern2>(A1, wT, a.dx, splitbuf, a.gamma, M, K, Np, stream);
         if (e != hipSuccess) return e;
         e = launch_norm_backward(a, partial, nparts_used, stream);
         if (e != hipSuccess) return e;
     }
     if (N > 0) {
-        e = run_gemm(A2, qT, a.dW, splitbuf, nullptr, N, K, Mp, stream);
+        e = run_gemm<BKind::kInt8>(A2, qT, a.dW, splitbuf, nullptr, N, K, Mp, stream);
         if (e != hipSuccess) return e;
     }
     dg_reduce_kernel<<<cdiv(K, kDgCols), kDgCols * kDgSplit, 0, stream>>>(partial, (int)nparts_used, (int)K, a.dg);
