@@ -519,6 +519,7 @@ def bench_crossover(torch, bl, wl, K, N, Ms, steps, warmup, stream):
              bl.BITLINEAR_KERNEL_GEMV: "gemv", bl.BITLINEAR_KERNEL_MFMA: "mfma"}
     table = {}
     for M in Ms:
+        log(f"[bench]   M={M}")
         x = torch.from_numpy(wl.x_normal(M, K, seed=M).view("int16")).to(DEV)
         y = torch.empty((M, N), dtype=torch.float32, device=DEV)
         ws = torch.empty(bl.bitlinear_forward_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
@@ -676,6 +677,9 @@ def main():
     ap.add_argument("--only", default="",
                     help="run only these secondary workloads after the headline (comma-separated; "
                          "available: backward, layer, crossover, prefill)")
+    ap.add_argument("--skip", default="",
+                    help="skip these secondary workloads in a full run (comma-separated: layer, crossover, "
+                         "backward); for profiling runs, where counter collection serialises every dispatch")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay line (its 1024-node graphs are slow under counter collection)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -711,6 +715,7 @@ def main():
 
     secondary = {}
     only = [w for w in args.only.split(",") if w]
+    skip = [w for w in args.skip.split(",") if w]
     if not args.no_secondary and not only:
         log("[bench] single layer M=1")
         secondary["decode_m1_single_layer"] = bench_single_layer(torch, bl, wl, 1, N, K, 200, stream)
@@ -759,7 +764,7 @@ def main():
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
 
-    if (not args.no_secondary and not only) or "layer" in only:
+    if (not args.no_secondary and not only and "layer" not in skip) or "layer" in only:
         log("[bench] MLGRU scan, one sequence of 2048 tokens, d = 2048")
         secondary["mlgru_scan_b1_t2048_d2048"] = bench_mlgru_scan(torch, bl, wl, 1, 2048, 2048, 20, 3, stream)
         secondary["mlgru_scan_b64_t256_d2048"] = bench_mlgru_scan(torch, bl, wl, 64, 256, 2048, 10, 2, stream)
@@ -768,13 +773,13 @@ def main():
         log("[bench] one layer, decoding 64 tokens one call each")
         secondary["layer_decode_b1"] = bench_layer_decode(torch, bl, wl, 2048, 5632, 64, 10, 2, stream)
 
-    if (not args.no_secondary and not only) or "crossover" in only:
+    if (not args.no_secondary and not only and "crossover" not in skip) or "crossover" in only:
         for K2, N2 in ((2560, 2560), (2560, 6912), (6912, 2560)):
             log(f"[bench] kernel crossover K={K2} N={N2}")
             secondary[f"crossover_k{K2}_n{N2}"] = bench_crossover(torch, bl, wl, K2, N2,
                                                                   (1, 2, 4, 8, 16, 32, 64, 128), 5, 1, stream)
 
-    if (not args.no_secondary and not only) or "backward" in only:
+    if (not args.no_secondary and not only and "backward" not in skip) or "backward" in only:
         log("[bench] backward (straight-through) 8192 x 2048 x 2048")
         secondary["backward_8192x2048x2048"] = bench_backward(torch, bl, wl, 8192, 2048, 2048,
                                                               max(10, args.steps // 2), args.warmup, stream)

@@ -37,7 +37,6 @@ namespace {
 
 constexpr int kT = 64;          // transpose tile edge
 constexpr int kPrepThreads = 256;
-constexpr uint32_t kBf16One = 0x3F80u;
 
 // ---------------------------------------------------------------------------
 // Operand preparation
@@ -186,17 +185,15 @@ __global__ __launch_bounds__(kPrepThreads) void w_transpose_kernel(const uint32_
 // [l % 32].  R % 64 == 0 (zero-padded operands); rows and cols are
 // arbitrary (loads clamped, stores masked).
 //
-// A is bf16 [rows][R].  B comes in one of three forms (BKind):
-//   kBf16  -- bf16 [cols][R];
+// A is bf16 [rows][R].  B comes in one of two compact forms (BKind):
 //   kTern2 -- ternary values as 2-bit codes [cols][R / 16] words (the
 //             layout of w_transpose_kernel); a lane reads its column's four
 //             words of a stage once and expands half a word per step;
 //   kInt8  -- int8 [cols][R]; a lane reads 8 bytes per step and converts.
-// The compact forms cut a stage's LDS traffic (the writes of the staged
-// operand and the per-step fragment reads), which together with the
-// barrier is what bounds the bf16 form: per 64-deep stage it moved 192 KiB
-// of fragment reads and 64 KiB of writes through an LDS that delivers
-// 128 B per clock, as long as the MFMAs of the stage take.
+// Compared with a bf16 B operand, the compact forms cut a stage's LDS
+// traffic (the writes of the staged operand and the per-step fragment
+// reads) from 256 KiB to 172 KiB (kTern2) and 190 KiB (kInt8) per 64-deep
+// stage, and the staging registers and global reads with it.
 //
 // When the output has fewer tiles than the chip has compute units, the
 // reduction is split over `splits` blocks per tile (whole stages each); split
@@ -212,16 +209,16 @@ constexpr int kGPitch = kGK + 8;  // bf16 per LDS row: 144 bytes, 16-byte reads 
 constexpr int kGWM = 2, kGWN = 4; // wave grid
 constexpr int kGThreads = kGWM * kGWN * kWave;
 constexpr int kGFM = kGT / kGWM / 32, kGFN = kGT / kGWN / 32;  // fragments per wave: 4 x 2
-constexpr int kGLoads = kGT * kGK * 2 / 16 / kGThreads;          // 16-byte loads per thread per bf16 operand: 4
+constexpr int kGLoads = kGT * kGK * 2 / 16 / kGThreads;          // 16-byte loads per thread of the bf16 A operand: 4
 constexpr int kMaxSplits = 8;
 constexpr int kI8Pitch = kGK + 8;  // bytes per int8 LDS row: 8-byte reads of 32 rows hit distinct bank pairs
 
-enum class BKind { kBf16, kTern2, kInt8 };
+enum class BKind { kTern2, kInt8 };
 
 // Bytes of one B row of a stage in LDS.
 template <BKind BK>
 constexpr int b_lds_pitch() {
-    return BK == BKind::kBf16 ? kGPitch * 2 : (BK == BKind::kTern2 ? kGK / 4 : kI8Pitch);
+    return BK == BKind::kTern2 ? kGK / 4 : kI8Pitch;
 }
 
 struct GemmArgs {
@@ -286,7 +283,7 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     // global -> register staging of A: rows t / 8 + 64 i, 16-byte chunk t % 8
     const int srow = t / 8, sch = t % 8;
     constexpr int kRowStep = kGThreads / 8;  // 64
-    static_assert(kGLoads == 4, "four staged loads per bf16 operand");
+    static_assert(kGLoads == 4, "four staged loads of A per thread");
     const int64_t aoff0 = (int64_t)min(row0 + srow, g.rows - 1) * g.R + 8 * sch;
     const int64_t aoff1 = (int64_t)min(row0 + srow + kRowStep, g.rows - 1) * g.R + 8 * sch;
     const int64_t aoff2 = (int64_t)min(row0 + srow + 2 * kRowStep, g.rows - 1) * g.R + 8 * sch;
@@ -295,37 +292,25 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     constexpr int kLdsStep = kRowStep * kGPitch;
 
     // Staging of B, per form (offsets in the form's own elements):
-    //   kBf16: as A;  kTern2: threads t < 256 one 16-byte row (four words);
+    //   kTern2: threads t < 256 one 16-byte row (four words);
     //   kInt8: thread t two 16-byte pieces of row t / 2 (bytes 32 (t % 2) ..).
-    const uint16_t* B16 = static_cast<const uint16_t*>(g.B);
     const uint32_t* B2 = static_cast<const uint32_t*>(g.B);
     const int8_t* B8 = static_cast<const int8_t*>(g.B);
-    int64_t boff0 = 0, boff1 = 0, boff2 = 0, boff3 = 0;
-    if constexpr (BK == BKind::kBf16) {
-        boff0 = (int64_t)min(col0 + srow, g.cols - 1) * g.R + 8 * sch;
-        boff1 = (int64_t)min(col0 + srow + kRowStep, g.cols - 1) * g.R + 8 * sch;
-        boff2 = (int64_t)min(col0 + srow + 2 * kRowStep, g.cols - 1) * g.R + 8 * sch;
-        boff3 = (int64_t)min(col0 + srow + 3 * kRowStep, g.cols - 1) * g.R + 8 * sch;
-    } else if constexpr (BK == BKind::kTern2) {
+    int64_t boff0 = 0;
+    if constexpr (BK == BKind::kTern2)
         boff0 = (int64_t)min(col0 + (t & (kGT - 1)), g.cols - 1) * (g.R / 16);
-    } else {
+    else
         boff0 = (int64_t)min(col0 + t / 2, g.cols - 1) * g.R + 32 * (t % 2);
-    }
     const bool b_stager = BK != BKind::kTern2 || t < kGT;
     // Named registers (not arrays): the staged values stay in VGPRs.
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1;
     auto load_stage = [&](int st) {
         const int64_t o = (int64_t)st * kGK;
         ra0 = *reinterpret_cast<const uint4*>(g.A + aoff0 + o);
         ra1 = *reinterpret_cast<const uint4*>(g.A + aoff1 + o);
         ra2 = *reinterpret_cast<const uint4*>(g.A + aoff2 + o);
         ra3 = *reinterpret_cast<const uint4*>(g.A + aoff3 + o);
-        if constexpr (BK == BKind::kBf16) {
-            rb0 = *reinterpret_cast<const uint4*>(B16 + boff0 + o);
-            rb1 = *reinterpret_cast<const uint4*>(B16 + boff1 + o);
-            rb2 = *reinterpret_cast<const uint4*>(B16 + boff2 + o);
-            rb3 = *reinterpret_cast<const uint4*>(B16 + boff3 + o);
-        } else if constexpr (BK == BKind::kTern2) {
+        if constexpr (BK == BKind::kTern2) {
             if (b_stager) rb0 = *reinterpret_cast<const uint4*>(B2 + boff0 + (int64_t)st * (kGK / 16));
         } else {
             rb0 = *reinterpret_cast<const uint4*>(B8 + boff0 + o);
@@ -338,13 +323,7 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
         *reinterpret_cast<uint4*>(&As[buf][lds0 + 2 * kLdsStep]) = ra2;
         *reinterpret_cast<uint4*>(&As[buf][lds0 + 3 * kLdsStep]) = ra3;
         uint8_t* bs = Bs[buf];
-        if constexpr (BK == BKind::kBf16) {
-            uint16_t* b16 = reinterpret_cast<uint16_t*>(bs);
-            *reinterpret_cast<uint4*>(&b16[lds0]) = rb0;
-            *reinterpret_cast<uint4*>(&b16[lds0 + kLdsStep]) = rb1;
-            *reinterpret_cast<uint4*>(&b16[lds0 + 2 * kLdsStep]) = rb2;
-            *reinterpret_cast<uint4*>(&b16[lds0 + 3 * kLdsStep]) = rb3;
-        } else if constexpr (BK == BKind::kTern2) {
+        if constexpr (BK == BKind::kTern2) {
             if (b_stager) *reinterpret_cast<uint4*>(bs + t * kBPitch) = rb0;
         } else {
             // 8-byte pieces: the 72-byte row pitch is 8-byte aligned only
@@ -395,22 +374,17 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
         for (int i = 0; i < kGFM; ++i)
             f.a[i] = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + i * 32 * kGPitch + 16 * ks]));
+        if constexpr (BK == BKind::kInt8) {
 #pragma unroll
-        for (int j = 0; j < kGFN; ++j) {
-            if constexpr (BK == BKind::kBf16) {
-                const uint16_t* b16 = reinterpret_cast<const uint16_t*>(Bs[buf]);
-                f.b[j] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(&b16[(bcol + j * 32) * kGPitch + 8 * half + 16 * ks]));
-            } else if constexpr (BK == BKind::kInt8) {
+            for (int j = 0; j < kGFN; ++j)
                 b8[j] = *reinterpret_cast<const uint2*>(&Bs[buf][(bcol + j * 32) * kBPitch + 16 * ks + 8 * half]);
-            }
         }
     };
     auto expand_b = [&](int ks, Frags& f, int j) {
         if constexpr (BK == BKind::kTern2) {
             const uint32_t wd = ks == 0 ? bw[j].x : (ks == 1 ? bw[j].y : (ks == 2 ? bw[j].z : bw[j].w));
             f.b[j] = expand_ternary(wd, half);
-        } else if constexpr (BK == BKind::kInt8) {
+        } else {
             f.b[j] = expand_int8(b8[j]);
         }
     };

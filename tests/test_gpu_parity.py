@@ -466,6 +466,46 @@ def test_forward_structural_zeros():
     assert np.all(y == 0)
 
 
+def _near_tie_rows(M, K, seed):
+    """Token rows whose two largest |x g| tie exactly with swapped factors,
+    x = 6, g = 10 at one position and x = 10, g = 6 at another: which of
+    the two is larger after the fp32 scaling (x r) g depends on each row's
+    r, so some rows' absmax comes from the one and some from the other."""
+    r = wl.rng(seed, 21)
+    x = (r.standard_normal((M, K)) * 0.5).astype(np.float32)
+    g = (0.5 + r.random(K)).astype(np.float32)
+    i1, i2 = int(r.integers(0, K // 2)), int(r.integers(K // 2, K))
+    x[:, i1], g[i1] = 6.0, 10.0
+    x[:, i2], g[i2] = 10.0, 6.0
+    x[M // 2:, [i1, i2]] *= -1.0
+    return wl.f32_to_bf16_bits(x), g
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (1, 2048), (2, 1024), (4, 4096), (1, 8192), (3, 2176), (1, 16384)])
+def test_decode_quantisation_matches_stand_alone(M, K):
+    """The fused decode kernel quantises its token rows itself; its codes and
+    scales must equal those of the stand-alone quantiser, so its output must
+    equal, bit for bit, the GEMV path's (stand-alone quantisation, then the
+    GEMV: the same integer sums and the same rescale), here on rows built so
+    that the two largest |x g| tie, and on plain rows."""
+    N = 96
+    W = wl.w_normal(N, K, seed=K)
+    packed, gamma = gu.pack_on_gpu(W)
+    for seed in range(6):
+        if seed < 4:
+            x, g = _near_tie_rows(M, K, seed + 10 * K)
+        else:
+            x, g = wl.x_normal(M, K, seed=seed), wl.rms_weight(K, "random", seed=seed)
+        _say("decode vs stand-alone quantisation", M, K, "seed", seed)
+        xd, gd = gu.to_dev_bf16(x), gu.to_dev(g)
+        y_dec = bl.bitlinear_forward(xd, gd, packed, gamma, kernel=DECODE).cpu().numpy()
+        y_gemv = bl.bitlinear_forward(xd, gd, packed, gamma, kernel=GEMV).cpu().numpy()
+        assert np.array_equal(y_dec.view(np.uint32), y_gemv.view(np.uint32)), seed
+        q, s = bl.bitlinear_quantize(xd, gd)
+        ref = gu.orc().rmsnorm_quant(x, g, 1e-6)
+        gu.assert_q_parity(q.cpu().numpy(), ref[0], s.cpu().numpy(), ref[1])
+
+
 def test_forward_empty_and_deterministic():
     N, K = 64, 128
     x, W, g = gu.oracle_inputs(40, N, K, seed=5)
