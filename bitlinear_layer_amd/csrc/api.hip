@@ -155,8 +155,9 @@ int run_decode(const uint16_t* x, const float* g, int64_t g_stride, const uint8_
 // already in `act`.
 int run_product(const bl::ActStage& act, const uint8_t* packed, const float* gamma, int64_t M,
                 int64_t N, int64_t K, int64_t batch, void* out, bl::Epilogue ep, int kernel,
-                hipStream_t stream) {
+                hipStream_t stream, const uint16_t* res = nullptr) {
     bl::ProductArgs a;
+    a.res = res;
     a.q = act.q;
     a.s = act.s;
     a.sumq = act.sumq;
@@ -205,7 +206,8 @@ int forward_impl(const uint16_t* x, const float* rms_weight, const uint8_t* pack
 // B independent GLU mixers of one shape (B = 1 for bitlinear_glu_forward).
 // With res (bf16 [B][M][D]) the mixer adds its output to res and writes the
 // bf16 sum to out_res instead of y (fused into the down projection when
-// that runs on the one-token decode kernel; y is then scratch).
+// that runs on the one-token decode kernel or on the large-tile product;
+// y is then scratch).
 int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
              const float* gamma_gu, const float* rms_w_down, const uint8_t* packed_down,
              const float* gamma_down, int64_t B, int64_t M, int64_t D, int64_t F, float eps,
@@ -249,6 +251,13 @@ int glu_impl(const uint16_t* x, const float* rms_w_gu, const uint8_t* packed_gu,
     if (res != nullptr && bl::decode_supported((int)M, (int)F))
         return run_decode(h, rms_w_down, B > 1 ? F : 0, packed_down, gamma_down, B, M, D, F, eps, out_res,
                           bl::Epilogue::kResBf16, st, res);
+    if (res != nullptr && B == 1 && bl::product_takes_residual((int)M, (int)D, (int)F)) {
+        // the residual added in the down projection's epilogue: u is read and
+        // out written in bf16, and no fp32 output passes through HBM
+        TRY(hip_status(bl::launch_quant(h, rms_w_down, rows, M, (int)F, eps, act_h, st), "quantise launch"));
+        return run_product(act_h, packed_down, gamma_down, M, D, F, 1, out_res, bl::Epilogue::kResBf16,
+                           BITLINEAR_KERNEL_AUTO, st, res);
+    }
     if (use_decode(M, F, BITLINEAR_KERNEL_AUTO, false)) {
         TRY(run_decode(h, rms_w_down, B > 1 ? F : 0, packed_down, gamma_down, B, M, D, F, eps, y,
                        bl::Epilogue::kF32, st));
@@ -333,7 +342,8 @@ int check_mlgru_shape(int64_t B, int64_t T, int64_t d) {
 // decode kernel gathers the f, c and g rows of each channel and applies the
 // recurrence step in its epilogue, and the output projection's adds the
 // residual in its epilogue (same fp32 arithmetic as the separate kernels,
-// so the same bits).
+// so the same bits).  Above 128 tokens the output projection's large-tile
+// product adds the residual in its epilogue likewise.
 int mlgru_impl(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_in,
                const float* gamma_in, const float* rms_w_out, const uint8_t* packed_out,
                const float* gamma_out, int64_t B, int64_t T, int64_t d, float eps, float* state,
@@ -365,6 +375,13 @@ int mlgru_impl(const uint16_t* x, const float* rms_w_in, const uint8_t* packed_i
     if (res != nullptr && bl::decode_supported((int)M, (int)d))
         return run_decode(w.p, rms_w_out, 0, packed_out, gamma_out, 1, M, d, d, eps, out_res,
                           bl::Epilogue::kResBf16, st, res);
+    if (res != nullptr && bl::product_takes_residual((int)M, (int)d, (int)d)) {
+        // the residual added in the output projection's epilogue
+        bl::ActStage act = bl::act_stage_carve(w.act, M, d);
+        TRY(hip_status(bl::launch_quant(w.p, rms_w_out, M, M, (int)d, eps, act, st), "quantise launch"));
+        return run_product(act, packed_out, gamma_out, M, d, d, 1, out_res, bl::Epilogue::kResBf16,
+                           BITLINEAR_KERNEL_AUTO, st, res);
+    }
     TRY(forward_impl(w.p, rms_w_out, packed_out, gamma_out, 1, M, d, d, eps, y, w.act, w.act_bytes, st,
                      BITLINEAR_KERNEL_AUTO));
     if (res != nullptr)

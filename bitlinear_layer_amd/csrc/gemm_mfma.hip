@@ -463,6 +463,7 @@ template <int BM, int WM, int WN, Epilogue EP>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a) {
     constexpr int BN = 256;
     constexpr bool kGlu = EP == Epilogue::kGluBf16;
+    constexpr bool kRes = EP == Epilogue::kResBf16;
     constexpr int kWavesPerBlock = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -753,9 +754,26 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     const int col0 = tn * kCols;
     const bool interior = m0 + BM <= M && col0 + kCols <= N && (int64_t)BM * N <= ((int64_t)1 << 28);
     if (interior) {
-        constexpr uint32_t kEsz = kGlu ? 2 : 4;  // bytes per output element
+        constexpr uint32_t kEsz = (kGlu || kRes) ? 2 : 4;  // bytes per output element
         char* const obase = static_cast<char*>(a.out) + ((tok0 + m0) * N + col0) * kEsz;
         const uint32_t lane_col = (kGlu ? wn * (TN / 2) : wn * TN) + (lane & 31);
+        // The residual is loaded whole before the first store: loads and
+        // stores share one in-order memory counter, so a load issued after
+        // stores would wait for them.
+        uint32_t resv[kRes ? FM : 1][kRes ? 16 : 1][kRes ? FN : 1];
+        if constexpr (kRes) {
+            const char* const rbase = reinterpret_cast<const char*>(a.res) + ((tok0 + m0) * N + col0) * kEsz;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm * TM + i * 32 + 4 * (lane >> 5) + (v & 3) + 8 * (v >> 2);
+                    const uint32_t off = ((uint32_t)r * (uint32_t)N + lane_col) * kEsz;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        resv[i][v][j] = *reinterpret_cast<const uint16_t*>(rbase + off + j * 32 * kEsz);
+                }
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int r0 = wm * TM + i * 32 + 4 * (lane >> 5);
@@ -777,10 +795,15 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         const int32_t val = acc[i][j][v] - sq;
-                        if (EP == Epilogue::kI32)
+                        if constexpr (EP == Epilogue::kI32) {
                             *reinterpret_cast<int32_t*>(obase + off + j * 32 * kEsz) = val;
-                        else
+                        } else if constexpr (kRes) {
+                            // u = bf16(res + y), as the stand-alone residual pass forms it
+                            *reinterpret_cast<uint16_t*>(obase + off + j * 32 * kEsz) = (uint16_t)f32_to_bf16_bits(
+                                __uint_as_float(resv[i][v][j] << 16) + rescale(val, cs));
+                        } else {
                             *reinterpret_cast<float*>(obase + off + j * 32 * kEsz) = rescale(val, cs);
+                        }
                     }
                 }
             }
@@ -813,8 +836,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
                     const int n = tn * BN + wn * TN + j * 32 + (lane & 31);
                     if (n < N) {
                         const int32_t val = acc[i][j][v] - sq;
-                        if (EP == Epilogue::kI32)
+                        if constexpr (EP == Epilogue::kI32)
                             static_cast<int32_t*>(a.out)[tk * N + n] = val;
+                        else if constexpr (kRes)
+                            static_cast<uint16_t*>(a.out)[tk * N + n] = (uint16_t)f32_to_bf16_bits(
+                                __uint_as_float((uint32_t)a.res[tk * N + n] << 16) + rescale(val, cs));
                         else
                             static_cast<float*>(a.out)[tk * N + n] = rescale(val, cs);
                     }
@@ -879,12 +905,24 @@ hipError_t launch_ep(const ProductArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+bool product_takes_residual(int M, int N, int K) {
+    return M > 128 && K % kBK == 0 && (int64_t)256 * (K / 4) < ((int64_t)1 << 32) && N >= 1;
+}
+
 hipError_t launch_gemm_mfma(const ProductArgs& a, Epilogue ep, hipStream_t stream) {
+    if (ep == Epilogue::kResBf16) {
+        // The large-tile kernel with 128 x 256 tiles (8 waves of 64 x 64):
+        // each lane holds the 64 residual values of its fragments before the
+        // stores; the 256-row tile's 128 would not fit beside its registers.
+        if (!product_takes_residual(a.M, a.N, a.K) || a.res == nullptr) return hipErrorInvalidValue;
+        return launch_x32<128, 2, 4, Epilogue::kResBf16>(a, stream);
+    }
     if (skinny_supported(a.M, a.K, ep)) return launch_skinny(a, ep, stream);
     switch (ep) {
         case Epilogue::kF32: return launch_ep<Epilogue::kF32>(a, stream);
         case Epilogue::kI32: return launch_ep<Epilogue::kI32>(a, stream);
         case Epilogue::kGluBf16: return launch_ep<Epilogue::kGluBf16>(a, stream);
+        default: break;
     }
     return hipErrorInvalidValue;
 }

@@ -54,7 +54,8 @@ enum class Epilogue {
     kF32,        // y[m][n] = float(acc) * (gamma / s[m])
     kI32,        // acc[m][n]
     kGluBf16,    // h[m][f] = bf16(silu(z[m][f]) * z[m][F + f]), z = float(acc) * gamma / s
-    kResBf16,    // u[m][n] = bf16(res[m][n] + y[m][n]): a residual added (fused decode kernel only)
+    kResBf16,    // u[m][n] = bf16(res[m][n] + y[m][n]): a residual added (fused decode kernel, and
+                 // the large-tile product where product_takes_residual() holds)
     kMlgruStep,  // one MLGRU token per row m (its own sequence): z = y over rows n, d + n, 2d + n,
                  // state[m][n] updated, p[m][n] = bf16(g h) (fused decode kernel only)
 };
@@ -73,7 +74,12 @@ struct ProductArgs {
     int K;
     int batch;
     void* out;  // float*, int32_t* or uint16_t* by epilogue
+    const uint16_t* res = nullptr;  // kResBf16: bf16 [batch][M][N], the same layout as out
 };
+
+// Whether launch_gemm_mfma takes Epilogue::kResBf16 for this shape (the
+// large-tile kernel: more than 128 tokens, K a multiple of 128).
+bool product_takes_residual(int M, int N, int K);
 
 hipError_t launch_gemv(const ProductArgs& a, Epilogue ep, hipStream_t stream);
 hipError_t launch_gemm_mfma(const ProductArgs& a, Epilogue ep, hipStream_t stream);

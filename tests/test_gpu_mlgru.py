@@ -382,3 +382,32 @@ def test_layer_one_token_fused_equals_composed(B, d, F):
     assert torch.equal(y_mix.reshape(B, d), y)
     assert torch.equal(out.reshape(B, d), ref)
     assert torch.equal(s_fused, s_comp)
+
+
+# (B, T, d, F): more than 128 tokens, so the output and down projections run
+# on the large-tile product, which adds the residual in its epilogue.
+MANY_TOKENS = [(1, 300, 256, 384), (2, 160, 128, 256), (1, 1024, 2048, 5632)]
+
+
+@pytest.mark.parametrize("B,T,d,F", MANY_TOKENS)
+def test_layer_many_tokens_fused_equals_composed(B, T, d, F):
+    """Above 128 tokens the output projection and the GLU down projection
+    add the residual in the large-tile product's epilogue, with the fp32
+    arithmetic of the separate residual pass, so the layer's output and state
+    must equal, bit for bit, the same layer composed from the separate entry
+    points (token mixer, bf16(x + y), channel mixer, bf16(u + y))."""
+    _say("many-token fused vs composed", B, T, d, F)
+    (_, _), (mdev, gdev) = _layer(d, F, seed=3 * B + T)
+    x = gu.to_dev_bf16(wl.x_normal(B * T, d, seed=B + T).reshape(B, T, d))
+    h0 = wl.rng(B + T, 8).standard_normal((B, d)).astype(np.float32)
+    s_fused = gu.to_dev(h0.copy())
+    out = bl.bitlinear_layer_forward(x, mdev, gdev, s_fused)
+
+    s_comp = gu.to_dev(h0.copy())
+    y = bl.bitlinear_mlgru_forward(x, *mdev, s_comp)
+    u = _bf16_add(x, y)
+    yg = bl.bitlinear_glu_forward(u.reshape(B * T, d), *gdev)
+    ref = _bf16_add(u.reshape(B * T, d), yg)
+    torch.cuda.synchronize()
+    assert torch.equal(out.reshape(B * T, d), ref)
+    assert torch.equal(s_fused, s_comp)
