@@ -14,23 +14,26 @@
 // bits), r from x.
 //
 // Both products are dense floating-point contractions and run on the bf16
-// matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Their
-// operands are laid out with the reduction index contiguous and zero-padded
-// to a multiple of 64:
+// matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation), with the
+// reduction index contiguous in LDS and zero-padded to a multiple of 64:
 //   dxn [M][K] = gamma * A1 [M][Np] . wT [K][Np]^T,   A1 = bf16(dy),  wT = w^T
-//   dW  [N][K] =         A2 [N][Mp] . qT [K][Mp]^T,   A2 = bf16(dy / s)^T, qT = q^T
-// w and q are exact in bf16, so the only roundings besides the fp32
-// accumulation are those of dy and dy / s to bf16.  The second operands
-// stay compact until they reach registers: wT as 2-bit codes (16 reduction
-// indices per word) and qT as int8, each expanded to bf16 fragments right
-// before its MFMAs, which keeps the LDS traffic of a stage well below what
-// two bf16 operands take.
+//   dW  [N][K] =         A2 [N][Mp] . qT [K][Mp]^T,   A2 = bf16(dy (1 / s))^T, qT = q^T
+// None of A1, A2 or qT is written to memory: the products read dy (fp32)
+// and q (int8) where the forward left them and form their operands while
+// staging a tile into LDS -- A1 by rounding rows of dy, A2 by scaling
+// columns of dy with 1 / s and rounding, qT by transposing 8 x 4 blocks of
+// q bytes in registers.  w and q are exact in bf16, so the only roundings
+// besides the fp32 accumulation are those of dy and dy (1 / s) to bf16.
+// The weight operand stays compact until it reaches registers: wT as 2-bit
+// codes (16 reduction indices per word), expanded to bf16 fragments right
+// before its MFMAs.
 //
-// Kernels: dy_prep (A1 and A2 from one read of dy), q_transpose (int8),
-// w_transpose (2-bit codes, transposed), the NT GEMM, norm_backward (dx in
-// place over dxn, per-block dg partials) and dg_reduce (fixed order, fp64).
+// Kernels: w_transpose (2-bit codes, transposed), the NT GEMM (twice),
+// norm_backward (dx in place over dxn, per-block dg partials) and dg_reduce
+// (fixed order, fp64).
 #include "device_common.h"
 #include "launch.h"
+#include "xcd.h"
 
 namespace bl {
 namespace {
@@ -41,98 +44,6 @@ constexpr int kPrepThreads = 256;
 // ---------------------------------------------------------------------------
 // Operand preparation
 // ---------------------------------------------------------------------------
-
-// One 64 x 64 tile of dy: A1[m][n] = bf16(dy[m][n]) for m < M, n < Np (zero
-// past N); A2[n][m] = bf16(dy[m][n] / s[m]) for n < N, m < Mp (zero past M).
-// Rows of dy are read 16 bytes at a time when N % 4 == 0 (VEC), and both
-// outputs are written four bf16 (8 bytes) at a time.
-template <bool VEC>
-__global__ __launch_bounds__(kPrepThreads) void dy_prep_kernel(const float* __restrict__ dy,
-                                                               const float* __restrict__ s, int M, int N,
-                                                               int Mp, int Np, uint2* __restrict__ A1,
-                                                               uint2* __restrict__ A2) {
-    __shared__ float tile[kT][kT + 1];
-    __shared__ float sv[kT];
-    const int64_t mt = Mp / kT;  // tiles along m; the grid is flat (m fastest)
-    const int m0 = (int)(blockIdx.x % mt) * kT, n0 = (int)(blockIdx.x / mt) * kT;
-    const int t = threadIdx.x;
-    if (t < kT) sv[t] = (m0 + t < M) ? s[m0 + t] : 1.0f;
-    // 64 rows x 16 groups of four columns
-#pragma unroll
-    for (int i = 0; i < kT / 16; ++i) {
-        const int r = t / 16 + 16 * i, c = 4 * (t % 16);
-        const int m = m0 + r, n = n0 + c;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (m < M) {
-            const float* src = dy + (int64_t)m * N + n;
-            if (VEC) {
-                if (n < N) v = *reinterpret_cast<const float4*>(src);
-            } else {
-                v.x = n < N ? src[0] : 0.f;
-                v.y = n + 1 < N ? src[1] : 0.f;
-                v.z = n + 2 < N ? src[2] : 0.f;
-                v.w = n + 3 < N ? src[3] : 0.f;
-            }
-        }
-        tile[r][c] = v.x;
-        tile[r][c + 1] = v.y;
-        tile[r][c + 2] = v.z;
-        tile[r][c + 3] = v.w;
-    }
-    __syncthreads();
-    auto pack4 = [](float a, float b, float c, float d) {
-        return make_uint2(f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
-                          f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16));
-    };
-    // A1 rows m, four columns per thread
-#pragma unroll
-    for (int i = 0; i < kT / 16; ++i) {
-        const int r = t / 16 + 16 * i, c = 4 * (t % 16);
-        const int m = m0 + r;
-        if (m < M) A1[((int64_t)m * Np + n0 + c) / 4] = pack4(tile[r][c], tile[r][c + 1], tile[r][c + 2], tile[r][c + 3]);
-    }
-    // A2 rows n, four tokens per thread; dy / s is an IEEE fp32 division
-#pragma unroll
-    for (int i = 0; i < kT / 16; ++i) {
-        const int c = t / 16 + 16 * i, r = 4 * (t % 16);
-        const int n = n0 + c;
-        if (n < N)
-            A2[((int64_t)n * Mp + m0 + r) / 4] = pack4(tile[r][c] / sv[r], tile[r + 1][c] / sv[r + 1],
-                                                       tile[r + 2][c] / sv[r + 2], tile[r + 3][c] / sv[r + 3]);
-    }
-}
-
-// qT[k][m] = q[m][k] (int8) for k < K, m < Mp (zero past M).  K % 16 == 0.
-__global__ __launch_bounds__(kPrepThreads) void q_transpose_kernel(const int8_t* __restrict__ q, int M, int K,
-                                                                   int Mp, int8_t* __restrict__ qT) {
-    __shared__ int8_t tile[kT][kT + 4];
-    const int64_t mt = Mp / kT;  // flat grid, m fastest
-    const int m0 = (int)(blockIdx.x % mt) * kT, k0 = (int)(blockIdx.x / mt) * kT;
-    const int t = threadIdx.x;
-    {
-        const int r = t / 4, ch = t % 4;  // 64 rows x 4 chunks of 16 codes
-        const int m = m0 + r, k = k0 + 16 * ch;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (m < M && k < K) v = *reinterpret_cast<const uint4*>(q + (int64_t)m * K + k);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[r][16 * ch]);
-        dst[0] = v.x;
-        dst[1] = v.y;
-        dst[2] = v.z;
-        dst[3] = v.w;
-    }
-    __syncthreads();
-    // 64 columns x 4 runs of 16 tokens: one 16-byte store per thread
-    const int c = t / 4, r0 = 16 * (t % 4);
-    const int k = k0 + c;
-    if (k < K) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)(uint8_t)tile[r0 + 4 * i][c] | ((uint32_t)(uint8_t)tile[r0 + 4 * i + 1][c] << 8) |
-                   ((uint32_t)(uint8_t)tile[r0 + 4 * i + 2][c] << 16) | ((uint32_t)(uint8_t)tile[r0 + 4 * i + 3][c] << 24);
-        *reinterpret_cast<uint4*>(qT + (int64_t)k * Mp + m0 + r0) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
 
 // wT[k] holds w[n][k] for n < Np (zero past N) as 2-bit codes, 16 values of
 // n per 32-bit word, from the packed rows [N][K/4] (weight j of a 16-weight
@@ -185,15 +96,30 @@ __global__ __launch_bounds__(kPrepThreads) void w_transpose_kernel(const uint32_
 // [l % 32].  R % 64 == 0 (zero-padded operands); rows and cols are
 // arbitrary (loads clamped, stores masked).
 //
-// A is bf16 [rows][R].  B comes in one of two compact forms (BKind):
-//   kTern2 -- ternary values as 2-bit codes [cols][R / 16] words (the
-//             layout of w_transpose_kernel); a lane reads its column's four
-//             words of a stage once and expands half a word per step;
-//   kInt8  -- int8 [cols][R]; a lane reads 8 bytes per step and converts.
+// Both operands are formed while a stage is staged into LDS (global loads
+// into registers, conversion, LDS writes).  A comes from dy [M][N] fp32
+// (AKind):
+//   kRows       -- A[m][n] = bf16(dy[m][n]), zero for n >= N (dxn: rows M,
+//                  R = Np); a thread converts 8 consecutive n of 4 rows;
+//   kColsScaled -- A[n][m] = bf16(dy[m][n] * (1 / s[m])), zero for m >= M
+//                  (dW: rows N, R = Mp); a thread reads 4 consecutive n of
+//                  8 rows m, so that each of its 4 LDS rows gets 8
+//                  consecutive reduction indices from one 16-byte write.
+// VEC: N % 4 == 0, so 16-byte loads of dy rows are aligned and a 4-wide
+// chunk is wholly inside or outside the row; else loads are per element.
+// B comes in one of two compact forms (BKind):
+//   kTern2    -- ternary values as 2-bit codes [cols][R / 16] words (the
+//                layout of w_transpose_kernel); a lane reads its column's
+//                four words of a stage once and expands half a word per step;
+//   kInt8Cols -- q [M][cols] int8 as the forward wrote it: a thread reads 4
+//                bytes of 8 rows m and transposes the 8 x 4 block with byte
+//                permutes into 8 reduction bytes for each of 4 columns; in
+//                LDS each column holds its stage's 64 bytes, and a lane
+//                reads 8 bytes per step and converts them exactly.
 // Compared with a bf16 B operand, the compact forms cut a stage's LDS
 // traffic (the writes of the staged operand and the per-step fragment
-// reads) from 256 KiB to 172 KiB (kTern2) and 190 KiB (kInt8) per 64-deep
-// stage, and the staging registers and global reads with it.
+// reads) from 256 KiB to 172 KiB (kTern2) and 190 KiB (kInt8Cols) per
+// 64-deep stage.
 //
 // When the output has fewer tiles than the chip has compute units, the
 // reduction is split over `splits` blocks per tile (whole stages each); split
@@ -209,11 +135,11 @@ constexpr int kGPitch = kGK + 8;  // bf16 per LDS row: 144 bytes, 16-byte reads 
 constexpr int kGWM = 2, kGWN = 4; // wave grid
 constexpr int kGThreads = kGWM * kGWN * kWave;
 constexpr int kGFM = kGT / kGWM / 32, kGFN = kGT / kGWN / 32;  // fragments per wave: 4 x 2
-constexpr int kGLoads = kGT * kGK * 2 / 16 / kGThreads;          // 16-byte loads per thread of the bf16 A operand: 4
 constexpr int kMaxSplits = 8;
 constexpr int kI8Pitch = kGK + 8;  // bytes per int8 LDS row: 8-byte reads of 32 rows hit distinct bank pairs
 
-enum class BKind { kTern2, kInt8 };
+enum class AKind { kRows, kColsScaled };
+enum class BKind { kTern2, kInt8Cols };
 
 // Bytes of one B row of a stage in LDS.
 template <BKind BK>
@@ -222,12 +148,14 @@ constexpr int b_lds_pitch() {
 }
 
 struct GemmArgs {
-    const uint16_t* A;
-    const void* B;
+    const float* dy;     // [M][N]
+    const float* s;      // [M]: the activation scales (kColsScaled)
+    const void* B;       // kTern2: wT words [cols][R / 16]; kInt8Cols: q [M][cols]
     float* C;            // final output (splits == 1)
     float* P;            // split partials (splits > 1)
     const float* alpha;  // device scalar, or nullptr for 1
     int rows, cols, R, splits;
+    int M, N;            // shape of dy
 };
 
 // Eight ternary values of a w_transpose word as bf16 (-1, 0, +1): the half
@@ -263,16 +191,46 @@ __device__ __forceinline__ bf16x8 expand_int8(uint2 v) {
     return __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
-template <BKind BK>
+// Two fp32 values as a bf16 pair (round to nearest even), lo in bits 0..15.
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+__device__ __forceinline__ float f4_get(const float4& v, int j) {
+    return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+// Four consecutive floats of a dy row from column n: one 16-byte load when
+// VEC (n % 4 == 0, N % 4 == 0), else per element; zero past the row's end.
+template <bool VEC>
+__device__ __forceinline__ float4 load_dy4(const float* row, int n, int N) {
+    if constexpr (VEC) {
+        return n < N ? *reinterpret_cast<const float4*>(row + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+        return make_float4(n < N ? row[n] : 0.f, n + 1 < N ? row[n + 1] : 0.f, n + 2 < N ? row[n + 2] : 0.f,
+                           n + 3 < N ? row[n + 3] : 0.f);
+    }
+}
+
+template <AKind AK, BKind BK, bool VEC>
 __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     constexpr int kBPitch = b_lds_pitch<BK>();
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kGT * kGPitch];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGT * kBPitch];
+    // Work item f = split * tiles + tile, output column tiles fastest, under
+    // the XCD map: an XCD takes whole rows of tiles of one split, so each
+    // A panel (a row of tiles' rows over the split's stages) is fetched into
+    // one L2, and B panels into as many as there are splits.
     const int ntc = (g.cols + kGT - 1) / kGT;
-    const int tile = blockIdx.x / g.splits, split = blockIdx.x % g.splits;
+    const int tiles = (int)(gridDim.x / g.splits);
+    const int f = xcd_tile(blockIdx.x, gridDim.x);
+    const int split = f / tiles, tile = f % tiles;
     const int tr = tile / ntc, tc = tile % ntc;
     const int row0 = tr * kGT, col0 = tc * kGT;
-    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    const int t = threadIdx.x, lane = t & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
     const int wm = wave / kGWN, wn = wave % kGWN;
 
     // stages [st0, st1) of this split
@@ -280,59 +238,140 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     const int per = (nst + g.splits - 1) / g.splits;
     const int st0 = min(split * per, nst), st1 = min(st0 + per, nst);
 
-    // global -> register staging of A: rows t / 8 + 64 i, 16-byte chunk t % 8
+    // Staging of A (eight 4-float pieces per thread and stage):
+    //   kRows: rows srow + 64 p (p < 4), stage elements 8 sch .. 8 sch + 7,
+    //          written as one 16-byte bf16 piece per row;
+    //   kColsScaled: dy rows m = 64 st + 8 wave + i (i < 8), columns
+    //          row0 + 4 lane .. + 3, written as 8 bf16 of reduction index
+    //          8 wave .. 8 wave + 7 into each of the LDS rows 4 lane + j.
     const int srow = t / 8, sch = t % 8;
     constexpr int kRowStep = kGThreads / 8;  // 64
-    static_assert(kGLoads == 4, "four staged loads of A per thread");
-    const int64_t aoff0 = (int64_t)min(row0 + srow, g.rows - 1) * g.R + 8 * sch;
-    const int64_t aoff1 = (int64_t)min(row0 + srow + kRowStep, g.rows - 1) * g.R + 8 * sch;
-    const int64_t aoff2 = (int64_t)min(row0 + srow + 2 * kRowStep, g.rows - 1) * g.R + 8 * sch;
-    const int64_t aoff3 = (int64_t)min(row0 + srow + 3 * kRowStep, g.rows - 1) * g.R + 8 * sch;
-    const int lds0 = srow * kGPitch + 8 * sch;
     constexpr int kLdsStep = kRowStep * kGPitch;
+    const int lds0 = srow * kGPitch + 8 * sch;
+    int64_t arow[4] = {0, 0, 0, 0};
+    if constexpr (AK == AKind::kRows) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) arow[p] = (int64_t)min(row0 + srow + p * kRowStep, g.rows - 1) * g.N;
+    }
+    // kColsScaled: first of the thread's four dy columns (clamped into the
+    // row when VEC; those output rows are not stored)
+    const int ncol = AK == AKind::kColsScaled ? (VEC ? min(row0 + 4 * lane, g.N - 4) : row0 + 4 * lane) : 0;
+    float4 ra[8];
+    float sl = 1.0f;  // kColsScaled: lane l holds s of the stage's row 8 wave + l % 8
 
-    // Staging of B, per form (offsets in the form's own elements):
+    // Staging of B:
     //   kTern2: threads t < 256 one 16-byte row (four words);
-    //   kInt8: thread t two 16-byte pieces of row t / 2 (bytes 32 (t % 2) ..).
+    //   kInt8Cols: q rows m = 64 st + 8 wave + i (i < 8), 4 bytes from column
+    //          col0 + 4 lane (clamped into the row: cols % 16 == 0).
     const uint32_t* B2 = static_cast<const uint32_t*>(g.B);
     const int8_t* B8 = static_cast<const int8_t*>(g.B);
-    int64_t boff0 = 0;
-    if constexpr (BK == BKind::kTern2)
-        boff0 = (int64_t)min(col0 + (t & (kGT - 1)), g.cols - 1) * (g.R / 16);
-    else
-        boff0 = (int64_t)min(col0 + t / 2, g.cols - 1) * g.R + 32 * (t % 2);
+    const int64_t boff0 = BK == BKind::kTern2 ? (int64_t)min(col0 + (t & (kGT - 1)), g.cols - 1) * (g.R / 16) : 0;
+    const int kcol = BK == BKind::kInt8Cols ? min(col0 + 4 * lane, g.cols - 4) : 0;
     const bool b_stager = BK != BKind::kTern2 || t < kGT;
-    // Named registers (not arrays): the staged values stay in VGPRs.
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1;
+    uint4 rb0;
+    uint32_t rq[8];
+
     auto load_stage = [&](int st) {
-        const int64_t o = (int64_t)st * kGK;
-        ra0 = *reinterpret_cast<const uint4*>(g.A + aoff0 + o);
-        ra1 = *reinterpret_cast<const uint4*>(g.A + aoff1 + o);
-        ra2 = *reinterpret_cast<const uint4*>(g.A + aoff2 + o);
-        ra3 = *reinterpret_cast<const uint4*>(g.A + aoff3 + o);
+        if constexpr (AK == AKind::kRows) {
+            const int n = st * kGK + 8 * sch;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                ra[2 * p] = load_dy4<VEC>(g.dy + arow[p], n, g.N);
+                ra[2 * p + 1] = load_dy4<VEC>(g.dy + arow[p], n + 4, g.N);
+            }
+        } else {
+            // rows m >= M read as zero (the reduction padding); s is then
+            // read at a valid index and does not matter.  s goes through a
+            // vector load: a scalar load would share the LDS reads' counter
+            // and, returning out of order, make every fragment wait for it.
+            sl = g.s[min(st * kGK + 8 * wave + (lane & 7), g.M - 1)];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int m = st * kGK + 8 * wave + i;
+                const int mc = min(m, g.M - 1);
+                ra[i] = m < g.M ? load_dy4<VEC>(g.dy + (int64_t)mc * g.N, ncol, g.N) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
         if constexpr (BK == BKind::kTern2) {
             if (b_stager) rb0 = *reinterpret_cast<const uint4*>(B2 + boff0 + (int64_t)st * (kGK / 16));
         } else {
-            rb0 = *reinterpret_cast<const uint4*>(B8 + boff0 + o);
-            rb1 = *reinterpret_cast<const uint4*>(B8 + boff0 + o + 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int mc = min(st * kGK + 8 * wave + i, g.M - 1);
+                rq[i] = *reinterpret_cast<const uint32_t*>(B8 + (int64_t)mc * g.cols + kcol);
+            }
         }
     };
-    auto store_stage = [&](int buf) {
-        *reinterpret_cast<uint4*>(&As[buf][lds0]) = ra0;
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + kLdsStep]) = ra1;
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + 2 * kLdsStep]) = ra2;
-        *reinterpret_cast<uint4*>(&As[buf][lds0 + 3 * kLdsStep]) = ra3;
+    // Conversion and LDS writes of the staged registers, in pieces that the
+    // main loop spreads between the MFMAs of a stage's last 16-deep step
+    // (a wave's VALU work then issues while its MFMAs run):
+    //   kRows: pieces 0..3, one LDS row each;
+    //   kColsScaled: piece 0 the reciprocals 1 / s of the stage's 8 rows (one
+    //          division per lane, broadcast from lanes 0..7), pieces 1..4 one
+    //          LDS row (dy column) each;
+    //   kTern2: one piece;
+    //   kInt8Cols: pieces 0 and 2 the row-pair byte interleaves of columns
+    //          0, 1 and of columns 2, 3, pieces 1 and 3 the LDS rows of
+    //          those columns.
+    // The transposing forms write LDS rows 4 lane + j; with rows of 144
+    // (A) or 72 (B) bytes that would put 4 lanes on each bank.  Their
+    // 16-byte (A) and 8-byte (B) chunks are therefore XOR-swizzled by row:
+    // chunk c of row r sits at c ^ ((r >> 4) & 3) (A) and c ^ ((r >> 5) & 3)
+    // (B), which spreads the writes of any 16 (A) or 32 (B) lanes over all
+    // banks and keeps the fragment reads conflict-free.
+    constexpr bool kSwz = AK == AKind::kColsScaled;
+    static_assert(kSwz == (BK == BKind::kInt8Cols), "the dW operand forms go together");
+    constexpr int kPiecesA = AK == AKind::kRows ? 4 : 5;
+    constexpr int kPiecesB = BK == BKind::kTern2 ? 1 : 4;
+    constexpr int kPieces = kPiecesA + kPiecesB;
+    float inv[8];
+    uint32_t e[4];
+    auto store_piece = [&](int buf, int pc) {
+        if (pc < kPiecesA) {
+            if constexpr (AK == AKind::kRows) {
+                const float4 u = ra[2 * pc], v = ra[2 * pc + 1];
+                *reinterpret_cast<uint4*>(&As[buf][lds0 + pc * kLdsStep]) =
+                    make_uint4(bf16_pair(u.x, u.y), bf16_pair(u.z, u.w), bf16_pair(v.x, v.y), bf16_pair(v.z, v.w));
+            } else if (pc == 0) {
+                const float r = 1.0f / sl;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) inv[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), i));
+            } else {
+                const int j = pc - 1;
+                uint32_t d[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    d[h] = bf16_pair(f4_get(ra[2 * h], j) * inv[2 * h], f4_get(ra[2 * h + 1], j) * inv[2 * h + 1]);
+                *reinterpret_cast<uint4*>(&As[buf][(4 * lane + j) * kGPitch + 8 * (wave ^ ((lane >> 2) & 3))]) =
+                    make_uint4(d[0], d[1], d[2], d[3]);
+            }
+            return;
+        }
+        const int pb = pc - kPiecesA;
         uint8_t* bs = Bs[buf];
         if constexpr (BK == BKind::kTern2) {
             if (b_stager) *reinterpret_cast<uint4*>(bs + t * kBPitch) = rb0;
+        } else if ((pb & 1) == 0) {
+            // 8 x 4 bytes (row i, column c) -> e[pr] = rows 2 pr, 2 pr + 1 of
+            // columns 2 hc and 2 hc + 1, interleaved byte by byte
+            const uint32_t sel = pb == 0 ? 0x05010400u : 0x07030602u;
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) e[pr] = __builtin_amdgcn_perm(rq[2 * pr + 1], rq[2 * pr], sel);
         } else {
-            // 8-byte pieces: the 72-byte row pitch is 8-byte aligned only
-            uint2* d = reinterpret_cast<uint2*>(bs + (t / 2) * kBPitch + 32 * (t % 2));
-            d[0] = make_uint2(rb0.x, rb0.y);
-            d[1] = make_uint2(rb0.z, rb0.w);
-            d[2] = make_uint2(rb1.x, rb1.y);
-            d[3] = make_uint2(rb1.z, rb1.w);
+            const int hc = pb >> 1;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const uint32_t sel = c ? 0x07060302u : 0x05040100u;
+                const uint32_t lo = __builtin_amdgcn_perm(e[1], e[0], sel);  // rows 0..3
+                const uint32_t hi = __builtin_amdgcn_perm(e[3], e[2], sel);  // rows 4..7
+                *reinterpret_cast<uint2*>(bs + (4 * lane + 2 * hc + c) * kBPitch + 8 * (wave ^ ((lane >> 3) & 3))) =
+                    make_uint2(lo, hi);
+            }
         }
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int pc = 0; pc < kPieces; ++pc) store_piece(buf, pc);
     };
 
     f32x16 acc[kGFM][kGFN];
@@ -341,17 +380,17 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < kGFN; ++j) acc[i][j] = f32x16{};
 
-    const int afrag = (wm * (kGT / kGWM) + (lane & 31)) * kGPitch + 8 * (lane >> 5);
+    const int afrag = (wm * (kGT / kGWM) + (lane & 31)) * kGPitch + 8 * ((lane >> 5) ^ (kSwz ? (lane >> 4) & 1 : 0));
     const int bcol = wn * (kGT / kGWN) + (lane & 31);  // B row (output column) of fragment 0
     const int half = lane >> 5;
     // Stage st sits in buffer (st - st0) % 2.  The loads of stage st + 1 are
-    // issued during stage st - 1 (or here); during stage st they are written
-    // to the other buffer ahead of its last 16-deep step, and the loads of
-    // stage st + 2 go out right after.  The last step's MFMAs then keep the
-    // matrix core busy while the waves meet at the barrier that publishes
-    // stage st + 1, instead of the core idling through the LDS writes, the
-    // barrier and the next stage's first reads.  Loads still get a whole
-    // stage to land.
+    // issued during stage st - 1 (or here).  During stage st they are
+    // converted and written to the other buffer in pieces between the MFMAs
+    // of its last 16-deep step, and the loads of stage st + 2 go out right
+    // after, so they still get a whole stage to land.  The last step reads
+    // no fragments from LDS, and its MFMAs keep the matrix core busy through
+    // the conversion work and the LDS writes, up to the barrier that
+    // publishes stage st + 1.
     if (st0 < st1) {
         load_stage(st0);
         store_stage(0);
@@ -373,11 +412,12 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < kGFM; ++i)
             f.a[i] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + i * 32 * kGPitch + 16 * ks]));
-        if constexpr (BK == BKind::kInt8) {
+                bf16x8, *reinterpret_cast<const uint4*>(&As[buf][afrag + i * 32 * kGPitch + 16 * (kSwz ? ks ^ (i & 1) : ks)]));
+        if constexpr (BK == BKind::kInt8Cols) {
 #pragma unroll
             for (int j = 0; j < kGFN; ++j)
-                b8[j] = *reinterpret_cast<const uint2*>(&Bs[buf][(bcol + j * 32) * kBPitch + 16 * ks + 8 * half]);
+                b8[j] = *reinterpret_cast<const uint2*>(
+                    &Bs[buf][(bcol + j * 32) * kBPitch + 8 * ((2 * ks + half) ^ ((2 * wn + j) & 3))]);
         }
     };
     auto expand_b = [&](int ks, Frags& f, int j) {
@@ -390,6 +430,7 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     };
     constexpr int KS = kGK / 16;
     constexpr int kMf = kGFM * kGFN;
+    constexpr int kPerSlot = (kPieces + kMf - 2) / (kMf - 1);
     for (int st = st0; st < st1; ++st) {
         const int buf = (st - st0) & 1;
         const bool more = st + 1 < st1;
@@ -405,18 +446,21 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
         for (int ks = 0; ks < KS; ++ks) {
             const bool ahead = ks + 1 < KS;
             if (ahead) read_frags(buf, ks + 1, nxt);
-            if (ks == KS - 1 && more) {
-                store_stage(buf ^ 1);
-                if (st + 2 < st1) load_stage(st + 2);
-            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int idx = 0; idx < kMf; ++idx) {
                 const int i = idx / kGFN, j = idx % kGFN;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
                 if (ahead && idx >= kMf - kGFN) expand_b(ks + 1, nxt, idx - (kMf - kGFN));
+                if (!ahead && more) {
+                    // pieces over the step's first kMf - 1 MFMAs
+#pragma unroll
+                    for (int q = 0; q < kPerSlot; ++q)
+                        if (idx * kPerSlot + q < kPieces) store_piece(buf ^ 1, idx * kPerSlot + q);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (!ahead && more && st + 2 < st1) load_stage(st + 2);
             if (ahead) cur = nxt;
         }
         __syncthreads();
@@ -670,11 +714,10 @@ size_t split_bytes(int64_t M, int64_t N, int64_t K) {
 }  // namespace
 
 size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const int64_t Mp = round_up(M, kT), Np = round_up(N, kT);
+    const int64_t Np = round_up(N, kT);
     const int64_t nparts = (M + kNormRows - 1) / kNormRows;
-    return act_stage_bytes(M, K) + (size_t)round_up(M * Np * 2, 256) + (size_t)round_up(N * Mp * 2, 256) +
-           (size_t)round_up(K * Mp, 256) + (size_t)round_up(K * (Np / 4), 256) +
-           (size_t)round_up(nparts * K * 4, 256) + split_bytes(M, N, K);
+    return act_stage_bytes(M, K) + (size_t)round_up(K * (Np / 4), 256) + (size_t)round_up(nparts * K * 4, 256) +
+           split_bytes(M, N, K);
 }
 
 namespace {
@@ -702,15 +745,18 @@ hipError_t launch_norm_backward(const BackwardArgs& a, float* partial, int64_t n
     return hipGetLastError();
 }
 
-template <BKind BK>
-hipError_t run_gemm(const uint16_t* A, const void* B, float* C, float* P, const float* alpha, int64_t rows,
-                    int64_t cols, int64_t R, hipStream_t stream) {
-    const int sp = gemm_splits(rows, cols, R, kTargetCUs);
-    GemmArgs g{A, B, C, P, alpha, (int)rows, (int)cols, (int)R, sp};
-    bwd_gemm_kernel<BK><<<cdiv(rows, kGT) * cdiv(cols, kGT) * sp, kGThreads, 0, stream>>>(g);
-    if (sp > 1) {
-        const int64_t n = rows * cols;
-        split_reduce_kernel<<<cdiv(n / 4, 256), 256, 0, stream>>>(P, sp, n, alpha, C);
+template <AKind AK, BKind BK>
+hipError_t run_gemm(const GemmArgs& g0, hipStream_t stream) {
+    GemmArgs g = g0;
+    g.splits = gemm_splits(g.rows, g.cols, g.R, kTargetCUs);
+    const unsigned grid = cdiv(g.rows, kGT) * cdiv(g.cols, kGT) * g.splits;
+    if (g.N % 4 == 0)
+        bwd_gemm_kernel<AK, BK, true><<<grid, kGThreads, 0, stream>>>(g);
+    else
+        bwd_gemm_kernel<AK, BK, false><<<grid, kGThreads, 0, stream>>>(g);
+    if (g.splits > 1) {
+        const int64_t n = (int64_t)g.rows * g.cols;
+        split_reduce_kernel<<<cdiv(n / 4, 256), 256, 0, stream>>>(g.P, g.splits, n, g.alpha, g.C);
     }
     return hipGetLastError();
 }
@@ -723,12 +769,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     char* base = static_cast<char*>(a.ws);
     ActStage act = act_stage_carve(base, M, K);
     base += act_stage_bytes(M, K);
-    uint16_t* A1 = reinterpret_cast<uint16_t*>(base);
-    base += round_up(M * Np * 2, 256);
-    uint16_t* A2 = reinterpret_cast<uint16_t*>(base);
-    base += round_up(N * Mp * 2, 256);
-    int8_t* qT = reinterpret_cast<int8_t*>(base);
-    base += round_up(K * Mp, 256);
     uint32_t* wT = reinterpret_cast<uint32_t*>(base);
     base += round_up(K * (Np / 4), 256);
     float* partial = reinterpret_cast<float*>(base);
@@ -740,27 +780,20 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     if (M > 0) {
         e = launch_quant(a.x, a.g, M, M, (int)K, a.eps, act, stream);
         if (e != hipSuccess) return e;
-        if (Np > 0) {
-            // flat grids: one dimension of grid y would cap N (or K) at 65535 tiles
-            const unsigned grid = cdiv(Mp, kT) * cdiv(Np, kT);
-            if (N % 4 == 0)
-                dy_prep_kernel<true><<<grid, kPrepThreads, 0, stream>>>(
-                    a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint2*>(A1), reinterpret_cast<uint2*>(A2));
-            else
-                dy_prep_kernel<false><<<grid, kPrepThreads, 0, stream>>>(
-                    a.dy, act.s, (int)M, (int)N, (int)Mp, (int)Np, reinterpret_cast<uint2*>(A1), reinterpret_cast<uint2*>(A2));
+        if (Np > 0)  // flat grid: one dimension of grid y would cap K at 65535 tiles
             w_transpose_kernel<<<cdiv(Np, kT) * cdiv(K, kT), kPrepThreads, 0, stream>>>(
                 reinterpret_cast<const uint32_t*>(a.packed), (int)N, (int)K, (int)Np, wT);
-        }
-        q_transpose_kernel<<<cdiv(Mp, kT) * cdiv(K, kT), kPrepThreads, 0, stream>>>(
-            act.q, (int)M, (int)K, (int)Mp, qT);
-        e = run_gemm<BKind::kTern2>(A1, wT, a.dx, splitbuf, a.gamma, M, K, Np, stream);
+        // dxn [M][K] = gamma bf16(dy) [M][Np] . wT^T
+        GemmArgs g{a.dy, act.s, wT, a.dx, splitbuf, a.gamma, (int)M, (int)K, (int)Np, 1, (int)M, (int)N};
+        e = run_gemm<AKind::kRows, BKind::kTern2>(g, stream);
         if (e != hipSuccess) return e;
         e = launch_norm_backward(a, partial, nparts_used, stream);
         if (e != hipSuccess) return e;
     }
     if (N > 0) {
-        e = run_gemm<BKind::kInt8>(A2, qT, a.dW, splitbuf, nullptr, N, K, Mp, stream);
+        // dW [N][K] = bf16(dy (1 / s))^T [N][Mp] . q [Mp][K]
+        GemmArgs g{a.dy, act.s, act.q, a.dW, splitbuf, nullptr, (int)N, (int)K, (int)Mp, 1, (int)M, (int)N};
+        e = run_gemm<AKind::kColsScaled, BKind::kInt8Cols>(g, stream);
         if (e != hipSuccess) return e;
     }
     dg_reduce_kernel<<<cdiv(K, kDgCols), kDgCols * kDgSplit, 0, stream>>>(partial, (int)nparts_used, (int)K, a.dg);

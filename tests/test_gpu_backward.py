@@ -1,15 +1,18 @@
 """Backward pass (straight-through estimator) on the GPU against the oracle.
 
 The two gradient products run in bf16 with fp32 accumulation; every other
-step is fp32 or exact.  The bar per element is derived from that arithmetic:
-rounding dy (or dy / s) to bf16 moves each term of a product by at most
-2^-9 of its size, and fp32 accumulation of R terms adds at most R * 2^-24 of
-the sum of their sizes, so for R <= 2^15
-    |dxn - dxn_ref| <= 2^-8 * gamma * sum_n |dy[m][n]| |w[n][k]|       (E)
-    |dW - dW_ref|   <= 2^-8 * sum_m |dy[m][n] / s[m]| |q[m][k]|
-and dx, dg inherit E through the RMSNorm backward (linear in dxn), plus
-1e-5 of their own terms for the fp32 arithmetic there.  Exact zeros are
-required where the method has them (M = 0, N = 0).
+step is fp32 or exact.  The bar per element is derived from that arithmetic.
+bf16 keeps 8 significant bits, so rounding a term's operand dy (or
+dy * (1 / s), itself two fp32 roundings of dy / s) to nearest bf16 moves the
+term by at most 2^-8 (plus 2^-22) of its size, and fp32 accumulation of
+R <= 2^15 terms adds at most R * 2^-24 <= 2^-9 of the sum of their sizes:
+    |dxn - dxn_ref| <= U * gamma * sum_n |dy[m][n]| |w[n][k]|             (E)
+    |dW - dW_ref|   <= U * sum_m |dy[m][n] / s[m]| |q[m][k]|
+with U = 2^-8 + 2^-9 + 2^-22; dx and dg inherit E through the RMSNorm
+backward (linear in dxn), plus 1e-5 of their own terms for the fp32
+arithmetic there.  Exact zeros are required where the method has them
+(M = 0, N = 0), and one token's dW, a single product per element, is
+checked bit for bit.
 """
 import numpy as np
 import pytest
@@ -22,7 +25,7 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 EPS = 1e-6
-U = 2.0 ** -8
+U = 2.0 ** -8 + 2.0 ** -9 + 2.0 ** -22
 
 
 def _case(M, N, K, seed, outliers=True):
@@ -103,6 +106,24 @@ SHAPES = [
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_backward_matches_oracle(M, N, K):
     _parity(M, N, K, seed=M * 7 + N * 3 + K)
+
+
+@pytest.mark.parametrize("N,K", [(300, 784), (37, 272), (64, 16)])
+def test_backward_one_token_dW_exact(N, K):
+    """M = 1: dW[n][k] = bf16(dy[n] * (1 / s)) * q[k], one product of a bf16
+    and an int8 value, exact in fp32.  q and s are the forward's (the
+    quantisation kernel the backward reruns); the rest is worked out here
+    with fp32 arithmetic and round-to-nearest-even bf16."""
+    x, g, W, dy = _case(1, N, K, seed=N + K)
+    packed, gamma = gu.pack_on_gpu(W)
+    q, s = bl.bitlinear_quantize(gu.to_dev_bf16(x), gu.to_dev(g), eps=EPS)
+    _, _, dW = _run_gpu(x, g, packed, gamma, dy)
+    q = q.cpu().numpy().astype(np.float64)
+    s = s.cpu().numpy().astype(np.float32)
+    a = dy[0].astype(np.float32) * (np.float32(1.0) / s[0])
+    a = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(a)).astype(np.float64)
+    want = a[:, None] * q[0][None, :]
+    assert np.array_equal(dW.astype(np.float64), want), np.abs(dW - want).max()
 
 
 def test_backward_without_outliers_and_unit_gain():
