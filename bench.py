@@ -142,9 +142,10 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel_file, digest):
+def read_traffic(kernel_file, digest, algorithmic_bytes):
     """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel source changed since it was taken."""
+    there is none, the kernel source changed since it was taken, or it was
+    taken on another workload (its algorithmic bytes per launch differ)."""
     path = os.path.join(ROOT, "profiles", "traffic_" + kernel_file.replace(".hip", "") + ".txt")
     if not os.path.exists(path):
         return None
@@ -157,6 +158,8 @@ def read_traffic(kernel_file, digest):
     if vals.get("source_sha256_16") != digest:
         return None
     try:
+        if int(vals["algorithmic_bytes_per_launch"]) != int(algorithmic_bytes):
+            return None
         return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
@@ -793,7 +796,7 @@ def main():
         cpu.pop("seconds")
 
     digest = source_digest(*DECODE_SOURCES)
-    traffic = read_traffic("decode.hip", digest)
+    traffic = read_traffic("decode.hip", digest, head["bytes_per_step"])
     achieved = head["bytes_per_step"] / (head["event_ms"] * 1e-3) / 1e9
     out = {
         "metric": "fused BitLinear: HBM GB/s at M=1 and int8 TOPS at M=8192 (% of roofline)",
