@@ -401,8 +401,9 @@ size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * dx fp32 [M][K], dg fp32 [K], dW fp32 [N][K] (the gradient with respect to
  * the fp32 master weights).  q and s are recomputed from x with the
  * forward's own kernel, so they are the forward's bits.  The two products
- * run in bf16 with fp32 accumulation: dy and dy / s are rounded to bf16
- * (nearest even); w and q are exact.  M = 0 gives dg = 0 and dW = 0; N = 0
+ * run in bf16 with fp32 accumulation: dy and dy * (1 / s) (one fp32
+ * reciprocal per token) are rounded to bf16 (nearest even); w and q are
+ * exact.  M = 0 gives dg = 0 and dW = 0; N = 0
  * gives dx = 0 and dg = 0.  Deterministic (fixed reduction orders). */
 int bitlinear_backward(const uint16_t* x, const float* rms_weight, const uint8_t* packed,
                        const float* gamma, const float* dy, int64_t M, int64_t N, int64_t K, float eps,
