@@ -679,7 +679,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="run only these secondary workloads after the headline (comma-separated; "
-                         "available: backward, layer, crossover, prefill)")
+                         "available: backward, layer, crossover, prefill, repack)")
     ap.add_argument("--skip", default="",
                     help="skip these secondary workloads in a full run (comma-separated: layer, crossover, "
                          "backward); for profiling runs, where counter collection serialises every dispatch")
@@ -755,6 +755,11 @@ def main():
         secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
         secondary["glu_m4096"] = bench_glu(torch, bl, wl, 4096, 2048, 5632, max(10, args.steps // 2),
                                            args.warmup, stream)
+
+    if only and "repack" in only:
+        log("[bench] re-ternarisation of 64 x 2048 x 2048 fp32 master weights")
+        secondary["repack_64x2048x2048"] = bench_repack(torch, bl, wl, 64, 2048, 2048, 10, 2, stream)
+        secondary["context_hbm_copy_2gib"] = bench_hbm_copy(torch, 2 << 30, 10)
 
     if only and "prefill" in only:
         log("[bench] prefill 8192 and the MFMA-tile sweep shapes")

@@ -93,6 +93,24 @@ def test_pack_batched(N, K):
         assert g1.item() == gamma[b] and np.array_equal(p1.cpu().numpy(), packed[b]), b
 
 
+def test_pack_batched_large():
+    """Five 4096 x 4096 matrices (320 MB of fp32, more than the chip's last-
+    level cache) in one call, one of them all zero: every matrix gets the
+    bytes and gamma of a call of its own, and the last one the oracle's."""
+    N = K = 4096
+    _say("pack batched large", 5, N, K)
+    W = torch.stack([wl.w_normal_device(N, K, seed=7, layer=b, device=gu.DEV) for b in range(5)])
+    W[1].zero_()
+    packed, gamma = bl.bitlinear_pack_weights_batched(W)
+    for b in range(5):
+        p1, g1 = bl.bitlinear_pack_weights(W[b].contiguous())
+        assert g1.item() == gamma[b].item() and torch.equal(p1, packed[b]), b
+    Wl = W[4].cpu().numpy()
+    g_ref = gu.orc().gamma(Wl)
+    assert gamma[4].item() == g_ref
+    assert np.array_equal(packed[4].cpu().numpy(), gu.orc().pack(gu.orc().ternarize(Wl, g_ref)))
+
+
 def test_unpack_marks_unused_code():
     p = torch.full((2, 4), 0xFF, dtype=torch.uint8, device=gu.DEV)
     w = bl.bitlinear_unpack_weights(p, 16).cpu().numpy()
