@@ -33,6 +33,7 @@
 // (fixed order, fp64).
 #include "device_common.h"
 #include "launch.h"
+#include "quant_row.h"
 #include "xcd.h"
 
 namespace bl {
@@ -673,6 +674,115 @@ __global__ __launch_bounds__(kNormThreads) void norm_backward_regs_kernel(const 
     }
 }
 
+// The register-form RMSNorm backward fused with the re-quantisation of the
+// same rows (q and s for the dW product), for rows of at most CPL * 512
+// elements.  Lane l holds the 8-element chunks l + 64 c (c < CPL) of its
+// wave's row -- the streaming quantiser's layout -- and quantises the row
+// with that kernel's own row function, so q and s are its bits; x is read
+// once for both.  The RMSNorm backward arithmetic is that of
+// norm_backward_regs_kernel (fp64 row sums, dx in place over dxn, the
+// block's dg partial added over its waves in wave order).
+template <int CPL, bool FULL>
+__global__ __launch_bounds__(kNormThreads) void norm_backward_quant_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ gw, int M, int K, float eps,
+    float* __restrict__ dxio, float* __restrict__ partial, int8_t* __restrict__ q, float* __restrict__ s) {
+    __shared__ float4 red[2 * CPL * kWave];
+    const int m0 = blockIdx.x * kNormRowsRegs;
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    constexpr int kWaves = kNormThreads / kWave;
+    const int nchunks = K / 8;
+    float4 gv[CPL][2], acc[CPL][2];
+    load_g_row<CPL, FULL>(gw, lane, nchunks, gv);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c][0] = acc[c][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto valid = [&](int c) { return FULL || (int)(lane + c * kWave) < nchunks; };
+    for (int rr = wave; rr < kNormRowsRegs; rr += kWaves) {
+        const int m = m0 + rr;
+        if (m >= M) break;
+        float* dr = dxio + (int64_t)m * K;
+        uint4 xc[CPL];
+        load_x_row<CPL, FULL>(x + (int64_t)m * K, lane, nchunks, xc);
+        float4 d[CPL][2];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int k = 8 * (int)(lane + c * kWave);
+            d[c][0] = d[c][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (valid(c)) {
+                d[c][0] = *reinterpret_cast<const float4*>(dr + k);
+                d[c][1] = *reinterpret_cast<const float4*>(dr + k + 4);
+            }
+        }
+        double ss = 0.0, S = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float xs[8] = {bf16_lo(xc[c].x), bf16_hi(xc[c].x), bf16_lo(xc[c].y), bf16_hi(xc[c].y),
+                                 bf16_lo(xc[c].z), bf16_hi(xc[c].z), bf16_lo(xc[c].w), bf16_hi(xc[c].w)};
+            const float ds[8] = {d[c][0].x, d[c][0].y, d[c][0].z, d[c][0].w, d[c][1].x, d[c][1].y, d[c][1].z, d[c][1].w};
+            const float gs[8] = {gv[c][0].x, gv[c][0].y, gv[c][0].z, gv[c][0].w,
+                                 gv[c][1].x, gv[c][1].y, gv[c][1].z, gv[c][1].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                ss += (double)xs[j] * (double)xs[j];
+                S += (double)ds[j] * (double)gs[j] * (double)xs[j];
+            }
+        }
+        ss = wave_sum(ss);
+        S = wave_sum(S);
+        const double rd = 1.0 / sqrt(ss / (double)K + (double)eps);
+        const float r = (float)rd, cc = (float)(rd * rd * rd * S / (double)K);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float xs[8] = {bf16_lo(xc[c].x), bf16_hi(xc[c].x), bf16_lo(xc[c].y), bf16_hi(xc[c].y),
+                                 bf16_lo(xc[c].z), bf16_hi(xc[c].z), bf16_lo(xc[c].w), bf16_hi(xc[c].w)};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float4 g4 = gv[c][h], d4 = d[c][h];
+                const float x0 = xs[4 * h], x1 = xs[4 * h + 1], x2 = xs[4 * h + 2], x3 = xs[4 * h + 3];
+                if (valid(c)) {
+                    float4 o;
+                    o.x = r * g4.x * d4.x - x0 * cc;
+                    o.y = r * g4.y * d4.y - x1 * cc;
+                    o.z = r * g4.z * d4.z - x2 * cc;
+                    o.w = r * g4.w * d4.w - x3 * cc;
+                    *reinterpret_cast<float4*>(dr + 8 * (int)(lane + c * kWave) + 4 * h) = o;
+                }
+                acc[c][h].x += d4.x * x0 * r;
+                acc[c][h].y += d4.y * x1 * r;
+                acc[c][h].z += d4.z * x2 * r;
+                acc[c][h].w += d4.w * x3 * r;
+            }
+        }
+        quant_row_regs<CPL, FULL>(
+            xc, [&](int c, float4& lo, float4& hi) { lo = gv[c][0]; hi = gv[c][1]; }, m, lane, K, eps, q, s,
+            nullptr);
+    }
+    // dg partial of the block: waves 0, 1, 2, 3 added in that order
+    for (int w = 0; w < kWaves; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float4 v = acc[c][h];
+                    const int i = (2 * c + h) * kWave + lane;
+                    if (w > 0) {
+                        const float4 p = red[i];
+                        v = make_float4(p.x + v.x, p.y + v.y, p.z + v.z, p.w + v.w);
+                    }
+                    red[i] = v;
+                }
+        }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < 2 * CPL * kWave; i += kNormThreads) {
+        const int ch = i / kWave, l = i % kWave;  // ch = 2 c + h
+        const int chunk = l + (ch / 2) * kWave;
+        if (FULL || chunk < nchunks)
+            *reinterpret_cast<float4*>(partial + (int64_t)blockIdx.x * K + 8 * chunk + 4 * (ch % 2)) = red[i];
+    }
+}
+
 // dg[k] = sum over blocks of the partials in fp64.  A block takes 16
 // columns; its 64 thread groups each sum every 64th partial (in order), and
 // the 64 group sums are added in group order, so the result is
@@ -745,6 +855,37 @@ hipError_t launch_norm_backward(const BackwardArgs& a, float* partial, int64_t n
     return hipGetLastError();
 }
 
+// The fused RMSNorm backward + re-quantisation applies where the forward's
+// quantiser is the streaming kernel (at least 64 rows) with at most four
+// 8-element chunks per lane (K <= 2048, so the row, dxn, g and the dg sums
+// stay in registers).
+bool norm_quant_fused(int64_t M, int64_t K) { return M >= 64 && K <= 4 * kWave * 8; }
+
+template <int CPL>
+void launch_norm_quant_cpl(const BackwardArgs& a, float* partial, unsigned grid, const ActStage& act,
+                           hipStream_t stream) {
+    const int M = (int)a.M, K = (int)a.K;
+    if (K == CPL * kWave * 8)
+        norm_backward_quant_kernel<CPL, true><<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx, partial,
+                                                                                 act.q, act.s);
+    else
+        norm_backward_quant_kernel<CPL, false><<<grid, kNormThreads, 0, stream>>>(a.x, a.g, M, K, a.eps, a.dx,
+                                                                                  partial, act.q, act.s);
+}
+
+hipError_t launch_norm_quant(const BackwardArgs& a, float* partial, int64_t nblocks, const ActStage& act,
+                             hipStream_t stream) {
+    const int cpl = (int)((a.K / 8 + kWave - 1) / kWave);
+    const unsigned grid = (unsigned)nblocks;
+    switch (cpl) {
+        case 1: launch_norm_quant_cpl<1>(a, partial, grid, act, stream); break;
+        case 2: launch_norm_quant_cpl<2>(a, partial, grid, act, stream); break;
+        case 3: launch_norm_quant_cpl<3>(a, partial, grid, act, stream); break;
+        default: launch_norm_quant_cpl<4>(a, partial, grid, act, stream); break;
+    }
+    return hipGetLastError();
+}
+
 template <AKind AK, BKind BK>
 hipError_t run_gemm(const GemmArgs& g0, hipStream_t stream) {
     GemmArgs g = g0;
@@ -777,9 +918,12 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     const int64_t nparts_used = M > 0 ? norm_blocks(M, K) : 0;  // <= nparts, the size reserved
 
     hipError_t e;
+    const bool fused_q = norm_quant_fused(M, K);
     if (M > 0) {
-        e = launch_quant(a.x, a.g, M, M, (int)K, a.eps, act, stream);
-        if (e != hipSuccess) return e;
+        if (!fused_q) {
+            e = launch_quant(a.x, a.g, M, M, (int)K, a.eps, act, stream);
+            if (e != hipSuccess) return e;
+        }
         if (Np > 0)  // flat grid: one dimension of grid y would cap K at 65535 tiles
             w_transpose_kernel<<<cdiv(Np, kT) * cdiv(K, kT), kPrepThreads, 0, stream>>>(
                 reinterpret_cast<const uint32_t*>(a.packed), (int)N, (int)K, (int)Np, wT);
@@ -787,7 +931,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
         GemmArgs g{a.dy, act.s, wT, a.dx, splitbuf, a.gamma, (int)M, (int)K, (int)Np, 1, (int)M, (int)N};
         e = run_gemm<AKind::kRows, BKind::kTern2>(g, stream);
         if (e != hipSuccess) return e;
-        e = launch_norm_backward(a, partial, nparts_used, stream);
+        e = fused_q ? launch_norm_quant(a, partial, nparts_used, act, stream)
+                    : launch_norm_backward(a, partial, nparts_used, stream);
         if (e != hipSuccess) return e;
     }
     if (N > 0) {

@@ -126,6 +126,28 @@ def test_backward_one_token_dW_exact(N, K):
     assert np.array_equal(dW.astype(np.float64), want), np.abs(dW - want).max()
 
 
+@pytest.mark.parametrize("M,N,K,row", [(100, 300, 272, 63), (100, 64, 1024, 0), (130, 37, 1040, 129),
+                                       (64, 200, 2048, 17)])
+def test_backward_one_row_dW_exact(M, N, K, row):
+    """dy zero except one token row: dW[n][k] = bf16(dy[row][n] * (1 / s)) * q[k]
+    exactly, the other rows adding exact zeros.  At 64 rows and more the
+    backward re-quantises x inside its RMSNorm backward kernel; q and s must
+    still be the forward quantiser's bits (ragged and whole chunk counts)."""
+    x, g, W, dy = _case(M, N, K, seed=M + N + K)
+    keep = dy[row].copy()
+    dy[:] = 0
+    dy[row] = keep
+    packed, gamma = gu.pack_on_gpu(W)
+    q, s = bl.bitlinear_quantize(gu.to_dev_bf16(x), gu.to_dev(g), eps=EPS)
+    _, _, dW = _run_gpu(x, g, packed, gamma, dy)
+    q = q.cpu().numpy()[row].astype(np.float64)
+    s = s.cpu().numpy().astype(np.float32)[row]
+    a = keep.astype(np.float32) * (np.float32(1.0) / s)
+    a = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(a)).astype(np.float64)
+    want = a[:, None] * q[None, :]
+    assert np.array_equal(dW.astype(np.float64), want), np.abs(dW - want).max()
+
+
 def test_backward_without_outliers_and_unit_gain():
     M, N, K = 96, 80, 256
     x, _, W, dy = _case(M, N, K, seed=5, outliers=False)
