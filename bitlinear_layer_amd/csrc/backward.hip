@@ -304,8 +304,8 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
         }
     };
     // Conversion and LDS writes of the staged registers, in pieces that the
-    // main loop spreads between the MFMAs of a stage's last 16-deep step
-    // (a wave's VALU work then issues while its MFMAs run):
+    // main loop spreads between the MFMAs of a stage's second-to-last
+    // 16-deep step (a wave's VALU work then issues while its MFMAs run):
     //   kRows: pieces 0..3, one LDS row each;
     //   kColsScaled: piece 0 the reciprocals 1 / s of the stage's 8 rows (one
     //          division per lane, broadcast from lanes 0..7), pieces 1..4 one
@@ -387,11 +387,10 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
     // Stage st sits in buffer (st - st0) % 2.  The loads of stage st + 1 are
     // issued during stage st - 1 (or here).  During stage st they are
     // converted and written to the other buffer in pieces between the MFMAs
-    // of its last 16-deep step, and the loads of stage st + 2 go out right
-    // after, so they still get a whole stage to land.  The last step reads
-    // no fragments from LDS, and its MFMAs keep the matrix core busy through
-    // the conversion work and the LDS writes, up to the barrier that
-    // publishes stage st + 1.
+    // of its second-to-last 16-deep step, and the loads of stage st + 2 go
+    // out right after, so they still get a whole stage to land.  The
+    // conversion work then issues while the MFMAs run, and the last step
+    // runs MFMAs only, up to the barrier that publishes stage st + 1.
     if (st0 < st1) {
         load_stage(st0);
         store_stage(0);
@@ -453,7 +452,7 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
                 const int i = idx / kGFN, j = idx % kGFN;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
                 if (ahead && idx >= kMf - kGFN) expand_b(ks + 1, nxt, idx - (kMf - kGFN));
-                if (!ahead && more) {
+                if (ks == KS - 2 && more) {
                     // pieces over the step's first kMf - 1 MFMAs
 #pragma unroll
                     for (int q = 0; q < kPerSlot; ++q)
@@ -461,7 +460,7 @@ __global__ __launch_bounds__(kGThreads) void bwd_gemm_kernel(GemmArgs g) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (!ahead && more && st + 2 < st1) load_stage(st + 2);
+            if (ks == KS - 2 && more && st + 2 < st1) load_stage(st + 2);
             if (ahead) cur = nxt;
         }
         __syncthreads();

@@ -100,6 +100,10 @@ SHAPES = [
     # its chained steps: 128 partials on the register form, 138 on the
     # two-pass form
     (2048, 64, 256), (1100, 40, 4160),
+    # 64 rows and more: re-quantisation inside the RMSNorm backward up to
+    # K = 2048 (here a ragged fourth chunk per lane), the separate quantiser
+    # and the register form above
+    (200, 100, 2000), (96, 48, 3072),
 ]
 
 
