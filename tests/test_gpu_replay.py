@@ -91,8 +91,8 @@ def test_graph_replay_matches_eager():
 
 
 def test_graph_replay_backward_matches_eager():
-    """The backward pass captured into a graph (eight launches, split
-    reduction included) and replayed on new x and dy equals eager calls."""
+    """The backward pass captured into a graph (seven launches, both split
+    reductions included) and replayed on new x and dy equals eager calls."""
     dev = gu.DEV
     M, N, K = 300, 2048, 512  # dW has 16 tiles, so its reduction is split
     packed, gamma = gu.pack_on_gpu(wl.w_normal(N, K, seed=21))
