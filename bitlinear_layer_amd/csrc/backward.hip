@@ -10,8 +10,10 @@
 //   dg[k]    = sum_m dxn[m][k] x[m][k] r[m],
 //   dx[m][k] = r g[k] dxn[m][k] - x[m][k] r^3 / K * sum_j dxn[m][j] g[j] x[m][j],
 // with r = (mean(x^2) + eps)^-1/2.  Nothing is kept from the forward call: q
-// and s are recomputed by the forward's own quantisation kernel (the same
-// bits), r from x.
+// and s are recomputed with the forward's own quantisation arithmetic (the
+// same bits) -- inside the RMSNorm backward kernel, which holds each row of
+// x anyway, where the forward's streaming quantiser applies (64 rows and
+// more, K <= 2048), else by that quantiser itself -- and r from x.
 //
 // Both products are dense floating-point contractions and run on the bf16
 // matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation), with the
@@ -28,9 +30,10 @@
 // codes (16 reduction indices per word), expanded to bf16 fragments right
 // before its MFMAs.
 //
-// Kernels: w_transpose (2-bit codes, transposed), the NT GEMM (twice),
-// norm_backward (dx in place over dxn, per-block dg partials) and dg_reduce
-// (fixed order, fp64).
+// Kernels: w_transpose (2-bit codes, transposed), the NT GEMM (dxn, then
+// dW, each with split_reduce when its reduction is split), norm_backward
+// (dx in place over dxn, per-block dg partials; one form also re-quantises
+// x) and dg_reduce (fixed order, fp64).
 #include "device_common.h"
 #include "launch.h"
 #include "quant_row.h"
