@@ -400,7 +400,7 @@ size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * gamma (fp32 scalar) of the forward, dy fp32 [M][N].  Outputs (device):
  * dx fp32 [M][K], dg fp32 [K], dW fp32 [N][K] (the gradient with respect to
  * the fp32 master weights).  q and s are recomputed from x with the
- * forward's own kernel, so they are the forward's bits.  The two products
+ * forward's own quantisation arithmetic, so they are the forward's bits.  The two products
  * run in bf16 with fp32 accumulation: dy and dy * (1 / s) (one fp32
  * reciprocal per token) are rounded to bf16 (nearest even); w and q are
  * exact.  M = 0 gives dg = 0 and dW = 0; N = 0
