@@ -443,9 +443,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dma_kernel(ProductArgs a
 // ---------------------------------------------------------------------------
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM, int WM, int WN, Epilogue EP>
+template <int BM, int WM, int WN, Epilogue EP, int BN>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a) {
-    constexpr int BN = 256;
     constexpr bool kGlu = EP == Epilogue::kGluBf16;
     constexpr bool kRes = EP == Epilogue::kResBf16;
     constexpr int kWavesPerBlock = WM * WN;
@@ -834,14 +833,35 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_x32_kernel(ProductArgs a
     }
 }
 
-template <int BM, int WM, int WN, Epilogue EP>
+template <int BM, int WM, int WN, Epilogue EP, int BN = 256>
 hipError_t launch_x32(const ProductArgs& a, hipStream_t stream) {
-    constexpr int kCols = EP == Epilogue::kGluBf16 ? 128 : 256;
+    constexpr int kCols = EP == Epilogue::kGluBf16 ? BN / 2 : BN;
     const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + BM - 1) / BM);
     if (tiles * a.batch > 0x7fffffff) return hipErrorInvalidValue;  // one grid dimension
     const dim3 grid((unsigned)(tiles * a.batch));
-    gemm_x32_kernel<BM, WM, WN, EP><<<grid, WM * WN * kWave, 0, stream>>>(a);
+    gemm_x32_kernel<BM, WM, WN, EP, BN><<<grid, WM * WN * kWave, 0, stream>>>(a);
     return hipGetLastError();
+}
+
+// Blocks of the x32 product with BM x BN tiles over all problems of the call.
+template <int BM, int BN, Epilogue EP>
+int64_t x32_tiles(const ProductArgs& a) {
+    constexpr int kCols = EP == Epilogue::kGluBf16 ? BN / 2 : BN;
+    return (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + BM - 1) / BM) * a.batch;
+}
+
+// The x32 product with the largest tiles that still give more than 128
+// blocks (half the compute units): 256 x 256 (8 waves of 64 x 128), else
+// 128 x 256 (8 waves of 64 x 64), else 128 x 128 (4 waves of 64 x 64; two
+// blocks fit a compute unit).  kResBf16 starts at 128 x 256: the 256-row
+// tile's 128 residual values per lane would not fit beside its registers.
+template <Epilogue EP>
+hipError_t launch_x32_sized(const ProductArgs& a, hipStream_t stream) {
+    if constexpr (EP != Epilogue::kResBf16) {
+        if (x32_tiles<256, 256, EP>(a) > 128) return launch_x32<256, 4, 2, EP>(a, stream);
+    }
+    if (x32_tiles<128, 256, EP>(a) > 128) return launch_x32<128, 2, 4, EP>(a, stream);
+    return launch_x32<128, 2, 2, EP, 128>(a, stream);
 }
 
 template <int BM, int BN, int WM, int WN, Epilogue EP, int BK>
@@ -876,11 +896,7 @@ hipError_t launch_ep(const ProductArgs& a, hipStream_t stream) {
         const int64_t span = (EP == Epilogue::kGluBf16 ? (int64_t)a.N : 0) + 256;
         const bool offs32 = span * (a.K / 4) < ((int64_t)1 << 32);
         if (!whole_stages || !offs32) return launch_tile<256, 256, 4, 2, EP>(a, stream);
-        // 256 x 256 tiles (8 waves of 64 x 128) unless they would leave at
-        // least half of the 256 CUs idle; then 128 x 256 (8 waves of 64 x 64).
-        constexpr int kCols = EP == Epilogue::kGluBf16 ? 128 : 256;
-        const int64_t tiles = (int64_t)((a.N + kCols - 1) / kCols) * ((a.M + 255) / 256) * a.batch;
-        return tiles > 128 ? launch_x32<256, 4, 2, EP>(a, stream) : launch_x32<128, 2, 4, EP>(a, stream);
+        return launch_x32_sized<EP>(a, stream);
     }
     if (a.K % 256 == 0) return launch_dma_tile<64, 256, 1, 8, EP, 256>(a, stream);
     return whole_stages ? launch_dma_tile<64, 256, 1, 8, EP, 128>(a, stream)
@@ -895,11 +911,10 @@ bool product_takes_residual(int M, int N, int K) {
 
 hipError_t launch_gemm_mfma(const ProductArgs& a, Epilogue ep, hipStream_t stream) {
     if (ep == Epilogue::kResBf16) {
-        // The large-tile kernel with 128 x 256 tiles (8 waves of 64 x 64):
-        // each lane holds the 64 residual values of its fragments before the
-        // stores; the 256-row tile's 128 would not fit beside its registers.
+        // The large-tile kernel with 64 x 64 wave tiles: each lane holds the
+        // 64 residual values of its fragments before the stores.
         if (!product_takes_residual(a.M, a.N, a.K) || a.res == nullptr) return hipErrorInvalidValue;
-        return launch_x32<128, 2, 4, Epilogue::kResBf16>(a, stream);
+        return launch_x32_sized<Epilogue::kResBf16>(a, stream);
     }
     if (skinny_supported(a.M, a.K, ep)) return launch_skinny(a, ep, stream);
     switch (ep) {
