@@ -858,7 +858,13 @@ int64_t x32_tiles(const ProductArgs& a) {
 template <Epilogue EP>
 hipError_t launch_x32_sized(const ProductArgs& a, hipStream_t stream) {
     if constexpr (EP != Epilogue::kResBf16) {
-        if (x32_tiles<256, 256, EP>(a) > 128) return launch_x32<256, 4, 2, EP>(a, stream);
+        // 256 x 256 tiles when they fill at least half the chip, unless
+        // 128 x 256 tiles need fewer than 1.6 times as many rounds of 256
+        // blocks (each of those tiles is half the work): a partial last
+        // round of large tiles leaves compute units idle for a whole tile.
+        const int64_t t256 = x32_tiles<256, 256, EP>(a);
+        const int64_t r256 = (t256 + 255) / 256, r128 = (x32_tiles<128, 256, EP>(a) + 255) / 256;
+        if (t256 > 128 && 10 * r128 >= 16 * r256) return launch_x32<256, 4, 2, EP>(a, stream);
     }
     if (x32_tiles<128, 256, EP>(a) > 128) return launch_x32<128, 2, 4, EP>(a, stream);
     return launch_x32<128, 2, 2, EP, 128>(a, stream);

@@ -567,8 +567,10 @@ def assert_h_parity(h_gpu, h_ref):
     assert diff.max(initial=0) <= 1 and np.mean(diff != 0) <= 1e-3, (diff.max(), np.mean(diff != 0))
 
 
+# (768, 64, 11008): 258 tiles of 256 x 256 (two rounds of 256 blocks), so the
+# gate|up product takes 128 x 256 tiles (three rounds of half the work).
 @pytest.mark.parametrize("M,D,F", [(1, 256, 320), (5, 256, 320), (130, 256, 320), (1, 3008, 64), (3, 2048, 5632),
-                                   (2, 208, 96)])
+                                   (2, 208, 96), (768, 64, 11008)])
 def test_glu_hidden(M, D, F):
     x, g_gu, W_gu, g_dn, W_dn = _glu_inputs(M, D, F, seed=M)
     ref = gu.orc().glu(x, g_gu, W_gu, g_dn, W_dn)
