@@ -120,20 +120,32 @@ def _check(status):
         raise BitlinearError(status, bitlinear_last_error())
 
 
+# The raw handle of the current device's current stream.  torch's internal
+# hook returns it without building a Stream object (which costs a few
+# microseconds per call); the public call is the fallback.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_current_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    """The stream handle for the C ABI (an int; ctypes passes it as void*):
+    the given stream, or the current stream of the current device."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and _current_device is not None:
+        return _raw_stream(_current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """A tensor's device address as an int (ctypes passes it as void*)."""
+    return None if t is None else t.data_ptr()
 
 
 def _dev(t, name, dtypes, ndim=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
@@ -162,7 +174,7 @@ def _out(t, name, dtypes, shape, like):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.device.type != "cuda" or t.device != like.device:
+    if not t.is_cuda or t.get_device() != like.get_device():
         raise ValueError(f"{name} must be on {like.device}, is on {t.device}")
     return t
 
