@@ -386,8 +386,10 @@ def test_layer_one_token_fused_equals_composed(B, d, F):
 
 # (B, T, d, F): more than 128 tokens, so the output and down projections run
 # on the large-tile product, which adds the residual in its epilogue (on
-# 128 x 128 tiles up to 2048 tokens at d = 2048, on 128 x 256 tiles above).
-MANY_TOKENS = [(1, 300, 256, 384), (2, 160, 128, 256), (1, 1024, 2048, 5632), (1, 2200, 2048, 512)]
+# 128 x 128 tiles up to 2048 tokens at d = 2048, on 128 x 256 tiles above;
+# d = 192 leaves the last 128-column tile half full).
+MANY_TOKENS = [(1, 300, 256, 384), (2, 160, 128, 256), (1, 200, 192, 256), (1, 1024, 2048, 5632),
+               (1, 2200, 2048, 512)]
 
 
 @pytest.mark.parametrize("B,T,d,F", MANY_TOKENS)
